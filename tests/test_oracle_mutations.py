@@ -1,0 +1,112 @@
+"""Plant plausible mistakes in copies of the oracle and check that the pins catch
+each one (no GPU).  The mistakes live only in throw-away module copies built
+from the oracle's source text; the oracle itself is never modified."""
+import importlib
+import os
+import types
+
+import pytest
+
+import oracle
+import test_oracle_aux_front as T_AF
+import test_oracle_golden as T_G
+import test_oracle_permutation as T_P
+import test_oracle_routing as T_R
+
+ORACLE_DIR = os.path.dirname(oracle.__file__)
+
+PINS = [
+    T_R.pin_weights_sum_to_scale, T_R.pin_sigmoid_bias_semantics, T_R.pin_brute_force,
+    T_R.pin_pre_renorm_equals_post, T_R.pin_special_cases, T_R.pin_grouping_reductions,
+    T_R.pin_scores_counts_decode,
+    T_P.pin_permutation_invariants, T_P.pin_counting_sort, T_P.pin_local_expert_shard,
+    T_AF.pin_aux_closed_form, T_AF.pin_aux_finite_difference, T_AF.pin_rmsnorm,
+    T_AF.pin_bf16_rounding, T_AF.pin_identity_projection,
+    T_G.pin_golden_routing, T_G.pin_golden_permutation, T_G.pin_golden_aux_loss,
+    T_G.pin_golden_rmsnorm,
+]
+
+# (module, text in the oracle, planted replacement, what the mistake is)
+MUTATIONS = [
+    ("routing", 'order = np.argsort(-masked, axis=1, kind="stable")',
+     'order = (E - 1) - np.argsort(-masked[:, ::-1], axis=1, kind="stable")',
+     "ties go to the higher expert index"),
+    ("routing", "key = key + bias64.astype(np.float32)", "key = key",
+     "bias dropped from the selection key"),
+    ("routing", "w = w * float(scale)", "w = w",
+     "routed scaling factor not applied"),
+    ("routing", "        w = 1.0 / (1.0 + np.exp(-xs))\n        if renorm:\n            w = w / w.sum(axis=1, keepdims=True)",
+     "        w = 1.0 / (1.0 + np.exp(-xs))",
+     "sigmoid weights not renormalised"),
+    ("routing", "        w = 1.0 / (1.0 + np.exp(-xs))",
+     "        w = 1.0 / (1.0 + np.exp(-xs)) + (0.0 if bias64 is None else np.take_along_axis(np.broadcast_to(bias64, x.shape), ids.astype(np.int64), axis=1))",
+     "bias leaks into the sigmoid weights"),
+    ("routing", "    for i in range(group_topn):\n", "    for i in range(1):\n",
+     "group score is the group max, not the top-n sum"),
+    ("routing", 'order = np.argsort(-score, axis=1, kind="stable")',
+     'order = (score.shape[1] - 1) - np.argsort(-score[:, ::-1], axis=1, kind="stable")',
+     "group ties go to the higher group index"),
+    ("routing", "key = e / e.sum(axis=1, keepdims=True, dtype=np.float32)",
+     "key = e / e.sum(axis=0, keepdims=True, dtype=np.float32)",
+     "softmax normalised over the wrong axis"),
+    ("routing", "    ids = order[:, :k].astype(np.int32)", "    ids = np.sort(order[:, :k], axis=1).astype(np.int32)",
+     "ids listed by index instead of by descending key"),
+    ("routing", "        scores = p / p.sum(axis=1, keepdims=True)\n\n    counts",
+     "        scores = p\n\n    counts", "full-E softmax scores not normalised"),
+    ("permutation", "padded[e + 1] = padded[e] + -(-counts[e] // tile) * tile",
+     "padded[e + 1] = padded[e] + counts[e]", "segments not padded to the tile"),
+    ("permutation", "slots = padded[e] + np.arange(t_idx.size, dtype=np.int64)",
+     "slots = padded[e] + np.arange(t_idx.size, dtype=np.int64)[::-1]",
+     "tokens placed in descending order inside a segment"),
+    ("permutation", "mn_limit[c] = min(start + (i + 1) * tile, start + int(counts[e]))",
+     "mn_limit[c] = start + (i + 1) * tile", "row limit ignores the segment end"),
+    ("permutation", "batch_idx[c] = e", "batch_idx[c] = e + off",
+     "tile map holds the global expert, not the local one"),
+    ("permutation", "e2p[t_idx * k + j_idx] = slots", "e2p[t_idx * k + (k - 1 - j_idx)] = slots",
+     "expanded index built with a transposed slot index"),
+    ("aux_loss", "return float(coeff) * num_experts / (topk * float(total_num_tokens) ** 2)",
+     "return float(coeff) * num_experts / (topk * float(total_num_tokens))",
+     "token count not squared"),
+    ("aux_loss", "column_sums = p.sum(axis=0)", "column_sums = p.sum(axis=0) / p.shape[0]",
+     "column sums averaged over local rows"),
+    ("aux_loss", "row = float(grad_loss) * _constant(total_num_tokens, num_experts, topk, coeff) * c",
+     "row = _constant(total_num_tokens, num_experts, topk, coeff) * c",
+     "upstream gradient ignored"),
+    ("front_end", "r = 1.0 / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + float(eps))",
+     "r = 1.0 / np.sqrt(np.mean(x * x, axis=1, keepdims=True))", "eps dropped"),
+    ("front_end", "y = x * r * g[None, :]", "y = x * r", "gamma not applied"),
+    ("front_end", "r = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)",
+     "r = np.ldexp(np.floor(np.ldexp(m, 8)), e - 8)", "bf16 rounding truncates"),
+    ("front_end", "    z = a @ w\n", "    z = a[:, ::-1] @ w\n", "hidden features reversed in the projection"),
+    ("front_end", "        sel = 1.0 / (1.0 + np.exp(-zs))", "        sel = 1.0 / (1.0 + np.exp(-zs)); sel = sel / sel.sum(axis=1, keepdims=True)",
+     "sigmoid affinities renormalised"),
+]
+
+
+def _mutated_module(modname, old, new):
+    path = os.path.join(ORACLE_DIR, modname + ".py")
+    with open(path) as f:
+        src = f.read()
+    assert src.count(old) >= 1, f"mutation anchor not found in {modname}: {old!r}"
+    mod = types.ModuleType(f"oracle.{modname}")
+    mod.__dict__["__package__"] = "oracle"
+    exec(compile(src.replace(old, new, 1), path + " (mutated)", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("modname,old,new,what", MUTATIONS, ids=[m[3] for m in MUTATIONS])
+def test_pins_catch_planted_mistake(monkeypatch, modname, old, new, what):
+    orig = importlib.import_module(f"oracle.{modname}")
+    mut = _mutated_module(modname, old, new)
+    for name, val in list(mut.__dict__.items()):
+        if callable(val) and getattr(val, "__module__", None) in (None, f"oracle.{modname}"):
+            monkeypatch.setattr(orig, name, val, raising=False)
+            if hasattr(oracle, name):
+                monkeypatch.setattr(oracle, name, val)
+    caught = []
+    for pin in PINS:
+        try:
+            pin()
+        except Exception as exc:  # an assertion or a crash both reveal the mistake
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught the planted mistake: {what}"
