@@ -1,0 +1,267 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE routing hot path on one MI355X.
+
+One step = one moe_route_permute call (score function, bias, grouped top-k,
+top-k, weights, per-expert counts, tile-padded offsets, both index maps and
+the per-tile expert map) over one batch of synthetic logits already resident
+in HBM.  Default workload: T=16384 tokens, E=256 experts, k=8, bf16 logits,
+grouped sigmoid with an fp32 correction bias (8 groups, keep 4, top-2-sum
+group score), routed scaling 2.5, tile 8.
+
+Timing: the K timed steps are captured once into a HIP graph and replayed
+(the per-call host cost of a ctypes call is larger than the GPU time of a
+step).  Step i reads rotating buffer set i mod R, with R sets spanning more
+than twice the 256 MB Infinity Cache, so every step starts cold.  The route
+kernel's average duration comes from HIP events the library records on the
+launch stream around each launch (a separate eager pass with a backlogged
+queue, so host latency does not enter the brackets).
+
+Prints one JSON line.  ``--gpus`` above 1 is refused: this path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 * 2 ** 20
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="deepseek_v3_like")
+    ap.add_argument("--rotate-mb", type=int, default=2 * 256 + 64,
+                    help="bytes spanned by the rotating buffer sets (MiB)")
+    ap.add_argument("--warm", action="store_true",
+                    help="also time a single buffer set (cache-warm), reported separately")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--json-out", default=None)
+    return ap.parse_args()
+
+
+def kernel_sources_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "top_expert_routing_amd", "csrc")
+    for name in ("route_kernels.hip", "device_common.hpp", "kernels.hpp"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def load_traffic(workload: str):
+    """HBM bytes per route-kernel launch from committed rocprofv3 --pmc runs,
+    or None when absent or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"route_kernel_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_sha256") != kernel_sources_digest():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(w, sample_T: int, seconds: float):
+    """The oracle (route + permute) on a bounded sample of the same workload."""
+    import numpy as np  # noqa: F401
+    import oracle
+    from workloads import route_inputs
+    logits, bias = route_inputs(w, T=sample_T)
+    reps, t_total = 0, 0.0
+    while t_total < seconds or reps < 1:
+        t0 = time.perf_counter()
+        r = oracle.route(logits, w.logits_dtype, w.k, score_fn=w.score_fn,
+                         pre_softmax=w.pre_softmax, n_group=w.n_group,
+                         topk_group=w.topk_group, group_topn=w.group_topn, renorm=w.renorm,
+                         scale=w.scale, bias=bias, bias_dtype=w.bias_dtype)
+        oracle.permute(r.ids, w.tile, num_experts=w.E)
+        t_total += time.perf_counter() - t0
+        reps += 1
+        if reps >= 50:
+            break
+    return sample_T * reps / t_total, reps, t_total
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py: this routing path runs on one GPU; --gpus {a.gpus} is not supported "
+              "(tokens shard independently across GPUs; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import top_expert_routing_amd as mr
+    from workloads import WORKLOADS, route_inputs
+
+    w = WORKLOADS[a.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    T, E, k, tile = w.T, w.E, w.k, w.tile
+
+    logits_np, bias_np = route_inputs(w)
+    if w.logits_dtype == "bf16":
+        x0 = torch.from_numpy(logits_np.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        x0 = torch.from_numpy(logits_np).to(dev)
+    b0 = None
+    if bias_np is not None:
+        b0 = torch.from_numpy(bias_np).to(dev) if w.bias_dtype == "f32" else \
+            torch.from_numpy(bias_np.view(np.int16)).to(dev).view(torch.bfloat16)
+    args = mr.make_route_args(T, E, k, score_fn=w.score_fn, pre_softmax=w.pre_softmax,
+                              n_group=w.n_group, topk_group=w.topk_group,
+                              group_topn=w.group_topn, renorm=w.renorm, scale=w.scale,
+                              logits_dtype=w.logits_dtype, bias_dtype=w.bias_dtype)
+
+    # rotating sets: inputs and outputs of a step, repeated past 2x the MALL
+    probe = mr.alloc_route_outputs(args, dev, permute=True, tile=tile)
+    out_bytes = sum(t.numel() * t.element_size() for t in vars(probe).values()
+                    if isinstance(t, torch.Tensor))
+    set_bytes = x0.numel() * x0.element_size() + out_bytes
+    R = max(2, math.ceil(max(a.rotate_mb * 2 ** 20, 2 * MALL_BYTES + 1) / set_bytes))
+    sets = []
+    for r in range(R):
+        x = x0.clone()
+        o = probe if r == 0 else mr.alloc_route_outputs(args, dev, permute=True, tile=tile)
+        sets.append((x, o))
+
+    def step(i):
+        x, o = sets[i % R]
+        mr.route_permute(args, x, b0, tile=tile, out=o)
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: a HIP graph of exactly K steps --------------------------------
+    K = a.steps
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=cap):
+        for i in range(K):
+            step(i)
+    g.replay()                      # first replay uploads the graph
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = gpu_ms / K
+
+    # ---- per-kernel durations: library event brackets, backlogged queue -------------
+    nprof = min(K, 200)
+    torch.cuda._sleep(int(2.4e9 * 0.05))      # ~50 ms of queued work ahead of the brackets
+    mr.moe_profile_begin()
+    for i in range(nprof):
+        step(i)
+    mr.moe_profile_end()
+    torch.cuda.synchronize()
+    kt = {}
+    for name, kind in (("route_kernel", mr.MOE_KERNEL_ROUTE), ("scan_kernel", mr.MOE_KERNEL_SCAN),
+                       ("scatter_kernel", mr.MOE_KERNEL_SCATTER)):
+        ms, n = mr.moe_profile_read(kind)
+        kt[name] = (ms / n * 1000.0) if n else None      # microseconds
+
+    # ---- algorithmic bytes --------------------------------------------------------------
+    o = sets[0][1]
+    total = int(o.total_num_padded_tokens.item())
+    ntiles = int(o.num_non_exiting_ctas.item())
+    lsz = 2 if w.logits_dtype == "bf16" else 4
+    route_bytes = T * E * lsz + (E * 4 if w.has_bias else 0) + T * k * 4 + T * k * 4
+    step_bytes = (route_bytes + T * k * 4 + total * 4 + 2 * ntiles * 4 + E * 4 + (E + 1) * 4 + 8)
+    route_us = kt["route_kernel"]
+    achieved = route_bytes / (route_us * 1e-6) / 1e9 if route_us else None
+    traffic = load_traffic(a.workload)
+
+    warm = None
+    if a.warm:
+        gw = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gw, stream=cap):
+            for i in range(K):
+                x, o0 = sets[0]
+                mr.route_permute(args, x, b0, tile=tile, out=o0)
+        gw.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        gw.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        warm = e0.elapsed_time(e1) / K
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        sample_T = min(T, 4096)
+        tps, reps, secs = cpu_baseline(w, sample_T, a.cpu_seconds)
+        cpu = {"value": tps, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"{sample_T} of {T} tokens of the same workload, oracle route + "
+                         f"permute, {reps} repetitions in {secs:.1f} s; NumPy single-threaded "
+                         f"(host reports {os.cpu_count()} CPUs)"}
+
+    line = {
+        "metric": "routed tokens/sec + achieved HBM GB/s, T=16384 E=256 k=8 grouped sigmoid",
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": a.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: {w.description}",
+            "T": T, "E": E, "k": k, "tile_tokens_dim": tile,
+            "logits_dtype": w.logits_dtype,
+            "step": "moe_route_permute (route + scan + scatter kernels)",
+            "timing": f"HIP graph of {K} steps, {R} rotating buffer sets "
+                      f"({R * set_bytes / 2**20:.0f} MiB, cold in L2 and MALL)",
+        },
+        "step_hbm_gbs": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "step_algorithmic_bytes": step_bytes,
+        "kernel_us": kt,
+        "roofline": {
+            "kernel": "route_kernel",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": route_bytes,
+        },
+        "cpu_baseline": cpu,
+        "wall_s_timed_region": wall,
+    }
+    if warm is not None:
+        line["warm_single_set_ms_per_step"] = warm
+    s = json.dumps(line)
+    print(s, flush=True)
+    if a.json_out:
+        with open(a.json_out, "w") as f:
+            f.write(s + "\n")
+
+
+if __name__ == "__main__":
+    main()

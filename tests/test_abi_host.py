@@ -1,0 +1,136 @@
+"""Host-only checks of the C ABI (no GPU): the library loads, exports every
+symbol include/moe_route.h declares, and rejects invalid arguments with the
+documented status before enqueueing anything.
+
+Every call here fails validation, so no kernel is ever launched; the non-NULL
+pointer values are never dereferenced."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import top_expert_routing_amd as mr
+from top_expert_routing_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_route.h")
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) -
+                  {"if", "while", "for", "sizeof", "return"})
+
+
+def test_header_symbols_exported():
+    names = _declared_functions()
+    assert "moe_route" in names and "rmsnorm_gate_route" in names
+    for n in names:
+        assert hasattr(_lib.lib, n), f"{n} declared in the header but not exported"
+    assert set(names) == set(_lib.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", mr.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}$", out, flags=re.M), n
+
+
+def _route(args, **kw):
+    p = dict(logits=FAKE, bias=None, ids=FAKE, weights=FAKE, scores=None, counts=None,
+             ws=None, ws_bytes=0)
+    p.update(kw)
+    return _lib.lib.moe_route(ctypes.byref(args), p["logits"], p["bias"], p["ids"], p["weights"],
+                              p["scores"], p["counts"], p["ws"], p["ws_bytes"], None)
+
+
+def _permute(args, tile=8, off=0, n_loc=None, **kw):
+    n_loc = args.num_experts if n_loc is None else n_loc
+    p = dict(ws=FAKE, ws_bytes=1 << 30, counts=FAKE, p2t=FAKE)
+    p.update(kw)
+    return _lib.lib.moe_route_permute(
+        ctypes.byref(args), tile, off, n_loc, FAKE, None, FAKE, FAKE, None, p["counts"], FAKE,
+        FAKE, FAKE, FAKE, p["p2t"], FAKE, FAKE, p["ws"], p["ws_bytes"], None)
+
+
+BAD_ROUTE = [
+    (dict(T=-1, E=8, k=2), mr.MOE_EINVAL),
+    (dict(T=4, E=0, k=1), mr.MOE_EINVAL),
+    (dict(T=4, E=8, k=0), mr.MOE_EINVAL),
+    (dict(T=4, E=8, k=9), mr.MOE_EINVAL),
+    (dict(T=4, E=4096, k=8), mr.MOE_EUNSUPPORTED),
+    (dict(T=4, E=256, k=65), mr.MOE_EUNSUPPORTED),
+    (dict(T=4, E=8, k=2, n_group=3, topk_group=1), mr.MOE_EINVAL),        # E % n_group
+    (dict(T=4, E=8, k=5, n_group=4, topk_group=2), mr.MOE_EINVAL),        # k > kept experts
+    (dict(T=4, E=8, k=2, n_group=2, topk_group=3), mr.MOE_EINVAL),        # topk_group > n_group
+    (dict(T=4, E=8, k=2, n_group=2, topk_group=1, group_topn=5), mr.MOE_EINVAL),
+    (dict(T=4, E=16, k=2, n_group=2, topk_group=1, group_topn=3), mr.MOE_EUNSUPPORTED),
+    (dict(T=4, E=60, k=4, n_group=4, topk_group=2), mr.MOE_EUNSUPPORTED),  # group of 15
+    (dict(T=4, E=8, k=2, n_group=-1), mr.MOE_EINVAL),
+    (dict(T=4, E=8, k=2, scale=float("inf")), mr.MOE_EINVAL),
+    (dict(T=4, E=8, k=2, logits_dtype="f16"), mr.MOE_EINVAL),
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD_ROUTE)
+def test_route_validation(kw, status):
+    kw = dict(kw)
+    args = mr.make_route_args(kw.pop("T"), kw.pop("E"), kw.pop("k"), **kw)
+    assert _route(args) == status, _lib.last_error_message()
+    assert _lib.last_error_message()
+    assert _permute(args) == status
+
+
+def test_route_null_pointers_and_workspace():
+    args = mr.make_route_args(100, 8, 2)
+    assert _route(args, logits=None) == mr.MOE_EINVAL
+    assert _route(args, ids=None) == mr.MOE_EINVAL
+    # counts requested without enough workspace
+    assert _route(args, counts=FAKE, ws=FAKE, ws_bytes=4) == mr.MOE_EWORKSPACE
+    assert _route(args, counts=FAKE, ws=None, ws_bytes=0) == mr.MOE_EWORKSPACE
+    assert _permute(args, ws_bytes=4) == mr.MOE_EWORKSPACE
+    assert _permute(args, counts=None) == mr.MOE_EINVAL
+    assert _permute(args, p2t=None) == mr.MOE_EINVAL
+    w = ctypes.c_void_p(0x1002)     # misaligned float32 weights
+    assert _lib.lib.moe_route(ctypes.byref(args), FAKE, None, FAKE, w, None, None, None, 0,
+                              None) == mr.MOE_EINVAL
+
+
+@pytest.mark.parametrize("tile,off,n_loc,status", [
+    (6, 0, 8, mr.MOE_EINVAL), (0, 0, 8, mr.MOE_EINVAL), (2048, 0, 8, mr.MOE_EINVAL),
+    (8, -1, 8, mr.MOE_EINVAL), (8, 4, 8, mr.MOE_EINVAL), (8, 0, 0, mr.MOE_EINVAL)])
+def test_permute_validation(tile, off, n_loc, status):
+    args = mr.make_route_args(100, 8, 2)
+    assert _permute(args, tile=tile, off=off, n_loc=n_loc) == status
+
+
+def test_aux_loss_validation():
+    L = _lib.lib.moe_aux_loss
+    f = ctypes.c_float
+    assert L(FAKE, FAKE, -1, 10, 8, 2, f(0.01), FAKE, None, None, FAKE, 1 << 20, None) == mr.MOE_EINVAL
+    assert L(FAKE, FAKE, 10, 0, 8, 2, f(0.01), FAKE, None, None, FAKE, 1 << 20, None) == mr.MOE_EINVAL
+    assert L(FAKE, FAKE, 10, 10, 8, 9, f(0.01), FAKE, None, None, FAKE, 1 << 20, None) == mr.MOE_EINVAL
+    assert L(FAKE, FAKE, 10, 10, 8, 2, f(0.01), None, None, None, FAKE, 1 << 20, None) == mr.MOE_EINVAL
+    assert L(FAKE, None, 10, 10, 8, 2, f(0.01), FAKE, None, None, FAKE, 1 << 20, None) == mr.MOE_EINVAL
+    assert L(None, FAKE, 10, 10, 8, 2, f(0.01), FAKE, None, None, FAKE, 1 << 20, None) == mr.MOE_EINVAL
+    assert L(FAKE, FAKE, 10, 10, 8, 2, f(0.01), FAKE, None, None, FAKE, 0, None) == mr.MOE_EWORKSPACE
+    assert L(FAKE, FAKE, 10, 10, 8, 2, f(float("nan")), FAKE, None, None, FAKE, 1 << 20, None) == mr.MOE_EINVAL
+
+
+def test_size_helpers():
+    assert mr.moe_max_padded_tokens(16384, 8, 256, 8) == 16384 * 8 + 256 * 7
+    assert mr.moe_max_tiles(16384, 8, 256, 8) == (16384 * 8 + 256 * 7) // 8
+    assert mr.moe_max_padded_tokens(10, 2, 8, 3) == -1
+    assert mr.moe_max_tiles(-1, 2, 8, 4) == -1
+    args = mr.make_route_args(16384, 256, 8)
+    assert mr.moe_route_workspace_size(args, 8, 256) >= 256 * 256 * 4
+    assert mr.moe_route_workspace_size(args, 8, 256) % 256 == 0
+    assert mr.moe_aux_loss_workspace_size(65536, 128) > 0
+
+
+def test_status_strings():
+    for s in range(5):
+        assert _lib.lib.moe_status_string(s).decode().startswith(_lib.STATUS_NAMES[s])
+    assert b"unknown" in _lib.lib.moe_status_string(99)

@@ -1,0 +1,222 @@
+"""GPU parity: moe_route / moe_route_permute through the C ABI against the oracle.
+
+Sizes: the four routing workloads at their full token counts (the oracle
+handles them in seconds), ragged token counts that leave partial blocks, and
+the degenerate cases the method has (T = 0, all-tied logits, a hot expert,
+k = E, bias deciding the groups, an expert-parallel shard, bf16 weights,
+tile 1 and large tiles)."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import (compare_permutation, compare_route, fetch_permutation, log, to_dev,
+                         weights_to_f64)
+from workloads import (WORKLOADS, constant_logits, route_inputs, skewed_logits,
+                       tie_heavy_logits, RouteWorkload, with_overrides)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+mr = pytest.importorskip("top_expert_routing_amd")
+
+
+def _args(w: RouteWorkload, T: int, weights_dtype="f32"):
+    return mr.make_route_args(T, w.E, w.k, score_fn=w.score_fn, pre_softmax=w.pre_softmax,
+                              n_group=w.n_group, topk_group=w.topk_group,
+                              group_topn=w.group_topn, renorm=w.renorm, scale=w.scale,
+                              logits_dtype=w.logits_dtype, bias_dtype=w.bias_dtype,
+                              weights_dtype=weights_dtype)
+
+
+def _oracle(w: RouteWorkload, logits, bias):
+    return oracle.route(logits, w.logits_dtype, w.k, score_fn=w.score_fn,
+                        pre_softmax=w.pre_softmax, n_group=w.n_group, topk_group=w.topk_group,
+                        group_topn=w.group_topn, renorm=w.renorm, scale=w.scale, bias=bias,
+                        bias_dtype=w.bias_dtype)
+
+
+def run_and_check(w: RouteWorkload, logits, bias, label, tile=None, weights_dtype="f32",
+                  scores=False, off=0, n_loc=None, permute=True):
+    T = logits.shape[0]
+    tile = w.tile if tile is None else tile
+    n_loc = w.E - off if n_loc is None else n_loc
+    log(f"[gpu] {label}: T={T} E={w.E} k={w.k} {w.score_fn} pre={w.pre_softmax} "
+        f"groups={w.n_group}/{w.topk_group} tile={tile} wdt={weights_dtype} loc={off}+{n_loc}")
+    args = _args(w, T, weights_dtype)
+    x = to_dev(logits, w.logits_dtype)
+    b = to_dev(bias, w.bias_dtype) if bias is not None else None
+    if permute:
+        out = mr.route_permute(args, x, b, tile=tile, local_expert_offset=off,
+                               local_num_experts=n_loc, scores=scores)
+    else:
+        out = mr.route(args, x, b, scores=scores, counts=True)
+    torch.cuda.synchronize()
+    ids = out.topk_ids.cpu().numpy()
+    wts = weights_to_f64(out.topk_weights)
+    ref = _oracle(w, logits, bias)
+    nex = compare_route(ref, ids, wts, w.k, weights_bf16=(weights_dtype == "bf16"), label=label)
+    if scores:
+        s = out.scores.cpu().numpy().astype(np.float64)
+        assert np.allclose(s, ref.scores, rtol=1e-5, atol=1e-30), label
+    if permute:
+        compare_permutation(fetch_permutation(out), ids, tile, off, n_loc, label)
+        if nex == 0:
+            P = oracle.permute(ref.ids, tile, local_expert_offset=off, local_num_experts=n_loc)
+            assert np.array_equal(out.expanded_idx_to_permuted_idx.cpu().numpy(), P.e2p), label
+    else:
+        counts = out.expert_counts.cpu().numpy()
+        assert np.array_equal(counts, np.bincount(ids.ravel(), minlength=w.E)), label
+    log(f"[gpu] {label}: ok, exempt tokens {nex}")
+    return out, ref
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload_full_size(name):
+    w = WORKLOADS[name]
+    logits, bias = route_inputs(w)
+    run_and_check(w, logits, bias, f"{name} full", scores=(w.aux_coeff is not None))
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+@pytest.mark.parametrize("T", [1, 63, 65, 257, 4097])
+def test_workload_ragged(name, T):
+    w = WORKLOADS[name]
+    logits, bias = route_inputs(w, T=T, seed=w.seed + T)
+    run_and_check(w, logits, bias, f"{name} T={T}")
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_route_only_with_counts(name):
+    w = WORKLOADS[name]
+    logits, bias = route_inputs(w, T=1000, seed=7)
+    run_and_check(w, logits, bias, f"{name} route-only", permute=False, scores=True)
+
+
+SMALL = [
+    # (E, k, score_fn, pre, n_group, topk_group, topn, renorm, scale, dtype, bias_std)
+    (8, 2, "softmax", True, 0, 0, 2, True, 1.0, "f32", None),
+    (8, 2, "softmax", True, 0, 0, 2, False, 1.0, "f32", None),
+    (8, 2, "softmax", False, 0, 0, 2, True, 1.0, "bf16", None),
+    (16, 4, "sigmoid", False, 4, 2, 2, True, 2.5, "f32", 0.05),
+    (16, 3, "sigmoid", False, 4, 1, 1, False, 1.0, "bf16", 0.05),
+    (32, 4, "softmax", True, 0, 0, 2, True, 1.0, "bf16", 0.1),      # pre-softmax with bias
+    (32, 4, "softmax", False, 4, 2, 2, True, 1.0, "f32", 0.1),      # grouped softmax
+    (64, 6, "sigmoid", False, 8, 3, 2, True, 1.5, "bf16", 0.01),
+    (60, 4, "softmax", True, 0, 0, 2, True, 1.0, "bf16", None),     # ragged rows, no vec loads
+    (100, 5, "sigmoid", False, 0, 0, 2, False, 1.0, "f32", 0.02),
+    (128, 8, "sigmoid", False, 8, 4, 2, True, 2.5, "bf16", 0.01),
+    (160, 6, "softmax", True, 0, 0, 2, True, 1.0, "bf16", None),
+    (256, 8, "sigmoid", False, 8, 4, 2, True, 2.5, "bf16", 0.01),
+    (256, 8, "sigmoid", False, 4, 2, 1, True, 1.0, "f32", 0.01),    # group spans two lanes
+    (384, 8, "sigmoid", False, 0, 0, 2, True, 2.5, "bf16", 0.01),
+    (512, 10, "softmax", True, 0, 0, 2, True, 1.0, "bf16", None),
+    (1024, 16, "softmax", False, 0, 0, 2, True, 1.0, "f32", None),
+    (2048, 40, "sigmoid", False, 16, 8, 2, True, 1.0, "bf16", 0.01),
+    (256, 64, "softmax", True, 0, 0, 2, True, 1.0, "bf16", None),   # k = 64
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"E{c[0]}k{c[1]}{c[2]}{'pre' if c[3] else ''}g{c[4]}"
+                                             for c in SMALL])
+def test_small_shapes(case):
+    E, k, sf, pre, ng, tg, tn, rn, sc, dt, bstd = case
+    w = RouteWorkload(name="small", seed=100 + E + k, T=777, E=E, k=k, score_fn=sf,
+                      pre_softmax=pre, n_group=ng, topk_group=tg, group_topn=tn, renorm=rn,
+                      scale=sc, logits_dtype=dt, bias_std=bstd, bias_dtype="f32", tile=8)
+    logits, bias = route_inputs(w)
+    run_and_check(w, logits, bias, f"small E={E} k={k}", scores=True)
+
+
+def test_constant_logits_all_ties():
+    for name in ("mixtral_like", "deepseek_v3_like", "qwen_moe_like"):
+        w = WORKLOADS[name]
+        logits = constant_logits(300, w.E, dtype=w.logits_dtype)
+        bias = None if not w.has_bias else np.zeros(w.E, np.float32)
+        out, ref = run_and_check(w, logits, bias, f"{name} constant")
+        assert np.all(out.topk_ids.cpu().numpy() == np.arange(w.k)[None, :])
+
+
+def test_tie_heavy_bf16():
+    w = with_overrides(WORKLOADS["qwen_moe_like"], T=2000)
+    logits = tie_heavy_logits(2000, w.E, seed=5, levels=(-1.0, 0.0, 0.5, 1.0, 1.5), dtype="bf16")
+    run_and_check(w, logits, None, "tie heavy bf16")
+    w2 = with_overrides(WORKLOADS["deepseek_v3_like"], T=2000)
+    logits2 = tie_heavy_logits(2000, w2.E, seed=6, dtype="bf16")
+    run_and_check(w2, logits2, np.zeros(w2.E, np.float32), "tie heavy grouped")
+
+
+def test_hot_expert():
+    w = with_overrides(WORKLOADS["mixtral_like"], T=3000)
+    logits = skewed_logits(3000, w.E, seed=9, hot_expert=3, shift=3.0)
+    out, _ = run_and_check(w, logits, None, "hot expert")
+    assert out.expert_counts.cpu().numpy()[3] > 2800
+
+
+def test_bias_decides_groups():
+    w = with_overrides(WORKLOADS["deepseek_v3_like"], T=1500)
+    logits, _ = route_inputs(w, T=1500, seed=11)
+    bias = np.zeros(w.E, np.float32)
+    bias[200:232] = 5.0        # group 6 always kept, its experts always first
+    out, ref = run_and_check(w, logits, bias, "bias decides groups")
+    assert np.all((out.topk_ids.cpu().numpy()[:, 0] >= 200) & (out.topk_ids.cpu().numpy()[:, 0] < 232))
+
+
+def test_k_equals_E():
+    w = RouteWorkload(name="kE", seed=31, T=500, E=8, k=8, score_fn="softmax", pre_softmax=True,
+                      renorm=False, tile=4)
+    logits, _ = route_inputs(w)
+    run_and_check(w, logits, None, "k=E", scores=True)
+
+
+def test_local_expert_shard():
+    w = with_overrides(WORKLOADS["deepseek_v3_like"], T=3000)
+    logits, bias = route_inputs(w, T=3000, seed=13)
+    run_and_check(w, logits, bias, "EP shard 64..128", off=64, n_loc=64)
+    run_and_check(w, logits, bias, "EP shard last expert", off=255, n_loc=1)
+
+
+def test_bf16_weights():
+    w = with_overrides(WORKLOADS["deepseek_v3_like"], T=2048)
+    logits, bias = route_inputs(w, T=2048, seed=17)
+    run_and_check(w, logits, bias, "bf16 weights", weights_dtype="bf16")
+
+
+@pytest.mark.parametrize("tile", [1, 2, 64, 256])
+def test_tiles(tile):
+    w = with_overrides(WORKLOADS["qwen_moe_like"], T=1111)
+    logits, _ = route_inputs(w, T=1111, seed=19)
+    run_and_check(w, logits, None, f"tile {tile}", tile=tile)
+
+
+def test_empty_batch():
+    w = WORKLOADS["deepseek_v3_like"]
+    log("[gpu] T=0")
+    args = _args(w, 0)
+    x = torch.empty((0, w.E), dtype=torch.bfloat16, device="cuda:0")
+    out = mr.alloc_route_outputs(args, "cuda:0", permute=True, tile=8)
+    out.expert_counts.fill_(7)
+    out.padded_offsets.fill_(7)
+    out.total_num_padded_tokens.fill_(7)
+    out.num_non_exiting_ctas.fill_(7)
+    mr.route_permute(args, x, None, tile=8, out=out)
+    torch.cuda.synchronize()
+    assert out.expert_counts.cpu().tolist() == [0] * w.E
+    assert out.padded_offsets.cpu().tolist() == [0] * (w.E + 1)
+    assert out.total_num_padded_tokens.item() == 0 and out.num_non_exiting_ctas.item() == 0
+
+
+def test_deterministic():
+    w = WORKLOADS["deepseek_v3_like"]
+    logits, bias = route_inputs(w)
+    args = _args(w, w.T)
+    x = to_dev(logits, "bf16")
+    b = to_dev(bias, "f32")
+    log("[gpu] determinism")
+    o1 = mr.route_permute(args, x, b, tile=8)
+    o2 = mr.route_permute(args, x, b, tile=8)
+    torch.cuda.synchronize()
+    for f in ("topk_ids", "topk_weights", "expert_counts", "expanded_idx_to_permuted_idx",
+              "cta_idx_xy_to_batch_idx", "cta_idx_xy_to_mn_limit"):
+        assert torch.equal(getattr(o1, f), getattr(o2, f)), f
+    tot = o1.total_num_padded_tokens.item()
+    assert torch.equal(o1.permuted_idx_to_token_idx[:tot], o2.permuted_idx_to_token_idx[:tot])

@@ -1,0 +1,484 @@
+// Host side of the C ABI declared in include/moe_route.h: argument validation,
+// workspace sizing, kernel-shape selection and launches.  Validation runs
+// before anything is enqueued; on error nothing is written.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "kernels.hpp"
+#include "moe_route.h"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+thread_local int32_t g_hip_err = 0;
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof g_msg, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+moe_status hip_fail(hipError_t e, const char* what) {
+  g_hip_err = (int32_t)e;
+  return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+void clear_error() {
+  g_msg[0] = '\0';
+  g_hip_err = 0;
+}
+
+// ---- profiling aid: HIP events around each launch while enabled ------------------
+struct ProfRecord {
+  int kind;
+  hipEvent_t start, stop;
+};
+struct Profiler {
+  std::mutex mu;
+  std::atomic<bool> on{false};
+  std::vector<ProfRecord> pending;
+  std::vector<hipEvent_t> pool;
+  double total_ms[MOE_KERNEL_KINDS] = {};
+  int64_t launches[MOE_KERNEL_KINDS] = {};
+};
+Profiler& profiler() {
+  static Profiler* p = new Profiler();   // never destroyed: events may outlive exit order
+  return *p;
+}
+hipEvent_t take_event(Profiler& P) {
+  if (!P.pool.empty()) {
+    hipEvent_t e = P.pool.back();
+    P.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <class F>
+hipError_t launch_with_profile(int kind, hipStream_t stream, F&& f) {
+  Profiler& P = profiler();
+  if (!P.on.load(std::memory_order_relaxed)) return f();
+  std::lock_guard<std::mutex> lk(P.mu);
+  hipEvent_t a = take_event(P), b = take_event(P);
+  if (a == nullptr || b == nullptr) return f();
+  hipError_t e = hipEventRecord(a, stream);
+  if (e != hipSuccess) return e;
+  e = f();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(b, stream);
+  if (e != hipSuccess) return e;
+  P.pending.push_back({kind, a, b});
+  return hipSuccess;
+}
+
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+int next_pow2(int v) {
+  int p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+constexpr int kMaxExperts = 2048;
+constexpr int kMaxTopK = 64;
+
+bool grouping_on(const moe_route_args& a) {
+  return a.n_group > 1 && a.topk_group > 0 && a.topk_group < a.n_group;
+}
+
+// Shape of the route kernel for one call: lanes per token and experts per lane.
+struct Shape {
+  int lpt = 0, epl = 0, lg = 1;
+};
+
+bool pick_shape(const moe_route_args& a, Shape* s) {
+  const int E = a.num_experts;
+  if (!grouping_on(a)) {
+    // ungrouped: 32 experts per lane once rows are long enough, fewer lanes
+    // per token for short rows so that a wavefront carries many tokens
+    int epl = E <= 32 ? 8 : (E <= 64 ? 16 : 32);
+    int lpt = next_pow2((E + epl - 1) / epl);
+    if (lpt > 64) return false;
+    s->lpt = lpt;
+    s->epl = epl;
+    s->lg = 1;
+    return true;
+  }
+  const int gsz = E / a.n_group;
+  for (int epl : {32, 16, 8, 4}) {
+    if (gsz % epl) continue;
+    const int lg = gsz / epl;
+    const int lpt = next_pow2((E + epl - 1) / epl);
+    if (!is_pow2(lg) || lg > lpt || lpt > 64) continue;
+    s->lpt = lpt;
+    s->epl = epl;
+    s->lg = lg;
+    return true;
+  }
+  return false;
+}
+
+moe_status validate_route(const moe_route_args* a, Shape* shape) {
+  if (a == nullptr) return fail(MOE_EINVAL, "args is NULL");
+  if (a->num_tokens < 0) return fail(MOE_EINVAL, "num_tokens < 0");
+  if (a->num_experts < 1) return fail(MOE_EINVAL, "num_experts < 1");
+  if (a->num_experts > kMaxExperts)
+    return fail(MOE_EUNSUPPORTED, "num_experts > %d", kMaxExperts);
+  if (a->top_k < 1 || a->top_k > a->num_experts)
+    return fail(MOE_EINVAL, "top_k must be in [1, num_experts]");
+  if (a->top_k > kMaxTopK) return fail(MOE_EUNSUPPORTED, "top_k > %d", kMaxTopK);
+  if (a->score_fn != MOE_SOFTMAX && a->score_fn != MOE_SIGMOID)
+    return fail(MOE_EINVAL, "score_fn must be MOE_SOFTMAX or MOE_SIGMOID");
+  if (a->logits_dtype != MOE_F32 && a->logits_dtype != MOE_BF16)
+    return fail(MOE_EINVAL, "logits_dtype must be MOE_F32 or MOE_BF16");
+  if (a->bias_dtype != MOE_F32 && a->bias_dtype != MOE_BF16)
+    return fail(MOE_EINVAL, "bias_dtype must be MOE_F32 or MOE_BF16");
+  if (a->weights_dtype != MOE_F32 && a->weights_dtype != MOE_BF16)
+    return fail(MOE_EINVAL, "weights_dtype must be MOE_F32 or MOE_BF16");
+  if (!std::isfinite(a->routed_scaling_factor))
+    return fail(MOE_EINVAL, "routed_scaling_factor is not finite");
+  if (a->n_group < 0 || a->topk_group < 0) return fail(MOE_EINVAL, "negative group parameter");
+  if (a->n_group > 1 && a->topk_group > a->n_group)
+    return fail(MOE_EINVAL, "topk_group > n_group");
+  if (grouping_on(*a)) {
+    if (a->num_experts % a->n_group)
+      return fail(MOE_EINVAL, "num_experts %% n_group != 0");
+    const int gsz = a->num_experts / a->n_group;
+    if (a->group_score_topn < 1 || a->group_score_topn > gsz)
+      return fail(MOE_EINVAL, "group_score_topn must be in [1, E / n_group]");
+    if (a->top_k > a->topk_group * gsz)
+      return fail(MOE_EINVAL, "top_k exceeds the experts of the kept groups");
+    if (a->group_score_topn > 2)
+      return fail(MOE_EUNSUPPORTED, "group_score_topn > 2");
+  }
+  if (!pick_shape(*a, shape))
+    return fail(MOE_EUNSUPPORTED,
+                "no kernel shape for E=%d, n_group=%d: the group size must be a multiple of 4 "
+                "whose lane count is a power of two",
+                a->num_experts, a->n_group);
+  return MOE_OK;
+}
+
+int num_blocks(int T) { return (T + moe::kTokensPerBlock - 1) / moe::kTokensPerBlock; }
+
+size_t route_ws_bytes(const moe_route_args& a, int loc_n) {
+  return align256((size_t)num_blocks(a.num_tokens) * loc_n * sizeof(int32_t));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+moe::RouteParams make_params(const moe_route_args& a, const Shape& sh, const void* logits,
+                             const void* bias, int32_t* ids, void* weights, float* scores,
+                             int32_t* hist, int loc_off, int loc_n) {
+  moe::RouteParams p{};
+  p.logits = logits;
+  p.bias = bias;
+  p.ids = ids;
+  p.weights = weights;
+  p.scores = scores;
+  p.hist = hist;
+  p.T = a.num_tokens;
+  p.E = a.num_experts;
+  p.k = a.top_k;
+  p.kind = a.score_fn == MOE_SIGMOID
+               ? moe::kKindSigmoid
+               : (a.use_pre_softmax ? moe::kKindSoftmaxPre : moe::kKindSoftmaxPost);
+  p.bias_bf16 = a.bias_dtype == MOE_BF16;
+  p.weights_bf16 = a.weights_dtype == MOE_BF16;
+  p.grouped = grouping_on(a);
+  p.n_group = a.n_group;
+  p.topk_group = a.topk_group;
+  p.topn = a.group_score_topn;
+  p.lg = sh.lg;
+  p.renorm = a.renormalize != 0;
+  p.scale = a.routed_scaling_factor;
+  const size_t esz = a.logits_dtype == MOE_BF16 ? 2 : 4;
+  p.vec = ((size_t)a.num_experts * esz) % 16 == 0 && aligned(logits, 16) &&
+          (sh.epl * esz) % 16 == 0;
+  p.loc_off = loc_off;
+  p.loc_n = loc_n;
+  p.hmask_len = hist != nullptr ? (loc_n + 1) & ~1 : 0;
+  p.cap = a.top_k <= 32 ? 32 : 64;
+  return p;
+}
+
+moe_status launch_route_checked(const moe::RouteParams& p, const Shape& sh, bool bf16,
+                                hipStream_t stream) {
+  const size_t lds = moe::route_lds_bytes(sh.lpt, sh.epl, p.hmask_len, p.cap, p.k);
+  if (lds > 160 * 1024)
+    return fail(MOE_EUNSUPPORTED, "route kernel needs %zu bytes of LDS", lds);
+  hipError_t e = launch_with_profile(MOE_KERNEL_ROUTE, stream, [&] {
+    return moe::launch_route(p, sh.lpt, sh.epl, bf16, num_blocks(p.T), stream);
+  });
+  if (e != hipSuccess) return hip_fail(e, "route_kernel launch");
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
+    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: outside the implemented limits";
+    case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace too small";
+    case MOE_EHIP: return "MOE_EHIP: HIP launch failed";
+  }
+  return "unknown moe_status";
+}
+
+const char* moe_last_error_message(void) { return g_msg; }
+
+moe_status moe_profile_begin(void) {
+  clear_error();
+  Profiler& P = profiler();
+  std::lock_guard<std::mutex> lk(P.mu);
+  for (auto& r : P.pending) {
+    P.pool.push_back(r.start);
+    P.pool.push_back(r.stop);
+  }
+  P.pending.clear();
+  for (int i = 0; i < MOE_KERNEL_KINDS; ++i) {
+    P.total_ms[i] = 0.0;
+    P.launches[i] = 0;
+  }
+  P.on.store(true);
+  return MOE_OK;
+}
+
+moe_status moe_profile_end(void) {
+  profiler().on.store(false);
+  return MOE_OK;
+}
+
+moe_status moe_profile_read(int32_t kind, double* total_ms, int64_t* launches) {
+  clear_error();
+  if (kind < 0 || kind >= MOE_KERNEL_KINDS || total_ms == nullptr || launches == nullptr)
+    return fail(MOE_EINVAL, "invalid kernel kind or NULL output");
+  Profiler& P = profiler();
+  std::lock_guard<std::mutex> lk(P.mu);
+  std::vector<ProfRecord> keep;
+  for (auto& r : P.pending) {
+    if (r.kind != kind) {
+      keep.push_back(r);
+      continue;
+    }
+    hipError_t e = hipEventSynchronize(r.stop);
+    float ms = 0.0f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess) return hip_fail(e, "profile event");
+    P.total_ms[kind] += ms;
+    P.launches[kind] += 1;
+    P.pool.push_back(r.start);
+    P.pool.push_back(r.stop);
+  }
+  P.pending.swap(keep);
+  *total_ms = P.total_ms[kind];
+  *launches = P.launches[kind];
+  return MOE_OK;
+}
+int32_t moe_last_hip_error(void) { return g_hip_err; }
+
+int64_t moe_max_padded_tokens(int32_t T, int32_t k, int32_t loc_n, int32_t tile) {
+  if (T < 0 || k < 1 || loc_n < 1 || !is_pow2(tile)) return -1;
+  return (int64_t)T * k + (int64_t)loc_n * (tile - 1);
+}
+
+int64_t moe_max_tiles(int32_t T, int32_t k, int32_t loc_n, int32_t tile) {
+  const int64_t m = moe_max_padded_tokens(T, k, loc_n, tile);
+  return m < 0 ? -1 : m / tile;
+}
+
+size_t moe_route_workspace_size(const moe_route_args* a, int32_t tile, int32_t loc_n) {
+  (void)tile;
+  if (a == nullptr || a->num_tokens < 0 || loc_n < 1) return 0;
+  return route_ws_bytes(*a, loc_n);
+}
+
+moe_status moe_route(const moe_route_args* args, const void* logits, const void* bias,
+                     int32_t* topk_ids, void* topk_weights, float* scores,
+                     int32_t* expert_counts, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+  clear_error();
+  Shape sh;
+  moe_status st = validate_route(args, &sh);
+  if (st != MOE_OK) return st;
+  const moe_route_args& a = *args;
+  const int T = a.num_tokens, E = a.num_experts;
+  if (T == 0) {
+    if (expert_counts == nullptr) return MOE_OK;
+    hipError_t e = moe::launch_empty_outputs(expert_counts, E, nullptr, nullptr, nullptr, stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "empty_outputs launch");
+  }
+  if (logits == nullptr || topk_ids == nullptr || topk_weights == nullptr)
+    return fail(MOE_EINVAL, "logits, topk_ids and topk_weights are required");
+  if (a.weights_dtype == MOE_F32 && !aligned(topk_weights, 4))
+    return fail(MOE_EINVAL, "topk_weights must be 4-byte aligned");
+  int32_t* hist = nullptr;
+  if (expert_counts != nullptr) {
+    const size_t need = route_ws_bytes(a, E);
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(MOE_EWORKSPACE, "workspace needs %zu bytes", need);
+    hist = static_cast<int32_t*>(workspace);
+  }
+  const moe::RouteParams p =
+      make_params(a, sh, logits, bias, topk_ids, topk_weights, scores, hist, 0, E);
+  st = launch_route_checked(p, sh, a.logits_dtype == MOE_BF16, stream);
+  if (st != MOE_OK) return st;
+  if (hist != nullptr) {
+    hipError_t e = launch_with_profile(MOE_KERNEL_SCAN, stream, [&] {
+      return moe::launch_scan(hist, num_blocks(T), E, expert_counts, stream);
+    });
+    if (e != hipSuccess) return hip_fail(e, "scan_kernel launch");
+  }
+  return MOE_OK;
+}
+
+moe_status moe_route_permute(const moe_route_args* args, int32_t tile, int32_t loc_off,
+                             int32_t loc_n, const void* logits, const void* bias,
+                             int32_t* topk_ids, void* topk_weights, float* scores,
+                             int32_t* expert_counts, int32_t* padded_offsets,
+                             int32_t* total_num_padded_tokens, int32_t* num_non_exiting_ctas,
+                             int32_t* e2p, int32_t* p2t, int32_t* batch_idx, int32_t* mn_limit,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  clear_error();
+  Shape sh;
+  moe_status st = validate_route(args, &sh);
+  if (st != MOE_OK) return st;
+  const moe_route_args& a = *args;
+  const int T = a.num_tokens, E = a.num_experts;
+  if (!is_pow2(tile) || tile > 1024)
+    return fail(MOE_EINVAL, "tile_tokens_dim must be a power of two in [1, 1024]");
+  if (loc_off < 0 || loc_n < 1 || (int64_t)loc_off + loc_n > E)
+    return fail(MOE_EINVAL, "local experts [off, off + n) must lie inside [0, E)");
+  if (expert_counts == nullptr || padded_offsets == nullptr ||
+      total_num_padded_tokens == nullptr || num_non_exiting_ctas == nullptr)
+    return fail(MOE_EINVAL, "bookkeeping outputs are required");
+  if ((int64_t)T * a.top_k + (int64_t)loc_n * (tile - 1) > INT32_MAX)
+    return fail(MOE_EUNSUPPORTED, "padded token count exceeds int32");
+  if (T == 0) {
+    hipError_t e = moe::launch_empty_outputs(expert_counts, loc_n, padded_offsets,
+                                             total_num_padded_tokens, num_non_exiting_ctas,
+                                             stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "empty_outputs launch");
+  }
+  if (logits == nullptr || topk_ids == nullptr || topk_weights == nullptr || e2p == nullptr ||
+      p2t == nullptr || batch_idx == nullptr || mn_limit == nullptr)
+    return fail(MOE_EINVAL, "a required pointer is NULL");
+  if (a.weights_dtype == MOE_F32 && !aligned(topk_weights, 4))
+    return fail(MOE_EINVAL, "topk_weights must be 4-byte aligned");
+  const size_t need = route_ws_bytes(a, loc_n);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(MOE_EWORKSPACE, "workspace needs %zu bytes", need);
+  int32_t* hist = static_cast<int32_t*>(workspace);
+  const int nb = num_blocks(T);
+
+  const moe::RouteParams p =
+      make_params(a, sh, logits, bias, topk_ids, topk_weights, scores, hist, loc_off, loc_n);
+  st = launch_route_checked(p, sh, a.logits_dtype == MOE_BF16, stream);
+  if (st != MOE_OK) return st;
+  hipError_t e = launch_with_profile(MOE_KERNEL_SCAN, stream, [&] {
+    return moe::launch_scan(hist, nb, loc_n, expert_counts, stream);
+  });
+  if (e != hipSuccess) return hip_fail(e, "scan_kernel launch");
+
+  moe::ScatterParams q{};
+  q.ids = topk_ids;
+  q.T = T;
+  q.k = a.top_k;
+  q.El = loc_n;
+  q.off = loc_off;
+  q.tile = tile;
+  q.counts = expert_counts;
+  q.excl = hist;
+  q.e2p = e2p;
+  q.p2t = p2t;
+  q.padded_offsets = padded_offsets;
+  q.total_out = total_num_padded_tokens;
+  q.nctas_out = num_non_exiting_ctas;
+  q.batch_idx = batch_idx;
+  q.mn_limit = mn_limit;
+  e = launch_with_profile(MOE_KERNEL_SCATTER, stream, [&] { return moe::launch_scatter(q, nb, stream); });
+  if (e != hipSuccess) return hip_fail(e, "scatter_kernel launch");
+  return MOE_OK;
+}
+
+size_t moe_aux_loss_workspace_size(int64_t rows, int32_t num_experts) {
+  if (rows < 0 || num_experts < 1) return 0;
+  return align256((size_t)moe::aux_fwd_blocks(rows, num_experts) * sizeof(double));
+}
+
+moe_status moe_aux_loss(const float* probs, const int32_t* tokens_per_expert, int64_t rows,
+                        int64_t total_num_tokens, int32_t E, int32_t top_k, float coeff,
+                        float* loss, const float* grad_loss, float* grad_probs, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  clear_error();
+  if (rows < 0) return fail(MOE_EINVAL, "rows < 0");
+  if (total_num_tokens < 1) return fail(MOE_EINVAL, "total_num_tokens < 1");
+  if (E < 1) return fail(MOE_EINVAL, "num_experts < 1");
+  if (E > 2048) return fail(MOE_EUNSUPPORTED, "num_experts > 2048");
+  if (top_k < 1 || top_k > E) return fail(MOE_EINVAL, "top_k must be in [1, num_experts]");
+  if (!std::isfinite(coeff)) return fail(MOE_EINVAL, "coeff is not finite");
+  if (loss == nullptr && grad_probs == nullptr)
+    return fail(MOE_EINVAL, "neither loss nor grad_probs requested");
+  if (tokens_per_expert == nullptr) return fail(MOE_EINVAL, "tokens_per_expert is NULL");
+  if (rows * (int64_t)E > ((int64_t)1 << 40)) return fail(MOE_EUNSUPPORTED, "probs too large");
+  const double scale =
+      (double)coeff * E / ((double)top_k * (double)total_num_tokens * (double)total_num_tokens);
+  if (loss != nullptr) {
+    if (rows > 0 && probs == nullptr) return fail(MOE_EINVAL, "probs is NULL");
+    const size_t need = moe_aux_loss_workspace_size(rows, E);
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(MOE_EWORKSPACE, "workspace needs %zu bytes", need);
+  }
+  if (loss != nullptr) {
+    const int nb = moe::aux_fwd_blocks(rows, E);
+    hipError_t e = launch_with_profile(MOE_KERNEL_AUX_FWD, stream, [&] {
+      return moe::launch_aux_fwd(probs, tokens_per_expert, rows, E, scale,
+                                 static_cast<double*>(workspace), nb, loss, stream);
+    });
+    if (e != hipSuccess) return hip_fail(e, "aux forward launch");
+  }
+  if (grad_probs != nullptr && rows > 0) {
+    hipError_t e = launch_with_profile(MOE_KERNEL_AUX_BWD, stream, [&] {
+      return moe::launch_aux_bwd(tokens_per_expert, rows, E, scale, grad_loss, grad_probs,
+                                 stream);
+    });
+    if (e != hipSuccess) return hip_fail(e, "aux backward launch");
+  }
+  return MOE_OK;
+}
+
+size_t rmsnorm_gate_route_workspace_size(int32_t T, int32_t H, int32_t E) {
+  (void)T;
+  (void)H;
+  (void)E;
+  return 0;
+}
+
+moe_status rmsnorm_gate_route(const void* hidden, const void* gamma, const void* router_weights,
+                              const void* router_bias, int32_t dtype, int32_t T, int32_t H,
+                              int32_t E, float eps, int32_t top_k, int32_t act_fn, void* normed,
+                              int32_t* topk_ids, void* affinities, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  clear_error();
+  (void)hidden; (void)gamma; (void)router_weights; (void)router_bias; (void)dtype; (void)T;
+  (void)H; (void)E; (void)eps; (void)top_k; (void)act_fn; (void)normed; (void)topk_ids;
+  (void)affinities; (void)workspace; (void)workspace_bytes; (void)stream;
+  return fail(MOE_EUNSUPPORTED, "rmsnorm_gate_route is not built in this library version");
+}
+
+}  // extern "C"
