@@ -215,8 +215,12 @@ def test_deterministic():
     o1 = mr.route_permute(args, x, b, tile=8)
     o2 = mr.route_permute(args, x, b, tile=8)
     torch.cuda.synchronize()
-    for f in ("topk_ids", "topk_weights", "expert_counts", "expanded_idx_to_permuted_idx",
-              "cta_idx_xy_to_batch_idx", "cta_idx_xy_to_mn_limit"):
+    for f in ("topk_ids", "topk_weights", "expert_counts", "padded_offsets",
+              "total_num_padded_tokens", "num_non_exiting_ctas", "expanded_idx_to_permuted_idx"):
         assert torch.equal(getattr(o1, f), getattr(o2, f)), f
+    # entries at or beyond the totals are documented as not written
     tot = o1.total_num_padded_tokens.item()
+    nt = o1.num_non_exiting_ctas.item()
     assert torch.equal(o1.permuted_idx_to_token_idx[:tot], o2.permuted_idx_to_token_idx[:tot])
+    assert torch.equal(o1.cta_idx_xy_to_batch_idx[:nt], o2.cta_idx_xy_to_batch_idx[:nt])
+    assert torch.equal(o1.cta_idx_xy_to_mn_limit[:nt], o2.cta_idx_xy_to_mn_limit[:nt])

@@ -55,12 +55,30 @@ class moe_route_args(ctypes.Structure):
     ]
 
 
+def _hip_runtimes():
+    try:
+        with open("/proc/self/maps") as f:
+            paths = {l.split()[-1] for l in f if "libamdhip64" in l}
+    except OSError:
+        return set()
+    return {os.path.realpath(p) for p in paths}
+
+
 def _load():
+    # torch supplies device memory and streams; it ships its own HIP runtime.
+    # Import it first so that the library's libamdhip64.so.7 dependency binds
+    # to that same runtime (matching SONAME): one process, one HIP runtime.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it with `python top_expert_routing_amd/_build.py` "
             "(the routing path has no fallback)")
     lib = ctypes.CDLL(LIB_PATH)
+    runtimes = _hip_runtimes()
+    if len(runtimes) > 1:
+        raise ImportError("two HIP runtimes are loaded in this process (" +
+                          ", ".join(sorted(runtimes)) + "); import torch before anything "
+                          "that loads /opt/rocm's libamdhip64")
     vp, i32, i64, sz, f32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
                              ctypes.c_float)
     args_p = ctypes.POINTER(moe_route_args)
