@@ -206,6 +206,7 @@ moe::RouteParams make_params(const moe_route_args& a, const Shape& sh, const voi
   const size_t esz = a.logits_dtype == MOE_BF16 ? 2 : 4;
   p.vec = ((size_t)a.num_experts * esz) % 16 == 0 && aligned(logits, 16) &&
           (sh.epl * esz) % 16 == 0;
+  p.bias_vec = bias != nullptr && aligned(bias, 16);
   p.loc_off = loc_off;
   p.loc_n = loc_n;
   p.hmask_len = hist != nullptr ? (loc_n + 1) & ~1 : 0;
@@ -215,7 +216,8 @@ moe::RouteParams make_params(const moe_route_args& a, const Shape& sh, const voi
 
 moe_status launch_route_checked(const moe::RouteParams& p, const Shape& sh, bool bf16,
                                 hipStream_t stream) {
-  const size_t lds = moe::route_lds_bytes(sh.lpt, sh.epl, p.hmask_len, p.cap, p.k);
+  const size_t lds = moe::route_lds_bytes(sh.lpt, sh.epl, p.hmask_len, p.cap, p.k,
+                                          p.grouped ? p.n_group : 0);
   if (lds > 160 * 1024)
     return fail(MOE_EUNSUPPORTED, "route kernel needs %zu bytes of LDS", lds);
   hipError_t e = launch_with_profile(MOE_KERNEL_ROUTE, stream, [&] {
@@ -463,10 +465,9 @@ moe_status moe_aux_loss(const float* probs, const int32_t* tokens_per_expert, in
 }
 
 size_t rmsnorm_gate_route_workspace_size(int32_t T, int32_t H, int32_t E) {
-  (void)T;
-  (void)H;
-  (void)E;
-  return 0;
+  if (T < 1 || H < 128 || H % 128 || E < 1) return 0;
+  const int nchunks = H / moe::front_end_kchunk(H);
+  return align256((size_t)nchunks * T * E * sizeof(float));
 }
 
 moe_status rmsnorm_gate_route(const void* hidden, const void* gamma, const void* router_weights,
@@ -475,10 +476,46 @@ moe_status rmsnorm_gate_route(const void* hidden, const void* gamma, const void*
                               int32_t* topk_ids, void* affinities, void* workspace,
                               size_t workspace_bytes, hipStream_t stream) {
   clear_error();
-  (void)hidden; (void)gamma; (void)router_weights; (void)router_bias; (void)dtype; (void)T;
-  (void)H; (void)E; (void)eps; (void)top_k; (void)act_fn; (void)normed; (void)topk_ids;
-  (void)affinities; (void)workspace; (void)workspace_bytes; (void)stream;
-  return fail(MOE_EUNSUPPORTED, "rmsnorm_gate_route is not built in this library version");
+  if (dtype != MOE_BF16 && dtype != MOE_F16) return fail(MOE_EINVAL, "dtype must be MOE_BF16 or MOE_F16");
+  if (T < 1) return fail(MOE_EINVAL, "T must be >= 1");
+  if (T > 128) return fail(MOE_EINVAL, "T must be <= 128 (single-tile decode front end)");
+  if (H < 128 || H % 128) return fail(MOE_EINVAL, "H must be a positive multiple of 128");
+  if (H > 16384) return fail(MOE_EUNSUPPORTED, "H > 16384");
+  if (E < 1) return fail(MOE_EINVAL, "E must be >= 1");
+  if (E % 16 || E > 512) return fail(MOE_EUNSUPPORTED, "E must be a multiple of 16, at most 512");
+  if (top_k < 1 || top_k > E) return fail(MOE_EINVAL, "top_k must be in [1, E]");
+  if (top_k > 64) return fail(MOE_EUNSUPPORTED, "top_k > 64");
+  if (act_fn != MOE_SOFTMAX && act_fn != MOE_SIGMOID) return fail(MOE_EINVAL, "act_fn must be MOE_SOFTMAX or MOE_SIGMOID");
+  if (!std::isfinite(eps) || eps < 0.0f) return fail(MOE_EINVAL, "eps must be finite and >= 0");
+  if (hidden == nullptr || gamma == nullptr || router_weights == nullptr || normed == nullptr ||
+      topk_ids == nullptr || affinities == nullptr)
+    return fail(MOE_EINVAL, "a required pointer is NULL");
+  if (!aligned(hidden, 16) || !aligned(gamma, 16) || !aligned(router_weights, 16) ||
+      !aligned(normed, 16) || !aligned(affinities, 2) || (router_bias && !aligned(router_bias, 2)))
+    return fail(MOE_EINVAL, "hidden, gamma, router_weights and normed must be 16-byte aligned");
+  const size_t need = rmsnorm_gate_route_workspace_size(T, H, E);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(MOE_EWORKSPACE, "workspace needs %zu bytes", need);
+  moe::FrontEndParams q{};
+  q.hidden = hidden;
+  q.gamma = gamma;
+  q.W = router_weights;
+  q.rbias = router_bias;
+  q.f16 = dtype == MOE_F16;
+  q.T = T;
+  q.H = H;
+  q.E = E;
+  q.k = top_k;
+  q.eps = eps;
+  q.act_sigmoid = act_fn == MOE_SIGMOID;
+  q.normed = normed;
+  q.ids = topk_ids;
+  q.aff = affinities;
+  q.partial = static_cast<float*>(workspace);
+  hipError_t e = launch_with_profile(MOE_KERNEL_FRONT_END, stream,
+                                     [&] { return moe::launch_front_end(q, stream); });
+  if (e != hipSuccess) return hip_fail(e, "front end launch");
+  return MOE_OK;
 }
 
 }  // extern "C"

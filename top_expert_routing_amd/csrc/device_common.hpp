@@ -9,6 +9,7 @@ namespace moe {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -25,6 +26,11 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 __device__ __forceinline__ uint32_t ord_key(float f) {
   uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inverse of ord_key.
+__device__ __forceinline__ float unord_key(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
 // Selection order as one unsigned 64-bit integer: larger key first, then the
@@ -55,48 +61,161 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Reductions over a cluster of W consecutive lanes (W a power of two <= 64).
+// ---- cross-lane primitives -------------------------------------------------------
+// DPP controls (gfx9 encoding): quad permutes, mirrors inside a 16-lane row and
+// row shifts.  A DPP move is one VALU op; no LDS round trip.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i inside each 8 lanes
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i inside each 16 lanes
+constexpr int kDppRowShr = 0x110;     // + d: lane i reads lane i-d of its row (0 outside)
+constexpr int kDppRowShl = 0x100;     // + d: lane i reads lane i+d of its row (0 outside)
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, true);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// Butterfly-style all-reduce over clusters of W consecutive lanes (W a power of
+// two <= 64).  W <= 16 uses DPP (quad permutes, then half-row and row mirrors:
+// after reducing inside quads, the mirror partner always lies in the other
+// half); W >= 32 adds ds_bpermute steps.
+template <int W, class T, class Op>
+__device__ __forceinline__ T cl_reduce(T v, Op op) {
+  if constexpr (W >= 2) {
+    if constexpr (sizeof(T) == 8) v = op(v, dpp_u64<kDppXor1>(v));
+    else if constexpr (__is_same(T, float)) v = op(v, dpp_f<kDppXor1>(v));
+    else v = op(v, dpp_i<kDppXor1>(v));
+  }
+  if constexpr (W >= 4) {
+    if constexpr (sizeof(T) == 8) v = op(v, dpp_u64<kDppXor2>(v));
+    else if constexpr (__is_same(T, float)) v = op(v, dpp_f<kDppXor2>(v));
+    else v = op(v, dpp_i<kDppXor2>(v));
+  }
+  if constexpr (W >= 8) {
+    if constexpr (sizeof(T) == 8) v = op(v, dpp_u64<kDppHalfMirror>(v));
+    else if constexpr (__is_same(T, float)) v = op(v, dpp_f<kDppHalfMirror>(v));
+    else v = op(v, dpp_i<kDppHalfMirror>(v));
+  }
+  if constexpr (W >= 16) {
+    if constexpr (sizeof(T) == 8) v = op(v, dpp_u64<kDppMirror>(v));
+    else if constexpr (__is_same(T, float)) v = op(v, dpp_f<kDppMirror>(v));
+    else v = op(v, dpp_i<kDppMirror>(v));
+  }
+  if constexpr (W >= 32) v = op(v, __shfl_xor(v, 16, 64));
+  if constexpr (W >= 64) v = op(v, __shfl_xor(v, 32, 64));
+  return v;
+}
+
 template <int W>
 __device__ __forceinline__ float cl_max(float v) {
-#pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, W));
-  return v;
+  return cl_reduce<W>(v, [](float a, float b) { return fmaxf(a, b); });
 }
 template <int W>
 __device__ __forceinline__ float cl_min(float v) {
-#pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, W));
-  return v;
+  return cl_reduce<W>(v, [](float a, float b) { return fminf(a, b); });
 }
 template <int W>
 __device__ __forceinline__ float cl_sum(float v) {
-#pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, W);
-  return v;
+  return cl_reduce<W>(v, [](float a, float b) { return a + b; });
 }
 template <int W>
 __device__ __forceinline__ int cl_sum_i(int v) {
-#pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, W);
-  return v;
+  return cl_reduce<W>(v, [](int a, int b) { return a + b; });
 }
 template <int W>
 __device__ __forceinline__ uint64_t cl_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) {
-    uint64_t w = __shfl_xor(v, o, W);
-    v = w > v ? w : v;
-  }
-  return v;
+  return cl_reduce<W>(v, [](uint64_t a, uint64_t b) { return a > b ? a : b; });
 }
-// Exclusive prefix sum over the cluster (lane c gets sum of lanes < c).
+
+// Value of lane (lane ^ D) for D in {1, 2, 4, 8} (inside a 16-lane row).  For
+// D = 4 and 8 both row shifts are executed by every lane, then selected.
+template <int D>
+__device__ __forceinline__ uint64_t xor_lane_u64(uint64_t v, int lane) {
+  if constexpr (D == 1) {
+    return dpp_u64<kDppXor1>(v);
+  } else if constexpr (D == 2) {
+    return dpp_u64<kDppXor2>(v);
+  } else {
+    const uint64_t up = dpp_u64<kDppRowShl + D>(v);    // lane + D
+    const uint64_t dn = dpp_u64<kDppRowShr + D>(v);    // lane - D
+    return (lane & D) ? dn : up;
+  }
+}
+
+// Bitonic sort, descending, of NS unsigned 64-bit values held S = NS / LPT per
+// lane by a cluster of LPT lanes (LPT <= 16): element n = lane * S + s.
+// Pairs closer than S are compared inside a lane, farther ones across lanes
+// with DPP moves.
+template <int LPT, int NS>
+__device__ __forceinline__ void bitonic_desc(uint64_t (&v)[NS / LPT], int lane_c) {
+  constexpr int S = NS / LPT;
+  static_assert(S >= 1 && S * LPT == NS, "slots");
+#pragma unroll
+  for (int size = 2; size <= NS; size <<= 1) {
+#pragma unroll
+    for (int d = size >> 1; d >= 1; d >>= 1) {
+      if (d < S) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          const int t = s ^ d;
+          if (t > s) {
+            const int n = lane_c * S + s;
+            const bool desc = size == NS || (n & size) == 0;
+            const uint64_t a = v[s], b = v[t];
+            const bool sw = desc ? (a < b) : (a > b);
+            v[s] = sw ? b : a;
+            v[t] = sw ? a : b;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          uint64_t o;
+          const int D = d / S;
+          if (D == 1) o = xor_lane_u64<1>(v[s], lane_c);
+          else if (D == 2) o = xor_lane_u64<2>(v[s], lane_c);
+          else if (D == 4) o = xor_lane_u64<4>(v[s], lane_c);
+          else o = xor_lane_u64<8>(v[s], lane_c);
+          const int n = lane_c * S + s;
+          const bool desc = size == NS || (n & size) == 0;
+          const bool lower = (n & d) == 0;
+          const bool keep_max = lower == desc;
+          v[s] = keep_max ? (o > v[s] ? o : v[s]) : (o < v[s] ? o : v[s]);
+        }
+      }
+    }
+  }
+}
+
+// Exclusive prefix sum over the cluster (lane c gets the sum of lanes < c).
 template <int W>
 __device__ __forceinline__ int cl_excl_scan(int v, int lane_c) {
   int incl = v;
+  if constexpr (W <= 16) {
+    // Every lane must execute each DPP move (a lane reading a source lane that
+    // is switched off gets 0), so the shifted value is formed unconditionally
+    // and only then masked by the cluster position.
+    if constexpr (W >= 2) { const int u = dpp_i<kDppRowShr + 1>(incl); incl += lane_c >= 1 ? u : 0; }
+    if constexpr (W >= 4) { const int u = dpp_i<kDppRowShr + 2>(incl); incl += lane_c >= 2 ? u : 0; }
+    if constexpr (W >= 8) { const int u = dpp_i<kDppRowShr + 4>(incl); incl += lane_c >= 4 ? u : 0; }
+    if constexpr (W >= 16) { const int u = dpp_i<kDppRowShr + 8>(incl); incl += lane_c >= 8 ? u : 0; }
+  } else {
 #pragma unroll
-  for (int o = 1; o < W; o <<= 1) {
-    int u = __shfl_up(incl, o, W);
-    if (lane_c >= o) incl += u;
+    for (int o = 1; o < W; o <<= 1) {
+      const int u = __shfl_up(incl, o, W);
+      if (lane_c >= o) incl += u;
+    }
   }
   return incl - v;
 }

@@ -28,7 +28,8 @@ struct RouteParams {
   int grouped, n_group, topk_group, topn, lg;
   int renorm;
   float scale;
-  int vec;                // 16-byte vector loads allowed
+  int vec;                // 16-byte vector loads of logits allowed
+  int bias_vec;           // 16-byte aligned float32 bias
   int loc_off, loc_n;
   int hmask_len;          // LDS u64 words for the block bitmask (even)
   int cap;                // candidate list capacity per token (>= k)
@@ -48,13 +49,60 @@ struct ScatterParams {
   int32_t* mn_limit;
 };
 
-size_t route_lds_bytes(int lpt, int epl, int hmask_len, int cap, int k);
+// Byte offsets of the route kernel's LDS regions (shared by host and device).
+// Per-cluster strides are padded so that the clusters of one wavefront fall
+// on different LDS banks.
+struct RouteLds {
+  int bias, hmask, row, cand, cand_r, sel_idx, sel_r, gscore, total;
+  int row_stride, cand_stride, sel_stride, gs_stride;   // in elements
+};
+__host__ __device__ inline RouteLds route_lds_layout(int lpt, int epl, int hmask_len, int cap, int k,
+                                                    int n_group) {
+  RouteLds L{};
+  const int block = lpt * 64 < 512 ? lpt * 64 : 512;
+  const int ncl = block / lpt;
+  L.row_stride = lpt * (epl + 4) + 4;          // floats, a multiple of 4
+  L.cand_stride = cap + 2;                     // even: 16-byte aligned rows
+  L.sel_stride = k + 1;
+  L.gs_stride = n_group > 0 ? n_group + 1 : 0;
+  int off = 0;
+  auto take = [&](int bytes) { const int o = off; off += (bytes + 15) & ~15; return o; };
+  L.bias = take(lpt * epl * 4);
+  L.hmask = take(hmask_len * 8);
+  L.row = take(ncl * L.row_stride * 4);
+  L.cand = take(ncl * L.cand_stride * 8);
+  L.cand_r = take(ncl * L.cand_stride * 4);
+  L.sel_idx = take(ncl * L.sel_stride * 4);
+  L.sel_r = take(ncl * L.sel_stride * 4);
+  L.gscore = take(ncl * L.gs_stride * 4);
+  L.total = off;
+  return L;
+}
+
+size_t route_lds_bytes(int lpt, int epl, int hmask_len, int cap, int k, int n_group);
 size_t scatter_lds_bytes(int El);
 hipError_t launch_route(const RouteParams& p, int lpt, int epl, bool bf16, int nb, hipStream_t s);
 hipError_t launch_scan(int32_t* hist, int nb, int El, int32_t* counts, hipStream_t s);
 hipError_t launch_scatter(const ScatterParams& p, int nb, hipStream_t s);
 hipError_t launch_empty_outputs(int32_t* counts, int El, int32_t* padded_offsets, int32_t* total,
                                 int32_t* nctas, hipStream_t s);
+
+struct FrontEndParams {
+  const void* hidden;
+  const void* gamma;
+  const void* W;
+  const void* rbias;      // nullable [E]
+  int f16;                // 1: float16 inputs, 0: bfloat16
+  int T, H, E, k;
+  float eps;
+  int act_sigmoid;
+  void* normed;
+  int32_t* ids;
+  void* aff;
+  float* partial;         // workspace [H / kchunk, T, E]
+};
+int front_end_kchunk(int H);
+hipError_t launch_front_end(const FrontEndParams& q, hipStream_t s);
 
 int aux_fwd_blocks(int64_t rows, int E);
 hipError_t launch_aux_fwd(const float* probs, const int32_t* counts, int64_t rows, int E,

@@ -36,65 +36,212 @@ namespace {
 
 constexpr float kInf = __builtin_huge_valf();
 
+// Raw row slice of one lane: EPL logits as packed 32-bit words (two bf16 or
+// one float32 per word), decoded later so that the loads can be issued before
+// anything else.  Padded experts hold -inf.
 template <int EPL, bool BF16>
-__device__ __forceinline__ void load_row(const void* __restrict__ base, size_t row_elems, int e0,
-                                         int E, bool vec, bool tv, float (&x)[EPL]) {
-  if (tv && vec && e0 + EPL <= E) {
-    if constexpr (BF16) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(
-          static_cast<const uint16_t*>(base) + row_elems + e0);
+struct RawRow {
+  static constexpr int kWords = BF16 ? EPL / 2 : EPL;
+  uint32_t w[kWords];
+};
+
+template <int EPL, bool BF16>
+__device__ __forceinline__ void load_raw(RawRow<EPL, BF16>& r, const void* __restrict__ base,
+                                         size_t row_elems, int e0, int E, bool vec, bool tv) {
+  constexpr int NW = RawRow<EPL, BF16>::kWords;
+  if (tv && vec && e0 + EPL <= E && NW % 4 == 0) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(
+        static_cast<const char*>(base) + (row_elems + e0) * (BF16 ? 2 : 4));
 #pragma unroll
-      for (int v = 0; v < EPL / 8; ++v) {
-        const u32x4 q = __builtin_nontemporal_load(src + v);
-        x[8 * v + 0] = bf16_lo(q.x); x[8 * v + 1] = bf16_hi(q.x);
-        x[8 * v + 2] = bf16_lo(q.y); x[8 * v + 3] = bf16_hi(q.y);
-        x[8 * v + 4] = bf16_lo(q.z); x[8 * v + 5] = bf16_hi(q.z);
-        x[8 * v + 6] = bf16_lo(q.w); x[8 * v + 7] = bf16_hi(q.w);
-      }
-    } else {
-      const f32x4* src = reinterpret_cast<const f32x4*>(
-          static_cast<const float*>(base) + row_elems + e0);
+    for (int v = 0; v < NW / 4; ++v) {
+      const u32x4 q = __builtin_nontemporal_load(src + v);
+      r.w[4 * v] = q.x; r.w[4 * v + 1] = q.y; r.w[4 * v + 2] = q.z; r.w[4 * v + 3] = q.w;
+    }
+  } else if constexpr (BF16) {
+    const uint16_t* src = static_cast<const uint16_t*>(base) + row_elems;
 #pragma unroll
-      for (int v = 0; v < EPL / 4; ++v) {
-        const f32x4 q = __builtin_nontemporal_load(src + v);
-        x[4 * v + 0] = q.x; x[4 * v + 1] = q.y; x[4 * v + 2] = q.z; x[4 * v + 3] = q.w;
-      }
+    for (int i = 0; i < EPL; i += 2) {
+      const int e = e0 + i;
+      const uint32_t lo = e < E ? (tv ? (uint32_t)src[e] : 0u) : 0xFF80u;
+      const uint32_t hi = e + 1 < E ? (tv ? (uint32_t)src[e + 1] : 0u) : 0xFF80u;
+      r.w[i / 2] = lo | (hi << 16);
     }
   } else {
+    const uint32_t* src = static_cast<const uint32_t*>(base) + row_elems;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int e = e0 + i;
-      float v = 0.0f;
-      if (tv && e < E) {
-        if constexpr (BF16)
-          v = bf16_bits_to_f32(static_cast<const uint16_t*>(base)[row_elems + e]);
-        else
-          v = static_cast<const float*>(base)[row_elems + e];
-      }
-      x[i] = v;
+      r.w[i] = e < E ? (tv ? src[e] : 0u) : 0xFF800000u;
     }
   }
 }
 
+template <int EPL, bool BF16>
+__device__ __forceinline__ void decode_raw(const RawRow<EPL, BF16>& r, float (&x)[EPL]) {
+  if constexpr (BF16) {
+#pragma unroll
+    for (int i = 0; i < EPL / 2; ++i) {
+      x[2 * i] = bf16_lo(r.w[i]);
+      x[2 * i + 1] = bf16_hi(r.w[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) x[i] = __uint_as_float(r.w[i]);
+  }
+}
+
+__device__ __forceinline__ float fast_rcp(float v) { return __builtin_amdgcn_rcpf(v); }
+
 }  // namespace
 
+// Per-token context the emitters need.
+struct EmitCtx {
+  int32_t* ids;
+  void* weights;
+  bool weights_bf16, renorm, hist;
+  int k, loc_off, loc_n;
+  float scale;
+  uint64_t* hmask;
+  const float* rowc;      // the cluster's score-basis row (padded per lane)
+  int t, tl, lane_c;
+  bool tv, plain, exact_pre;
+  float m, inv_s;
+};
+
+template <int EPL>
+__device__ __forceinline__ float row_at(const float* rowc, int e) {
+  return rowc[(e / EPL) * (EPL + 4) + (e % EPL)];
+}
+
+// Weights and outputs for the S slots a lane holds: slot q has rank n[q]
+// (n < k is selected), expert e[q] and score basis r[q].
+template <int LPT, int S>
+__device__ __forceinline__ void emit_slots(const EmitCtx& c, const int (&n)[S], const int (&e)[S],
+                                           const float (&r)[S]) {
+  const int k = c.k;
+  float ref = 0.0f;
+  if (!c.plain && !c.exact_pre) {
+    float mx = -kInf;
+#pragma unroll
+    for (int q = 0; q < S; ++q) mx = n[q] < k ? fmaxf(mx, r[q]) : mx;
+    ref = cl_max<LPT>(mx);
+  }
+  float part = 0.0f;
+#pragma unroll
+  for (int q = 0; q < S; ++q)
+    part += n[q] < k ? (c.plain ? r[q] : (c.exact_pre ? 0.0f : exp_f32(r[q] - ref))) : 0.0f;
+  const float inv_den = fast_rcp(cl_sum<LPT>(part));
+  if (!c.tv) return;
+#pragma unroll
+  for (int q = 0; q < S; ++q) {
+    if (n[q] < k) {
+      float w;
+      if (c.plain)
+        w = c.renorm ? r[q] * inv_den : r[q];
+      else if (c.exact_pre)
+        w = exp_f32(r[q] - c.m) * c.inv_s;
+      else
+        w = exp_f32(r[q] - ref) * inv_den;
+      w *= c.scale;
+      const size_t o = (size_t)c.t * k + n[q];
+      c.ids[o] = e[q];
+      if (c.weights_bf16)
+        static_cast<uint16_t*>(c.weights)[o] = (uint16_t)f32_to_bf16_rne(w);
+      else
+        static_cast<float*>(c.weights)[o] = w;
+      if (c.hist) {
+        const int el = e[q] - c.loc_off;
+        if (el >= 0 && el < c.loc_n) atomicOr(&c.hmask[el], 1ull << c.tl);
+      }
+    }
+  }
+}
+
+// Candidate ranks by counting over a statically sized candidate list (NC
+// slots read with 16-byte broadcasts): rank = number of candidates ordered
+// before, over the first C slots.  Selected candidates (rank < k) are recorded
+// in rank order with their score basis.
+template <int LPT, int NC, int EPL>
+__device__ __forceinline__ void rank_static(const uint64_t* mycand, const float* rowc, int C,
+                                            int k, int lane_c, int* myselidx, float* myselr) {
+  uint64_t cv[NC];
+#pragma unroll
+  for (int q = 0; q < NC; q += 2) {
+    const u64x2 v = *reinterpret_cast<const u64x2*>(mycand + q);
+    cv[q] = v.x;
+    cv[q + 1] = v.y;
+  }
+#pragma unroll
+  for (int s0 = 0; s0 < NC; s0 += LPT) {
+    const int j = s0 + lane_c;
+    if (j < C) {
+      const uint64_t mine = mycand[j];
+      int rank = 0;
+#pragma unroll
+      for (int i = 0; i < NC; ++i) rank += (i < C && cv[i] > mine) ? 1 : 0;
+      if (rank < k) {
+        const int e = unpack_idx(mine);
+        myselidx[rank] = e;
+        myselr[rank] = row_at<EPL>(rowc, e);
+      }
+    }
+  }
+}
+
+// Rank the candidates by counting (static tiers of 16 and 32 slots, a loop
+// beyond), then emit from the rank-ordered selection list.
+template <int LPT, int EPL>
+__device__ __forceinline__ void counted_emit(const EmitCtx& c, const uint64_t* mycand, int C,
+                                             int* myselidx, float* myselr) {
+  const int k = c.k;
+  constexpr int EP = LPT * EPL;
+  if (C <= 16) {
+    rank_static<LPT, 16, EPL>(mycand, c.rowc, C, k, c.lane_c, myselidx, myselr);
+  } else if (EP > 16 && C <= 32) {
+    rank_static<LPT, (EP > 16 ? 32 : 16), EPL>(mycand, c.rowc, C, k, c.lane_c, myselidx, myselr);
+  } else {
+    for (int j = c.lane_c; j < C; j += LPT) {
+      const uint64_t mine = mycand[j];
+      int rank = 0;
+#pragma unroll 4
+      for (int i = 0; i < C; ++i) rank += mycand[i] > mine ? 1 : 0;
+      if (rank < k) {
+        const int e = unpack_idx(mine);
+        myselidx[rank] = e;
+        myselr[rank] = row_at<EPL>(c.rowc, e);
+      }
+    }
+  }
+  wave_lds_sync();
+  constexpr int KMAX = LPT * EPL < 64 ? LPT * EPL : 64;     // k <= min(E, 64)
+  constexpr int Q = (KMAX + LPT - 1) / LPT;
+  int n[Q], e[Q];
+  float r[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    n[q] = c.lane_c + q * LPT;
+    const bool ok = n[q] < k;
+    e[q] = ok ? myselidx[n[q]] : 0;
+    r[q] = ok ? myselr[n[q]] : 0.0f;
+    if (!ok) n[q] = k;
+  }
+  emit_slots<LPT, Q>(c, n, e, r);
+}
+
 // One template instance per (lanes per token, experts per lane, logits dtype).
+//
+// Padded experts (e >= E) carry logit -inf and bias -inf, so their keys are
+// -inf and no per-element validity masks are needed anywhere.
 template <int LPT, int EPL, bool BF16>
 __global__ void __launch_bounds__(kRouteBlock<LPT>) route_kernel(RouteParams p) {
   constexpr int BLOCK = kRouteBlock<LPT>;
   constexpr int NCL = BLOCK / LPT;          // clusters (tokens in flight) per block
   constexpr int TPC = kTokensPerBlock / NCL;
   constexpr int EP = LPT * EPL;             // padded row length
+  constexpr int LSTR = EPL + 4;             // row floats per lane (+4 against bank conflicts)
   static_assert(TPC * NCL == kTokensPerBlock, "block shape");
   static_assert(EPL <= 32, "lane masks are 32-bit");
-
-  extern __shared__ __align__(16) unsigned char smem[];
-  float* bias_s = reinterpret_cast<float*>(smem);
-  uint64_t* hmask = reinterpret_cast<uint64_t*>(bias_s + EP);
-  float* rowbuf = reinterpret_cast<float*>(hmask + p.hmask_len);
-  uint64_t* cand = reinterpret_cast<uint64_t*>(rowbuf + NCL * EP);
-  int* sel_idx = reinterpret_cast<int*>(cand + NCL * p.cap);
-  float* sel_r = reinterpret_cast<float*>(sel_idx + NCL * p.k);
+  constexpr float kLowest = -3.402823466e38f;
 
   const int tid = threadIdx.x;
   const int lane_c = tid % LPT;
@@ -103,41 +250,68 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>) route_kernel(RouteParams p) 
   const int E = p.E, k = p.k;
   const int blk = blockIdx.x;
 
-  for (int e = tid; e < EP; e += BLOCK) {
-    float b = 0.0f;
-    if (p.bias != nullptr && e < E)
-      b = p.bias_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(p.bias)[e])
-                      : static_cast<const float*>(p.bias)[e];
-    bias_s[e] = b;
+  // The first token's logits and this lane's bias are requested first.
+  RawRow<EPL, BF16> raw;
+  {
+    const int t = blk * kTokensPerBlock + cl;
+    load_raw<EPL, BF16>(raw, p.logits, (size_t)t * E, e0, E, p.vec, t < p.T);
+  }
+  float breg[EPL];
+  if (p.bias != nullptr && !p.bias_bf16 && p.bias_vec && e0 + EPL <= E) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(p.bias) + e0);
+#pragma unroll
+    for (int v = 0; v < EPL / 4; ++v) {
+      const f32x4 q = src[v];
+      breg[4 * v] = q.x; breg[4 * v + 1] = q.y; breg[4 * v + 2] = q.z; breg[4 * v + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = e0 + i;
+      float b = e < E ? 0.0f : -kInf;
+      if (p.bias != nullptr && e < E)
+        b = p.bias_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(p.bias)[e])
+                        : static_cast<const float*>(p.bias)[e];
+      breg[i] = b;
+    }
+  }
+
+  const RouteLds L = route_lds_layout(LPT, EPL, p.hmask_len, p.cap, k, p.grouped ? p.n_group : 0);
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* bias_s = reinterpret_cast<float*>(smem + L.bias);
+  uint64_t* hmask = reinterpret_cast<uint64_t*>(smem + L.hmask);
+  float* myrow = reinterpret_cast<float*>(smem + L.row) + cl * L.row_stride + lane_c * LSTR;
+  uint64_t* mycand = reinterpret_cast<uint64_t*>(smem + L.cand) + cl * L.cand_stride;
+  float* mycandr = reinterpret_cast<float*>(smem + L.cand_r) + cl * L.cand_stride;
+  int* myselidx = reinterpret_cast<int*>(smem + L.sel_idx) + cl * L.sel_stride;
+  float* myselr = reinterpret_cast<float*>(smem + L.sel_r) + cl * L.sel_stride;
+  float* mygs = reinterpret_cast<float*>(smem + L.gscore) + cl * L.gs_stride;
+
+  if (cl == 0) {
+#pragma unroll
+    for (int i = 0; i < EPL; i += 4)
+      *reinterpret_cast<f32x4*>(bias_s + e0 + i) = f32x4{breg[i], breg[i + 1], breg[i + 2], breg[i + 3]};
   }
   if (p.hist != nullptr)
     for (int e = tid; e < p.loc_n; e += BLOCK) hmask[e] = 0;
   __syncthreads();
 
-  float breg[EPL];
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) breg[i] = bias_s[e0 + i];
-
-  const uint32_t vmask = e0 >= E ? 0u
-                         : (e0 + EPL <= E ? (EPL == 32 ? 0xffffffffu : ((1u << EPL) - 1u))
-                                          : ((1u << (E - e0)) - 1u));
-  const int nvalid = __builtin_popcount(vmask);
-  float* myrow = rowbuf + cl * EP;
-  uint64_t* mycand = cand + cl * p.cap;
-  int* myselidx = sel_idx + cl * k;
-  float* myselr = sel_r + cl * k;
-
   const bool sigmoid = p.kind == kKindSigmoid;
   const bool pre = p.kind == kKindSoftmaxPre;
   const bool has_bias = p.bias != nullptr;
   const bool need_ms = !sigmoid && ((pre && (has_bias || !p.renorm)) || p.scores != nullptr);
+  const uint32_t lane_bits = EPL == 32 ? 0xffffffffu : ((1u << EPL) - 1u);
 
   for (int it = 0; it < TPC; ++it) {
     const int tl = it * NCL + cl;               // token within the block
     const int t = blk * kTokensPerBlock + tl;
     const bool tv = t < p.T;
     float x[EPL];
-    load_row<EPL, BF16>(p.logits, (size_t)t * E, e0, E, p.vec, tv, x);
+    decode_raw<EPL, BF16>(raw, x);
+    if (it + 1 < TPC) {                         // prefetch the cluster's next token
+      const int tn = t + NCL;
+      load_raw<EPL, BF16>(raw, p.logits, (size_t)tn * E, e0, E, p.vec, tn < p.T);
+    }
 
     // ---- score basis r (kept in x) and selection key --------------------------
     float m = 0.0f, inv_s = 0.0f, ssum = 0.0f;
@@ -145,19 +319,19 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>) route_kernel(RouteParams p) 
       float part = 0.0f;
 #pragma unroll
       for (int i = 0; i < EPL; ++i) {
-        x[i] = sigmoid_f32(x[i]);
-        part += ((vmask >> i) & 1u) ? x[i] : 0.0f;
+        x[i] = sigmoid_f32(x[i]);               // sigmoid(-inf) = 0
+        part += x[i];
       }
       if (p.scores != nullptr) ssum = cl_sum<LPT>(part);
     } else if (need_ms) {
       float mx = -kInf;
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) mx = ((vmask >> i) & 1u) ? fmaxf(mx, x[i]) : mx;
+      for (int i = 0; i < EPL; ++i) mx = fmaxf(mx, x[i]);
       m = cl_max<LPT>(mx);
       float s = 0.0f;
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) s += ((vmask >> i) & 1u) ? exp_f32(x[i] - m) : 0.0f;
-      inv_s = 1.0f / cl_sum<LPT>(s);
+      for (int i = 0; i < EPL; ++i) s += exp_f32(x[i] - m);     // exp(-inf) = 0
+      inv_s = fast_rcp(cl_sum<LPT>(s));
       if (pre && has_bias) {
 #pragma unroll
         for (int i = 0; i < EPL; ++i) x[i] = exp_f32(x[i] - m) * inv_s;
@@ -167,13 +341,17 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>) route_kernel(RouteParams p) 
     float m1 = -kInf, m2 = -kInf;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-      key[i] = ((vmask >> i) & 1u) ? x[i] + breg[i] : -kInf;
+      key[i] = x[i] + breg[i];                  // -inf for padded experts
       m2 = __builtin_amdgcn_fmed3f(m1, m2, key[i]);
       m1 = fmaxf(m1, key[i]);
     }
+    // the score basis, dynamically indexable by this lane
+#pragma unroll
+    for (int i = 0; i < EPL; i += 4)
+      *reinterpret_cast<f32x4*>(myrow + i) = f32x4{x[i], x[i + 1], x[i + 2], x[i + 3]};
 
     // ---- group-limited selection (a group spans p.lg whole lanes) ----------
-    bool kept = nvalid > 0;
+    bool kept = m1 > -kInf;
     if (p.grouped) {
       float g1 = m1, g2 = m2;
       for (int o = 1; o < p.lg; o <<= 1) {
@@ -185,121 +363,119 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>) route_kernel(RouteParams p) 
       }
       const float gs = p.topn == 1 ? g1 : g1 + g2;
       const int myg = lane_c / p.lg;
+      if (lane_c % p.lg == 0 && myg < p.n_group) mygs[myg] = gs;
+      wave_lds_sync();
       int rank = 0;
-      for (int h = 0; h < p.n_group; ++h) {
-        const float gh = __shfl(gs, h * p.lg, LPT);
-        rank += (gh > gs || (gh == gs && h < myg)) ? 1 : 0;
+#pragma unroll
+      for (int h = 0; h < LPT; ++h) {           // n_group <= LPT
+        const float gh = h < p.n_group ? mygs[h] : -kInf;
+        rank += (h < p.n_group && (gh > gs || (gh == gs && h < myg))) ? 1 : 0;
       }
       kept = kept && myg < p.n_group && rank < p.topk_group;
     }
 
     // ---- tau: a lower bound on the k-th eligible key ---------------------------
-    const int cnt_l = kept ? (nvalid < 2 ? nvalid : 2) : 0;
+    const int cnt_l = kept ? (m1 > -kInf ? 1 : 0) + (m2 > -kInf ? 1 : 0) : 0;
     float tau = cl_min<LPT>(cnt_l == 2 ? m2 : (cnt_l == 1 ? m1 : kInf));
-    if (cl_sum_i<LPT>(cnt_l) < k) tau = -kInf;
-    uint32_t cmask = 0;
-    if (kept) {
+    if (cl_sum_i<LPT>(cnt_l) < k) tau = kLowest;          // every finite key qualifies
+    // candidate bit i: key[i] - tau >= 0, read from the sign bit (no lane masks)
+    uint32_t below = 0;
 #pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        cmask |= (((vmask >> i) & 1u) && key[i] >= tau) ? (1u << i) : 0u;
-    }
+    for (int i = 0; i < EPL; ++i) below |= (__float_as_uint(key[i] - tau) >> 31) << i;
+    const uint32_t cmask = kept ? (~below & lane_bits) : 0u;
     const int pc = __builtin_popcount(cmask);
     const int coff = cl_excl_scan<LPT>(pc, lane_c);
     int C = cl_sum_i<LPT>(pc);
 
-#pragma unroll
-    for (int i = 0; i < EPL; i += 4)
-      *reinterpret_cast<float4*>(myrow + e0 + i) = make_float4(x[i], x[i + 1], x[i + 2], x[i + 3]);
-    wave_lds_sync();
-
     if (C <= p.cap) {
+      // compact the candidates: four set bits per round, reads batched
       uint32_t mm = cmask;
       int pos = coff;
       while (mm) {
-        const int i = __builtin_ctz(mm);
-        mm &= mm - 1u;
-        const int e = e0 + i;
-        mycand[pos++] = pack_key(myrow[e] + bias_s[e], e);
+        int ii[4];
+        bool hv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          hv[q] = mm != 0u;
+          ii[q] = hv[q] ? __builtin_ctz(mm) : 0;
+          mm &= hv[q] ? mm - 1u : mm;
+        }
+        float rr[4], bb[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          rr[q] = myrow[ii[q]];
+          bb[q] = bias_s[e0 + ii[q]];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (hv[q]) {
+            mycand[pos] = pack_key(rr[q] + bb[q], e0 + ii[q]);
+            mycandr[pos] = rr[q];
+            ++pos;
+          }
+        }
       }
     } else {
       // many keys tie at tau: k rounds of a cluster-wide maximum instead
       uint32_t taken = 0;
       for (int rr = 0; rr < k; ++rr) {
         uint64_t best = 0;
+        float bestr = 0.0f;
         if (kept) {
 #pragma unroll
           for (int i = 0; i < EPL; ++i) {
             const uint64_t c = pack_key(key[i], e0 + i);
-            best = ((((vmask & ~taken) >> i) & 1u) && c > best) ? c : best;
+            const bool take = !((taken >> i) & 1u) && c > best;
+            best = take ? c : best;
+            bestr = take ? x[i] : bestr;
           }
         }
-        best = cl_max_u64<LPT>(best);
-        const int wi = unpack_idx(best) - e0;
-        if (wi >= 0 && wi < EPL) taken |= 1u << wi;
-        if (lane_c == 0) mycand[rr] = best;
+        const uint64_t win = cl_max_u64<LPT>(best);
+        const int wi = unpack_idx(win) - e0;
+        if (wi >= 0 && wi < EPL) {
+          taken |= 1u << wi;
+          mycand[rr] = win;
+          mycandr[rr] = bestr;
+        }
       }
       C = k;
     }
     wave_lds_sync();
 
-    // ---- rank by counting: rank = number of candidates ordered before ------------
-    for (int j = lane_c; j < C; j += LPT) {
-      const uint64_t mine = mycand[j];
-      int rank = 0;
-      for (int i = 0; i < C; ++i) rank += mycand[i] > mine ? 1 : 0;
-      if (rank < k) {
-        const int e = unpack_idx(mine);
-        myselidx[rank] = e;
-        myselr[rank] = myrow[e];
-      }
+    // ---- order the candidates, emit the top k ---------------------------------
+    {
+      EmitCtx ec;
+      ec.ids = p.ids;
+      ec.weights = p.weights;
+      ec.weights_bf16 = p.weights_bf16 != 0;
+      ec.renorm = p.renorm != 0;
+      ec.hist = p.hist != nullptr;
+      ec.k = k;
+      ec.loc_off = p.loc_off;
+      ec.loc_n = p.loc_n;
+      ec.scale = p.scale;
+      ec.hmask = hmask;
+      ec.rowc = myrow - lane_c * LSTR;
+      ec.t = t;
+      ec.tl = tl;
+      ec.lane_c = lane_c;
+      ec.tv = tv;
+      ec.plain = sigmoid || (pre && has_bias);       // weight = basis (s or p)
+      ec.exact_pre = pre && !has_bias && !p.renorm;
+      ec.m = m;
+      ec.inv_s = inv_s;
+      counted_emit<LPT, EPL>(ec, mycand, C, myselidx, myselr);
     }
-    wave_lds_sync();
-
-    // ---- weights -------------------------------------------------------------------
-    const bool plain = sigmoid || (pre && has_bias);   // weight = basis (s or p)
-    const bool exact_pre = pre && !has_bias && !p.renorm;
-    float ref = 0.0f;
-    if (!plain && !exact_pre) {
-      float mx = -kInf;
-      for (int j = lane_c; j < k; j += LPT) mx = fmaxf(mx, myselr[j]);
-      ref = cl_max<LPT>(mx);
-    }
-    float part = 0.0f;
-    for (int j = lane_c; j < k; j += LPT) {
-      const float r = myselr[j];
-      part += plain ? r : (exact_pre ? 0.0f : exp_f32(r - ref));
-    }
-    const float denom = cl_sum<LPT>(part);
     if (tv) {
-      for (int j = lane_c; j < k; j += LPT) {
-        const float r = myselr[j];
-        float w;
-        if (plain)
-          w = p.renorm ? r / denom : r;
-        else if (exact_pre)
-          w = exp_f32(r - m) * inv_s;
-        else
-          w = exp_f32(r - ref) / denom;
-        w *= p.scale;
-        const int e = myselidx[j];
-        p.ids[(size_t)t * k + j] = e;
-        if (p.weights_bf16)
-          static_cast<uint16_t*>(p.weights)[(size_t)t * k + j] = (uint16_t)f32_to_bf16_rne(w);
-        else
-          static_cast<float*>(p.weights)[(size_t)t * k + j] = w;
-        if (p.hist != nullptr) {
-          const int el = e - p.loc_off;
-          if (el >= 0 && el < p.loc_n) atomicOr(&hmask[el], 1ull << tl);
-        }
-      }
       // ---- full-E scores for the aux loss --------------------------------------------
       if (p.scores != nullptr) {
         float* srow = p.scores + (size_t)t * E;
+        const float inv_ss = sigmoid ? fast_rcp(ssum) : 0.0f;
 #pragma unroll
         for (int i = 0; i < EPL; ++i) {
-          if ((vmask >> i) & 1u) {
+          if (e0 + i < E) {
             float v;
-            if (sigmoid) v = x[i] / ssum;
+            if (sigmoid) v = x[i] * inv_ss;
             else if (pre && has_bias) v = x[i];
             else v = exp_f32(x[i] - m) * inv_s;
             srow[e0 + i] = v;
@@ -318,7 +494,11 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>) route_kernel(RouteParams p) 
 }
 
 // Column-wise exclusive scan of hist [nb][El] in place; totals -> counts[El].
-// Block: 64 columns x 16 row chunks.
+// Block: 64 columns x 16 waves; wave w owns a contiguous run of rows.  Every
+// row of a run is requested before the first is used (one memory latency),
+// and the values stay in registers for the write-back.
+constexpr int kScanRowsPerWave = 32;
+
 __global__ void __launch_bounds__(1024) scan_kernel(int32_t* __restrict__ hist, int nb, int El,
                                                     int32_t* __restrict__ counts) {
   __shared__ int part[16][64];
@@ -328,106 +508,130 @@ __global__ void __launch_bounds__(1024) scan_kernel(int32_t* __restrict__ hist, 
   const int per = (nb + 15) / 16;
   const int r0 = w * per;
   const int r1 = min(nb, r0 + per);
-  int s = 0;
-  if (col < El)
-    for (int r = r0; r < r1; ++r) s += hist[(size_t)r * El + col];
-  part[w][lane] = s;
-  __syncthreads();
-  int pre = 0, tot = 0;
-  for (int i = 0; i < 16; ++i) {
-    const int v = part[i][lane];
-    pre += i < w ? v : 0;
-    tot += v;
-  }
-  if (col < El) {
-    int run = pre;
-    for (int r = r0; r < r1; ++r) {
-      const size_t a = (size_t)r * El + col;
-      const int v = hist[a];
-      hist[a] = run;
-      run += v;
+  const bool cv = col < El;
+  int s = 0, pre = 0, tot = 0;
+  if (per <= kScanRowsPerWave) {
+    int v[kScanRowsPerWave];
+#pragma unroll
+    for (int i = 0; i < kScanRowsPerWave; ++i)
+      v[i] = (cv && r0 + i < r1) ? hist[(size_t)(r0 + i) * El + col] : 0;
+#pragma unroll
+    for (int i = 0; i < kScanRowsPerWave; ++i) s += v[i];
+    part[w][lane] = s;
+    __syncthreads();
+    for (int i = 0; i < 16; ++i) {
+      const int u = part[i][lane];
+      pre += i < w ? u : 0;
+      tot += u;
     }
-    if (w == 0) counts[col] = tot;
+    int run = pre;
+#pragma unroll
+    for (int i = 0; i < kScanRowsPerWave; ++i) {
+      if (cv && r0 + i < r1) hist[(size_t)(r0 + i) * El + col] = run;
+      run += v[i];
+    }
+  } else {
+    if (cv)
+      for (int r = r0; r < r1; ++r) s += hist[(size_t)r * El + col];
+    part[w][lane] = s;
+    __syncthreads();
+    for (int i = 0; i < 16; ++i) {
+      const int u = part[i][lane];
+      pre += i < w ? u : 0;
+      tot += u;
+    }
+    if (cv) {
+      int run = pre;
+      for (int r = r0; r < r1; ++r) {
+        const size_t a = (size_t)r * El + col;
+        const int u = hist[a];
+        hist[a] = run;
+        run += u;
+      }
+    }
   }
+  if (cv && w == 0) counts[col] = tot;
 }
 
-// Exclusive scan of LDS array a[0..n) in place (n <= 8 * 256) with 256 threads;
-// returns the total to every thread.  Uses tsum[256] scratch.
-__device__ int block_excl_scan_256(int* a, int n, int* tsum) {
-  const int tid = threadIdx.x;
-  const int per = (n + 255) / 256;
-  const int lo = min(n, tid * per), hi = min(n, lo + per);
-  int s = 0;
-  for (int i = lo; i < hi; ++i) s += a[i];
-  tsum[tid] = s;
-  __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {
-    const int v = tid >= o ? tsum[tid - o] : 0;
-    __syncthreads();
-    tsum[tid] += v;
-    __syncthreads();
-  }
-  int run = tsum[tid] - s;
-  const int total = tsum[255];
-  __syncthreads();
-  for (int i = lo; i < hi; ++i) {
-    const int v = a[i];
-    a[i] = run;
-    run += v;
-  }
-  __syncthreads();
-  return total;
-}
+// Scatter: one block per 64-token block of the route kernel.
+constexpr int kScatterThreads = 256;
+constexpr int kScatterPairsPerThread = kTokensPerBlock * 64 / kScatterThreads;   // k <= 64
 
-__global__ void __launch_bounds__(256) scatter_kernel(ScatterParams p) {
+__global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int El = p.El;
   uint64_t* msk = reinterpret_cast<uint64_t*>(smem);
   int* po = reinterpret_cast<int*>(msk + El);          // El + 1
   int* base = po + El + 1;                              // El
-  int* tsum = base + El;                                // 256
   const int tid = threadIdx.x;
   const int blk = blockIdx.x;
   const int tile = p.tile;
-
-  for (int e = tid; e < El; e += 256) {
-    const int c = p.counts[e];
-    po[e] = (c + tile - 1) / tile * tile;
-    msk[e] = 0;
-    base[e] = p.excl[(size_t)blk * El + e];
-  }
-  if (tid == 0) po[El] = 0;
-  __syncthreads();
-  const int total = block_excl_scan_256(po, El + 1, tsum);  // po[El] = total
-  const int ntiles = total / tile;
-
   const int k = p.k;
   const int npairs = kTokensPerBlock * k;
   const int t0 = blk * kTokensPerBlock;
-  for (int q = tid; q < npairs; q += 256) {
-    const int t = t0 + q / k;
-    if (t < p.T) {
-      const int el = p.ids[(size_t)t0 * k + q] - p.off;
-      if (el >= 0 && el < El) atomicOr(&msk[el], 1ull << (q / k));
+  const int valid_pairs = min(npairs, (p.T - t0) * k);
+
+  // all global reads first
+  int idv[kScatterPairsPerThread];
+#pragma unroll
+  for (int i = 0; i < kScatterPairsPerThread; ++i) {
+    const int q = tid + i * kScatterThreads;
+    idv[i] = q < valid_pairs ? p.ids[(size_t)t0 * k + q] - p.off : -1;
+  }
+  for (int e = tid; e < El; e += kScatterThreads) {
+    const int c = p.counts[e];
+    po[e] = (c + tile - 1) / tile * tile;
+    base[e] = p.excl[(size_t)blk * El + e];
+    msk[e] = 0;
+  }
+  if (tid == 0) po[El] = 0;
+  __syncthreads();
+
+  // wave 0: exclusive scan of the padded sizes; everyone: token bitmasks
+  if (tid < 64) {
+    const int n = El + 1;
+    const int per = (n + 63) / 64;
+    const int lo = min(n, tid * per), hi = min(n, lo + per);
+    int sum = 0;
+    for (int i = lo; i < hi; ++i) sum += po[i];
+    int incl = sum;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o, 64);
+      if (tid >= o) incl += u;
+    }
+    int run = incl - sum;
+    for (int i = lo; i < hi; ++i) {
+      const int v = po[i];
+      po[i] = run;
+      run += v;
     }
   }
+#pragma unroll
+  for (int i = 0; i < kScatterPairsPerThread; ++i) {
+    const int q = tid + i * kScatterThreads;
+    const int el = idv[i];
+    if (el >= 0 && el < El) atomicOr(&msk[el], 1ull << (q / k));
+  }
   __syncthreads();
-  for (int q = tid; q < npairs; q += 256) {
+  const int total = po[El];
+  const int ntiles = total / tile;
+
+#pragma unroll
+  for (int i = 0; i < kScatterPairsPerThread; ++i) {
+    const int q = tid + i * kScatterThreads;
+    if (q >= valid_pairs) continue;
     const int tl = q / k;
-    const int t = t0 + tl;
-    if (t >= p.T) continue;
-    const size_t xi = (size_t)t0 * k + q;
-    const int el = p.ids[xi] - p.off;
+    const int el = idv[i];
     int slot = -1;
     if (el >= 0 && el < El) {
       const uint64_t below = tl == 0 ? 0ull : (msk[el] & ((1ull << tl) - 1ull));
       slot = po[el] + base[el] + __popcll(below);
-      p.p2t[slot] = t;
+      p.p2t[slot] = t0 + tl;
     }
-    p.e2p[xi] = slot;
+    p.e2p[(size_t)t0 * k + q] = slot;
   }
 
-  for (int c = blk * 256 + tid; c < ntiles; c += gridDim.x * 256) {
+  for (int c = blk * kScatterThreads + tid; c < ntiles; c += gridDim.x * kScatterThreads) {
     const int pos = c * tile;
     int lo = 0, hi = El - 1;            // last e with po[e] <= pos
     while (lo < hi) {
@@ -435,13 +639,12 @@ __global__ void __launch_bounds__(256) scatter_kernel(ScatterParams p) {
       if (po[mid] <= pos) lo = mid; else hi = mid - 1;
     }
     const int seg_end = po[lo] + p.counts[lo];
-    const int lim = min(pos + tile, seg_end);
     p.batch_idx[c] = lo;
-    p.mn_limit[c] = lim;
-    for (int s = max(pos, seg_end); s < pos + tile; ++s) p.p2t[s] = -1;
+    p.mn_limit[c] = min(pos + tile, seg_end);
+    for (int s2 = max(pos, seg_end); s2 < pos + tile; ++s2) p.p2t[s2] = -1;
   }
   if (blk == 0) {
-    for (int e = tid; e <= El; e += 256) p.padded_offsets[e] = po[e];
+    for (int e = tid; e <= El; e += kScatterThreads) p.padded_offsets[e] = po[e];
     if (tid == 0) {
       *p.total_out = total;
       *p.nctas_out = ntiles;
@@ -467,7 +670,7 @@ __global__ void empty_outputs_kernel(int32_t* counts, int El, int32_t* padded_of
 template <int LPT, int EPL, bool BF16>
 static hipError_t launch_route_inst(const RouteParams& p, int nb, hipStream_t s) {
   constexpr int BLOCK = kRouteBlock<LPT>;
-  const size_t lds = route_lds_bytes(LPT, EPL, p.hmask_len, p.cap, p.k);
+  const size_t lds = route_lds_bytes(LPT, EPL, p.hmask_len, p.cap, p.k, p.grouped ? p.n_group : 0);
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&route_kernel<LPT, EPL, BF16>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -477,12 +680,8 @@ static hipError_t launch_route_inst(const RouteParams& p, int nb, hipStream_t s)
   return hipGetLastError();
 }
 
-size_t route_lds_bytes(int lpt, int epl, int hmask_len, int cap, int k) {
-  const int block = lpt * 64 < 512 ? lpt * 64 : 512;
-  const int ncl = block / lpt;
-  const int ep = lpt * epl;
-  return (size_t)ep * 4 + (size_t)hmask_len * 8 + (size_t)ncl * ep * 4 + (size_t)ncl * cap * 8 +
-         (size_t)ncl * k * 8;
+size_t route_lds_bytes(int lpt, int epl, int hmask_len, int cap, int k, int n_group) {
+  return route_lds_layout(lpt, epl, hmask_len, cap, k, n_group).total;
 }
 
 using LaunchFn = hipError_t (*)(const RouteParams&, int, hipStream_t);
@@ -516,10 +715,11 @@ hipError_t launch_scan(int32_t* hist, int nb, int El, int32_t* counts, hipStream
   return hipGetLastError();
 }
 
-size_t scatter_lds_bytes(int El) { return (size_t)El * 8 + (size_t)(El + 1) * 4 + (size_t)El * 4 + 256 * 4; }
+size_t scatter_lds_bytes(int El) { return (size_t)El * 8 + (size_t)(El + 1) * 4 + (size_t)El * 4; }
 
 hipError_t launch_scatter(const ScatterParams& p, int nb, hipStream_t s) {
-  hipLaunchKernelGGL(scatter_kernel, dim3(nb), dim3(256), scatter_lds_bytes(p.El), s, p);
+  hipLaunchKernelGGL(scatter_kernel, dim3(nb), dim3(kScatterThreads), scatter_lds_bytes(p.El), s,
+                     p);
   return hipGetLastError();
 }
 
