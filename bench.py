@@ -25,6 +25,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -49,6 +50,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="finish with plain device copies of this many MiB (the reference "
+                         "kernel that scales rocprofv3 FETCH_SIZE/WRITE_SIZE readings)")
     return ap.parse_args()
 
 
@@ -62,16 +66,22 @@ def kernel_sources_digest() -> str:
 
 
 def load_traffic(workload: str):
-    """HBM bytes per route-kernel launch from committed rocprofv3 --pmc runs,
-    or None when absent or taken on different kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"route_kernel_{workload}_traffic.json")
+    """HBM bytes per route-kernel launch from the committed rocprofv3 --pmc summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size), or None when
+    absent or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"route_kernel_{workload}_traffic.md")
     if not os.path.exists(path):
         return None
+    fields = {}
     with open(path) as f:
-        d = json.load(f)
-    if d.get("source_sha256") != kernel_sources_digest():
+        for line in f:
+            m = re.match(r"^- (source_sha256|traffic_bytes_per_launch): *`?([0-9a-f]+)`?\s*$", line)
+            if m:
+                fields[m.group(1)] = m.group(2)
+    if fields.get("source_sha256") != kernel_sources_digest():
         return None
-    return d.get("bytes_per_launch")
+    v = fields.get("traffic_bytes_per_launch")
+    return int(v) if v is not None else None
 
 
 def cpu_baseline(w, sample_T: int, seconds: float):
@@ -90,8 +100,6 @@ def cpu_baseline(w, sample_T: int, seconds: float):
         oracle.permute(r.ids, w.tile, num_experts=w.E)
         t_total += time.perf_counter() - t0
         reps += 1
-        if reps >= 50:
-            break
     return sample_T * reps / t_total, reps, t_total
 
 
@@ -256,6 +264,15 @@ def main():
     }
     if warm is not None:
         line["warm_single_set_ms_per_step"] = warm
+    if a.copy_calibration_mb:
+        n = a.copy_calibration_mb * 2 ** 20 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        line["copy_calibration"] = {"bytes_read": n * 4, "bytes_written": n * 4, "launches": 3,
+                                    "op": "torch copy_ of a float32 tensor"}
     s = json.dumps(line)
     print(s, flush=True)
     if a.json_out:

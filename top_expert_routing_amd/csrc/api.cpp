@@ -14,6 +14,13 @@
 #include "kernels.hpp"
 #include "moe_route.h"
 
+namespace moe {
+LaunchStamp& launch_stamp() {
+  static thread_local LaunchStamp st;
+  return st;
+}
+}  // namespace moe
+
 namespace {
 
 thread_local char g_msg[512] = "";
@@ -65,19 +72,32 @@ hipEvent_t take_event(Profiler& P) {
   return e;
 }
 
+// While profiling is on, a launch group `f` is timed with two events: for a
+// single kernel they are stamped by the dispatch itself (kernel start and
+// end); a group of several kernels is bracketed by event records instead.
 template <class F>
-hipError_t launch_with_profile(int kind, hipStream_t stream, F&& f) {
+hipError_t launch_with_profile(int kind, hipStream_t stream, F&& f, bool single_kernel = true) {
   Profiler& P = profiler();
   if (!P.on.load(std::memory_order_relaxed)) return f();
   std::lock_guard<std::mutex> lk(P.mu);
   hipEvent_t a = take_event(P), b = take_event(P);
   if (a == nullptr || b == nullptr) return f();
-  hipError_t e = hipEventRecord(a, stream);
-  if (e != hipSuccess) return e;
-  e = f();
-  if (e != hipSuccess) return e;
-  e = hipEventRecord(b, stream);
-  if (e != hipSuccess) return e;
+  hipError_t e;
+  if (single_kernel) {
+    moe::LaunchStamp& st = moe::launch_stamp();
+    st.start = a;
+    st.stop = b;
+    e = f();
+    st = moe::LaunchStamp{};
+    if (e != hipSuccess) return e;
+  } else {
+    e = hipEventRecord(a, stream);
+    if (e != hipSuccess) return e;
+    e = f();
+    if (e != hipSuccess) return e;
+    e = hipEventRecord(b, stream);
+    if (e != hipSuccess) return e;
+  }
   P.pending.push_back({kind, a, b});
   return hipSuccess;
 }
@@ -451,7 +471,7 @@ moe_status moe_aux_loss(const float* probs, const int32_t* tokens_per_expert, in
     hipError_t e = launch_with_profile(MOE_KERNEL_AUX_FWD, stream, [&] {
       return moe::launch_aux_fwd(probs, tokens_per_expert, rows, E, scale,
                                  static_cast<double*>(workspace), nb, loss, stream);
-    });
+    }, /*single_kernel=*/false);
     if (e != hipSuccess) return hip_fail(e, "aux forward launch");
   }
   if (grad_probs != nullptr && rows > 0) {
@@ -512,8 +532,9 @@ moe_status rmsnorm_gate_route(const void* hidden, const void* gamma, const void*
   q.ids = topk_ids;
   q.aff = affinities;
   q.partial = static_cast<float*>(workspace);
-  hipError_t e = launch_with_profile(MOE_KERNEL_FRONT_END, stream,
-                                     [&] { return moe::launch_front_end(q, stream); });
+  hipError_t e = launch_with_profile(
+      MOE_KERNEL_FRONT_END, stream, [&] { return moe::launch_front_end(q, stream); },
+      /*single_kernel=*/false);
   if (e != hipSuccess) return hip_fail(e, "front end launch");
   return MOE_OK;
 }

@@ -134,8 +134,8 @@ hipError_t launch_aux_bwd(const int32_t* counts, int64_t rows, int E, double sca
   int64_t nb = (n + (int64_t)kAuxBlock * 4 * 8 - 1) / ((int64_t)kAuxBlock * 4 * 8);
   if (nb > 4096) nb = 4096;
   if (nb < 1) nb = 1;
-  hipLaunchKernelGGL(aux_bwd_kernel, dim3((unsigned)nb), dim3(kAuxBlock), 0, s, counts, rows, E,
-                     scale, grad_loss, vec, grad);
+  MOE_LAUNCH(aux_bwd_kernel, dim3((unsigned)nb), dim3(kAuxBlock), 0, s, counts, rows, E, scale,
+             grad_loss, vec, grad);
   return hipGetLastError();
 }
 

@@ -1,11 +1,32 @@
 // Internal interface between the host library and the gfx950 kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace moe {
+
+// Dispatch timestamps for the next single-kernel launch of this host thread.
+// While a profiling caller sets them, the launchers go through
+// hipExtLaunchKernel, which stamps the two events at the kernel's own start and
+// end (the same clock a kernel trace reads); otherwise both are null.
+struct LaunchStamp {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchStamp& launch_stamp();
+
+// Launch `kernel` on `s`, stamped when a profiling caller asked for it.
+#define MOE_LAUNCH(kernel, grid, block, lds, s, ...)                                     \
+  do {                                                                                   \
+    const ::moe::LaunchStamp st_ = ::moe::launch_stamp();                                \
+    if (st_.start != nullptr)                                                            \
+      hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)(lds), s, st_.start, st_.stop, \
+                            0u, __VA_ARGS__);                                            \
+    else                                                                                 \
+      hipLaunchKernelGGL(kernel, grid, block, lds, s, __VA_ARGS__);                      \
+  } while (0)
 
 constexpr int kTokensPerBlock = 64;   // tokens per route/scatter block (one u64 bitmask)
 

@@ -676,7 +676,7 @@ static hipError_t launch_route_inst(const RouteParams& p, int nb, hipStream_t s)
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((route_kernel<LPT, EPL, BF16>), dim3(nb), dim3(BLOCK), lds, s, p);
+  MOE_LAUNCH((route_kernel<LPT, EPL, BF16>), dim3(nb), dim3(BLOCK), lds, s, p);
   return hipGetLastError();
 }
 
@@ -711,15 +711,14 @@ hipError_t launch_route(const RouteParams& p, int lpt, int epl, bool bf16, int n
 }
 
 hipError_t launch_scan(int32_t* hist, int nb, int El, int32_t* counts, hipStream_t s) {
-  hipLaunchKernelGGL(scan_kernel, dim3((El + 63) / 64), dim3(1024), 0, s, hist, nb, El, counts);
+  MOE_LAUNCH(scan_kernel, dim3((El + 63) / 64), dim3(1024), 0, s, hist, nb, El, counts);
   return hipGetLastError();
 }
 
 size_t scatter_lds_bytes(int El) { return (size_t)El * 8 + (size_t)(El + 1) * 4 + (size_t)El * 4; }
 
 hipError_t launch_scatter(const ScatterParams& p, int nb, hipStream_t s) {
-  hipLaunchKernelGGL(scatter_kernel, dim3(nb), dim3(kScatterThreads), scatter_lds_bytes(p.El), s,
-                     p);
+  MOE_LAUNCH(scatter_kernel, dim3(nb), dim3(kScatterThreads), scatter_lds_bytes(p.El), s, p);
   return hipGetLastError();
 }
 
