@@ -184,7 +184,7 @@ def main():
     mr.moe_profile_end()
     torch.cuda.synchronize()
     kt = {}
-    for name, kind in (("route_kernel", mr.MOE_KERNEL_ROUTE), ("scan_kernel", mr.MOE_KERNEL_SCAN),
+    for name, kind in (("route_kernel", mr.MOE_KERNEL_ROUTE),
                        ("scatter_kernel", mr.MOE_KERNEL_SCATTER)):
         ms, n = mr.moe_profile_read(kind)
         kt[name] = (ms / n * 1000.0) if n else None      # microseconds
@@ -242,7 +242,7 @@ def main():
             "workload": f"{w.name}: {w.description}",
             "T": T, "E": E, "k": k, "tile_tokens_dim": tile,
             "logits_dtype": w.logits_dtype,
-            "step": "moe_route_permute (route + scan + scatter kernels)",
+            "step": "moe_route_permute (route + scatter kernels)",
             "timing": f"HIP graph of {K} steps, {R} rotating buffer sets "
                       f"({R * set_bytes / 2**20:.0f} MiB, cold in L2 and MALL)",
         },

@@ -17,8 +17,14 @@
  *   caller.  The library never allocates, frees, synchronises, or copies device
  *   memory to the host.  Scratch memory comes from the caller's `workspace`
  *   (device memory, 256-byte aligned, at least the size the matching
- *   *_workspace_size() helper returns); its contents on entry are ignored and
- *   on return are unspecified.  All arrays are dense and row-major.
+ *   *_workspace_size() helper returns).  For moe_aux_loss and
+ *   rmsnorm_gate_route its contents on entry are ignored.  The ROUTING
+ *   workspace (moe_route with expert_counts, moe_route_permute) starts with a
+ *   counting region (the first moe_route_count_region_bytes() bytes) that must
+ *   be zero-filled before the workspace's first use; every call leaves it
+ *   zero-filled again when its work completes, so one workspace serves any
+ *   sequence of routing calls of any sizes on one stream.  After an MOE_EHIP
+ *   failure mid-call, zero it again.  All arrays are dense and row-major.
  * Streams: all work is enqueued on `stream` (0 = the null stream); outputs are
  *   valid once that work completes.  Calls on different streams that share a
  *   workspace race.  Calls are otherwise re-entrant and thread-safe.
@@ -239,9 +245,13 @@ moe_status rmsnorm_gate_route(const void* hidden, const void* gamma, const void*
                               int32_t* topk_ids, void* affinities, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
 
-/* Workspace sizes in bytes (0 = none needed).  Pure host functions. */
+/* Workspace sizes in bytes (0 = none needed).  Pure host functions.
+ * moe_route_workspace_size() covers both routing entry points; its first
+ * moe_route_count_region_bytes() bytes are the counting region described in
+ * the conventions above (a constant, independent of the sizes). */
 size_t moe_route_workspace_size(const moe_route_args* args, int32_t tile_tokens_dim,
                                 int32_t local_num_experts);
+size_t moe_route_count_region_bytes(void);
 size_t moe_aux_loss_workspace_size(int64_t rows, int32_t num_experts);
 size_t rmsnorm_gate_route_workspace_size(int32_t T, int32_t H, int32_t E);
 
@@ -252,15 +262,17 @@ int64_t moe_max_padded_tokens(int32_t T, int32_t k, int32_t local_num_experts, i
 int64_t moe_max_tiles(int32_t T, int32_t k, int32_t local_num_experts, int32_t tile);
 
 /* Profiling aid for benchmarks.  Between moe_profile_begin() and
- * moe_profile_end() every kernel the library launches is bracketed by two HIP
- * events recorded on the caller's stream (the stream the kernel runs on).
- * moe_profile_read() waits for the recorded events of one kernel kind and
+ * moe_profile_end() every kernel the library launches is timed by two HIP
+ * events on the caller's stream (the stream the kernel runs on): a kind that
+ * is one kernel is launched through hipExtLaunchKernel, which stamps the
+ * events with the kernel's own start and end; a kind of several kernels
+ * (AUX_FWD, FRONT_END) is bracketed by event records.  moe_profile_read() waits for the recorded events of one kernel kind and
  * returns their summed elapsed time and launch count since
  * moe_profile_begin().  Kernel kinds: MOE_KERNEL_*.  Not for use while
  * capturing a HIP graph. */
 typedef enum moe_kernel_kind {
   MOE_KERNEL_ROUTE = 0,
-  MOE_KERNEL_SCAN = 1,
+  MOE_KERNEL_COUNTS = 1,
   MOE_KERNEL_SCATTER = 2,
   MOE_KERNEL_AUX_FWD = 3,
   MOE_KERNEL_AUX_BWD = 4,

@@ -91,6 +91,9 @@ def test_route_null_pointers_and_workspace():
     assert _route(args, counts=FAKE, ws=FAKE, ws_bytes=4) == mr.MOE_EWORKSPACE
     assert _route(args, counts=FAKE, ws=None, ws_bytes=0) == mr.MOE_EWORKSPACE
     assert _permute(args, ws_bytes=4) == mr.MOE_EWORKSPACE
+    # the routing workspace must be 256-byte aligned (its counting region is reused)
+    assert _permute(args, ws=ctypes.c_void_p(0x1010)) == mr.MOE_EINVAL
+    assert _route(args, counts=FAKE, ws=ctypes.c_void_p(0x1010), ws_bytes=1 << 30) == mr.MOE_EINVAL
     assert _permute(args, counts=None) == mr.MOE_EINVAL
     assert _permute(args, p2t=None) == mr.MOE_EINVAL
     w = ctypes.c_void_p(0x1002)     # misaligned float32 weights
@@ -125,7 +128,10 @@ def test_size_helpers():
     assert mr.moe_max_padded_tokens(10, 2, 8, 3) == -1
     assert mr.moe_max_tiles(-1, 2, 8, 4) == -1
     args = mr.make_route_args(16384, 256, 8)
-    assert mr.moe_route_workspace_size(args, 8, 256) >= 256 * 256 * 4
+    region = mr.moe_route_count_region_bytes()
+    assert region == 64 * 2048 * 4 + 17 * 256     # fixed: independent of the sizes
+    assert mr.moe_route_workspace_size(args, 8, 256) == region + 256 * 256 * 4
+    assert mr.moe_route_workspace_size(mr.make_route_args(1, 8, 2), 8, 8) == region + 256
     assert mr.moe_route_workspace_size(args, 8, 256) % 256 == 0
     assert mr.moe_aux_loss_workspace_size(65536, 128) > 0
 

@@ -224,3 +224,41 @@ def test_deterministic():
     assert torch.equal(o1.permuted_idx_to_token_idx[:tot], o2.permuted_idx_to_token_idx[:tot])
     assert torch.equal(o1.cta_idx_xy_to_batch_idx[:nt], o2.cta_idx_xy_to_batch_idx[:nt])
     assert torch.equal(o1.cta_idx_xy_to_mn_limit[:nt], o2.cta_idx_xy_to_mn_limit[:nt])
+
+
+def test_workspace_reuse_across_sizes():
+    """One zero-filled workspace serves a sequence of routing calls of different
+    sizes: each call leaves its counting region zero again."""
+    calls = [
+        (WORKLOADS["deepseek_v3_like"], 4097, True),
+        (WORKLOADS["qwen_moe_like"], 65536, False),
+        (with_overrides(WORKLOADS["qwen_moe_like"], E=2048, k=16), 300, True),
+        (WORKLOADS["mixtral_like"], 63, False),
+        (WORKLOADS["deepseek_v3_like"], 16384, True),
+    ]
+    need = max(mr.moe_route_workspace_size(_args(w, T), w.tile, w.E) for w, T, _ in calls)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda:0")
+    region = mr.moe_route_count_region_bytes()
+    assert 0 < region <= need
+    for i, (w, T, permute) in enumerate(calls):
+        label = f"reuse {i}: {w.name} T={T} E={w.E} permute={permute}"
+        log(f"[gpu] {label}")
+        logits, bias = route_inputs(w, T=T, seed=9000 + i)
+        args = _args(w, T)
+        x = to_dev(logits, w.logits_dtype)
+        b = to_dev(bias, w.bias_dtype) if bias is not None else None
+        out = mr.alloc_route_outputs(args, "cuda:0", counts=True, permute=permute, tile=w.tile)
+        out.workspace = ws
+        if permute:
+            mr.route_permute(args, x, b, tile=w.tile, out=out)
+        else:
+            mr.route(args, x, b, counts=True, out=out)
+        torch.cuda.synchronize()
+        ids = out.topk_ids.cpu().numpy()
+        ref = _oracle(w, logits, bias)
+        compare_route(ref, ids, weights_to_f64(out.topk_weights), w.k, label=label)
+        assert np.array_equal(out.expert_counts.cpu().numpy(),
+                              np.bincount(ids.ravel(), minlength=w.E)), label
+        if permute:
+            compare_permutation(fetch_permutation(out), ids, w.tile, 0, w.E, label)
+        assert int(ws[:region].count_nonzero().item()) == 0, f"{label}: counting region not cleared"

@@ -20,13 +20,13 @@ from typing import Optional
 from . import _lib
 from ._lib import (MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP,
                    MOE_F32, MOE_BF16, MOE_F16, MOE_SOFTMAX, MOE_SIGMOID, MoeError,
-                   moe_route_args, LIB_PATH, MOE_KERNEL_ROUTE, MOE_KERNEL_SCAN,
+                   moe_route_args, LIB_PATH, MOE_KERNEL_ROUTE, MOE_KERNEL_COUNTS,
                    MOE_KERNEL_SCATTER, MOE_KERNEL_AUX_FWD, MOE_KERNEL_AUX_BWD,
                    MOE_KERNEL_FRONT_END)
 
 __all__ = [
     "moe_route", "moe_route_permute", "moe_aux_loss", "rmsnorm_gate_route",
-    "moe_route_workspace_size", "moe_aux_loss_workspace_size",
+    "moe_route_workspace_size", "moe_route_count_region_bytes", "moe_aux_loss_workspace_size",
     "moe_profile_begin", "moe_profile_end", "moe_profile_read",
     "rmsnorm_gate_route_workspace_size", "moe_max_padded_tokens", "moe_max_tiles",
     "make_route_args", "route", "route_permute", "MoeError", "moe_route_args", "LIB_PATH",
@@ -126,6 +126,10 @@ def moe_route_workspace_size(args: moe_route_args, tile_tokens_dim: int,
                                                  local_num_experts))
 
 
+def moe_route_count_region_bytes() -> int:
+    return int(_lib.lib.moe_route_count_region_bytes())
+
+
 def moe_aux_loss_workspace_size(rows: int, num_experts: int) -> int:
     return int(_lib.lib.moe_aux_loss_workspace_size(ctypes.c_int64(rows), num_experts))
 
@@ -191,7 +195,8 @@ def alloc_route_outputs(args: moe_route_args, device, scores: bool = False,
     if counts or permute:
         out.expert_counts = torch.empty(n_loc, dtype=torch.int32, device=device)
         ws = moe_route_workspace_size(args, tile, n_loc)
-        out.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
+        # the counting region must start zero-filled; the library keeps it so
+        out.workspace = torch.zeros(max(ws, 1), dtype=torch.uint8, device=device)
     if permute:
         mp = moe_max_padded_tokens(T, k, n_loc, tile)
         mt = moe_max_tiles(T, k, n_loc, tile)

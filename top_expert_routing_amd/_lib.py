@@ -21,13 +21,13 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EUNSUPPORTED", 3: "MOE_EWO
 # Every symbol the header declares.
 EXPORTED = [
     "moe_route", "moe_route_permute", "moe_aux_loss", "rmsnorm_gate_route",
-    "moe_route_workspace_size", "moe_aux_loss_workspace_size",
+    "moe_route_workspace_size", "moe_route_count_region_bytes", "moe_aux_loss_workspace_size",
     "rmsnorm_gate_route_workspace_size", "moe_max_padded_tokens", "moe_max_tiles",
     "moe_status_string", "moe_last_error_message", "moe_last_hip_error",
     "moe_profile_begin", "moe_profile_end", "moe_profile_read",
 ]
 
-MOE_KERNEL_ROUTE, MOE_KERNEL_SCAN, MOE_KERNEL_SCATTER = 0, 1, 2
+MOE_KERNEL_ROUTE, MOE_KERNEL_COUNTS, MOE_KERNEL_SCATTER = 0, 1, 2
 MOE_KERNEL_AUX_FWD, MOE_KERNEL_AUX_BWD, MOE_KERNEL_FRONT_END = 3, 4, 5
 
 
@@ -93,6 +93,8 @@ def _load():
     lib.rmsnorm_gate_route.restype = i32
     lib.moe_route_workspace_size.argtypes = [args_p, i32, i32]
     lib.moe_route_workspace_size.restype = sz
+    lib.moe_route_count_region_bytes.argtypes = []
+    lib.moe_route_count_region_bytes.restype = sz
     lib.moe_aux_loss_workspace_size.argtypes = [i64, i32]
     lib.moe_aux_loss_workspace_size.restype = sz
     lib.rmsnorm_gate_route_workspace_size.argtypes = [i32, i32, i32]

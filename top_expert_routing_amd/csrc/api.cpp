@@ -192,22 +192,55 @@ moe_status validate_route(const moe_route_args* a, Shape* shape) {
 
 int num_blocks(int T) { return (T + moe::kTokensPerBlock - 1) / moe::kTokensPerBlock; }
 
-size_t route_ws_bytes(const moe_route_args& a, int loc_n) {
-  return align256((size_t)num_blocks(a.num_tokens) * loc_n * sizeof(int32_t));
+// Routing workspace: [counting rows | done counter][per-block counts].  The
+// first region has a fixed size (kMaxSuperRows rows of up to kMaxExperts), so
+// that it lies at the same place whatever the call's sizes; it is zero between
+// calls.
+constexpr size_t kCountRowsBytes = (size_t)moe::kMaxSuperRows * kMaxExperts * sizeof(int32_t);
+constexpr size_t kCountRegionBytes = kCountRowsBytes + 17 * 256;   // + the block counters
+
+struct CountPlan {
+  int nb = 0, group_blocks = 1, num_super = 1;
+};
+CountPlan count_plan(int T) {
+  CountPlan c;
+  c.nb = num_blocks(T);
+  int g = 1;
+  while ((int64_t)g * g < c.nb) ++g;                 // ~sqrt(nb) blocks per row
+  const int gmin = (c.nb + moe::kMaxSuperRows - 1) / moe::kMaxSuperRows;
+  c.group_blocks = g > gmin ? g : gmin;
+  if (c.group_blocks < 1) c.group_blocks = 1;
+  c.num_super = (c.nb + c.group_blocks - 1) / c.group_blocks;
+  return c;
+}
+
+size_t route_ws_bytes(const moe_route_args& a, int loc_n, bool permute) {
+  return kCountRegionBytes +
+         (permute ? align256((size_t)num_blocks(a.num_tokens) * loc_n * sizeof(int32_t)) : 0);
+}
+int32_t* ws_count_rows(void* ws) { return static_cast<int32_t*>(ws); }
+uint32_t* ws_done(void* ws) {
+  return reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kCountRowsBytes);
+}
+int32_t* ws_hist(void* ws) {
+  return reinterpret_cast<int32_t*>(static_cast<char*>(ws) + kCountRegionBytes);
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 moe::RouteParams make_params(const moe_route_args& a, const Shape& sh, const void* logits,
                              const void* bias, int32_t* ids, void* weights, float* scores,
-                             int32_t* hist, int loc_off, int loc_n) {
+                             int32_t* super_rows, int32_t* hist, int group_blocks, int loc_off,
+                             int loc_n) {
   moe::RouteParams p{};
   p.logits = logits;
   p.bias = bias;
   p.ids = ids;
   p.weights = weights;
   p.scores = scores;
+  p.super_rows = super_rows;
   p.hist = hist;
+  p.group_blocks = group_blocks;
   p.T = a.num_tokens;
   p.E = a.num_experts;
   p.k = a.top_k;
@@ -229,7 +262,7 @@ moe::RouteParams make_params(const moe_route_args& a, const Shape& sh, const voi
   p.bias_vec = bias != nullptr && aligned(bias, 16);
   p.loc_off = loc_off;
   p.loc_n = loc_n;
-  p.hmask_len = hist != nullptr ? (loc_n + 1) & ~1 : 0;
+  p.hmask_len = super_rows != nullptr ? (loc_n + 1) & ~1 : 0;
   p.cap = a.top_k <= 32 ? 32 : 64;
   return p;
 }
@@ -324,10 +357,12 @@ int64_t moe_max_tiles(int32_t T, int32_t k, int32_t loc_n, int32_t tile) {
   return m < 0 ? -1 : m / tile;
 }
 
+size_t moe_route_count_region_bytes(void) { return kCountRegionBytes; }
+
 size_t moe_route_workspace_size(const moe_route_args* a, int32_t tile, int32_t loc_n) {
   (void)tile;
   if (a == nullptr || a->num_tokens < 0 || loc_n < 1) return 0;
-  return route_ws_bytes(*a, loc_n);
+  return route_ws_bytes(*a, loc_n, true);
 }
 
 moe_status moe_route(const moe_route_args* args, const void* logits, const void* bias,
@@ -349,22 +384,24 @@ moe_status moe_route(const moe_route_args* args, const void* logits, const void*
     return fail(MOE_EINVAL, "logits, topk_ids and topk_weights are required");
   if (a.weights_dtype == MOE_F32 && !aligned(topk_weights, 4))
     return fail(MOE_EINVAL, "topk_weights must be 4-byte aligned");
-  int32_t* hist = nullptr;
+  int32_t* rows = nullptr;
+  const CountPlan cp = count_plan(T);
   if (expert_counts != nullptr) {
-    const size_t need = route_ws_bytes(a, E);
+    const size_t need = route_ws_bytes(a, E, false);
     if (workspace == nullptr || workspace_bytes < need)
       return fail(MOE_EWORKSPACE, "workspace needs %zu bytes", need);
-    hist = static_cast<int32_t*>(workspace);
+    if (!aligned(workspace, 256)) return fail(MOE_EINVAL, "workspace must be 256-byte aligned");
+    rows = ws_count_rows(workspace);
   }
-  const moe::RouteParams p =
-      make_params(a, sh, logits, bias, topk_ids, topk_weights, scores, hist, 0, E);
+  const moe::RouteParams p = make_params(a, sh, logits, bias, topk_ids, topk_weights, scores,
+                                         rows, nullptr, cp.group_blocks, 0, E);
   st = launch_route_checked(p, sh, a.logits_dtype == MOE_BF16, stream);
   if (st != MOE_OK) return st;
-  if (hist != nullptr) {
-    hipError_t e = launch_with_profile(MOE_KERNEL_SCAN, stream, [&] {
-      return moe::launch_scan(hist, num_blocks(T), E, expert_counts, stream);
+  if (rows != nullptr) {
+    hipError_t e = launch_with_profile(MOE_KERNEL_COUNTS, stream, [&] {
+      return moe::launch_counts(rows, cp.num_super, E, expert_counts, stream);
     });
-    if (e != hipSuccess) return hip_fail(e, "scan_kernel launch");
+    if (e != hipSuccess) return hip_fail(e, "counts_kernel launch");
   }
   return MOE_OK;
 }
@@ -402,20 +439,18 @@ moe_status moe_route_permute(const moe_route_args* args, int32_t tile, int32_t l
     return fail(MOE_EINVAL, "a required pointer is NULL");
   if (a.weights_dtype == MOE_F32 && !aligned(topk_weights, 4))
     return fail(MOE_EINVAL, "topk_weights must be 4-byte aligned");
-  const size_t need = route_ws_bytes(a, loc_n);
+  const size_t need = route_ws_bytes(a, loc_n, true);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(MOE_EWORKSPACE, "workspace needs %zu bytes", need);
-  int32_t* hist = static_cast<int32_t*>(workspace);
-  const int nb = num_blocks(T);
+  if (!aligned(workspace, 256)) return fail(MOE_EINVAL, "workspace must be 256-byte aligned");
+  const CountPlan cp = count_plan(T);
+  int32_t* rows = ws_count_rows(workspace);
+  int32_t* hist = ws_hist(workspace);
 
-  const moe::RouteParams p =
-      make_params(a, sh, logits, bias, topk_ids, topk_weights, scores, hist, loc_off, loc_n);
+  const moe::RouteParams p = make_params(a, sh, logits, bias, topk_ids, topk_weights, scores,
+                                         rows, hist, cp.group_blocks, loc_off, loc_n);
   st = launch_route_checked(p, sh, a.logits_dtype == MOE_BF16, stream);
   if (st != MOE_OK) return st;
-  hipError_t e = launch_with_profile(MOE_KERNEL_SCAN, stream, [&] {
-    return moe::launch_scan(hist, nb, loc_n, expert_counts, stream);
-  });
-  if (e != hipSuccess) return hip_fail(e, "scan_kernel launch");
 
   moe::ScatterParams q{};
   q.ids = topk_ids;
@@ -424,8 +459,12 @@ moe_status moe_route_permute(const moe_route_args* args, int32_t tile, int32_t l
   q.El = loc_n;
   q.off = loc_off;
   q.tile = tile;
+  q.super_rows = rows;
+  q.hist = hist;
+  q.done = ws_done(workspace);
+  q.group_blocks = cp.group_blocks;
+  q.num_super = cp.num_super;
   q.counts = expert_counts;
-  q.excl = hist;
   q.e2p = e2p;
   q.p2t = p2t;
   q.padded_offsets = padded_offsets;
@@ -433,7 +472,8 @@ moe_status moe_route_permute(const moe_route_args* args, int32_t tile, int32_t l
   q.nctas_out = num_non_exiting_ctas;
   q.batch_idx = batch_idx;
   q.mn_limit = mn_limit;
-  e = launch_with_profile(MOE_KERNEL_SCATTER, stream, [&] { return moe::launch_scatter(q, nb, stream); });
+  hipError_t e = launch_with_profile(MOE_KERNEL_SCATTER, stream,
+                                     [&] { return moe::launch_scatter(q, cp.nb, stream); });
   if (e != hipSuccess) return hip_fail(e, "scatter_kernel launch");
   return MOE_OK;
 }

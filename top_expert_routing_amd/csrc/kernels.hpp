@@ -30,6 +30,12 @@ LaunchStamp& launch_stamp();
 
 constexpr int kTokensPerBlock = 64;   // tokens per route/scatter block (one u64 bitmask)
 
+// Per-expert counting: each route block adds its counts into one of at most
+// kMaxSuperRows rows (blocks [s*G, (s+1)*G) into row s).  Those rows live at
+// the start of the routing workspace, must be zero on entry and are zero again
+// when a call completes: the consumer of the rows clears them.
+constexpr int kMaxSuperRows = 64;
+
 template <int LPT>
 constexpr int kRouteBlock = (LPT * 64 < 512) ? LPT * 64 : 512;
 
@@ -41,7 +47,9 @@ struct RouteParams {
   int32_t* ids;           // [T, k]
   void* weights;          // [T, k] f32 or bf16
   float* scores;          // nullable [T, E]
-  int32_t* hist;          // nullable [nb, loc_n]
+  int32_t* super_rows;    // nullable: per-expert counting rows (counting on when set)
+  int32_t* hist;          // nullable [nb, loc_n]: per-block counts, for the permutation
+  int group_blocks;       // blocks that add into one counting row
   int T, E, k;
   int kind;
   int bias_bf16;
@@ -59,8 +67,12 @@ struct RouteParams {
 struct ScatterParams {
   const int32_t* ids;
   int T, k, El, off, tile;
-  const int32_t* counts;  // [El]
-  const int32_t* excl;    // [nb, El] exclusive per-block base ranks
+  int32_t* super_rows;    // [num_super, El], cleared by the last block
+  const int32_t* hist;    // [nb, El] per-block counts
+  uint32_t* done;         // block counters ([0] top, [64 * (j + 1)] sub-counter j), reset by
+                          // their last user: 17 * 256 bytes
+  int group_blocks, num_super;
+  int32_t* counts;        // out [El]
   int32_t* e2p;
   int32_t* p2t;
   int32_t* padded_offsets;
@@ -103,7 +115,8 @@ __host__ __device__ inline RouteLds route_lds_layout(int lpt, int epl, int hmask
 size_t route_lds_bytes(int lpt, int epl, int hmask_len, int cap, int k, int n_group);
 size_t scatter_lds_bytes(int El);
 hipError_t launch_route(const RouteParams& p, int lpt, int epl, bool bf16, int nb, hipStream_t s);
-hipError_t launch_scan(int32_t* hist, int nb, int El, int32_t* counts, hipStream_t s);
+hipError_t launch_counts(int32_t* super_rows, int num_super, int El, int32_t* counts,
+                         hipStream_t s);
 hipError_t launch_scatter(const ScatterParams& p, int nb, hipStream_t s);
 hipError_t launch_empty_outputs(int32_t* counts, int El, int32_t* padded_offsets, int32_t* total,
                                 int32_t* nctas, hipStream_t s);

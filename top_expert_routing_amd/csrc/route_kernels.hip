@@ -10,7 +10,7 @@
 //   float32 sigmoid, selection by score + correction bias, unbiased weights:
 //     MAX SigmoidTopKRouter, routing steps 2-4.
 //
-// Three launches per moe_route_permute call, all on the caller's stream:
+// Two launches per moe_route_permute call, both on the caller's stream:
 //   route_kernel    one cluster of LPT lanes per token, EPL experts per lane.
 //                   Logits stream HBM -> VGPRs once (16-byte loads); keys,
 //                   group scores and a lower bound tau on the k-th key are
@@ -18,15 +18,18 @@
 //                   into LDS and ranked by counting.  Per block of 64 tokens
 //                   an LDS bitmask per expert records which tokens chose it;
 //                   its popcounts are the block's histogram row.
-//   scan_kernel     column-wise exclusive scan of the [blocks, experts]
-//                   histogram -> per-(block, expert) base rank and per-expert
-//                   totals (the expert_counts output).
-//   scatter_kernel  per block: padded offsets from the totals, the stable
-//                   in-block rank (popcount of lower bits of the bitmask),
-//                   slot = offset + base + rank; writes both index maps, the
-//                   padding, and the per-tile expert / row limit.
-// No atomics on global memory; every output is a pure function of the input,
-// so two runs are bit-identical.
+//                   At its end each block writes its counts row and adds it
+//                   into a counting row shared by a group of G blocks.
+//   scatter_kernel  per block: expert totals and the block's base ranks from
+//                   the counting rows plus the rows of earlier blocks of its
+//                   group, padded offsets, the stable in-block rank (popcount
+//                   of lower bits of the bitmask), slot = offset + base + rank;
+//                   writes both index maps, the padding, and the per-tile
+//                   expert / row limit.  The last block to finish reading the
+//                   counting rows clears them for the next call.
+// (moe_route with counts launches counts_kernel instead of scatter_kernel.)
+// Integer additions commute, so the atomics leave no trace of their order:
+// every output is a pure function of the input and two runs are bit-identical.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -292,7 +295,8 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>) route_kernel(RouteParams p) 
     for (int i = 0; i < EPL; i += 4)
       *reinterpret_cast<f32x4*>(bias_s + e0 + i) = f32x4{breg[i], breg[i + 1], breg[i + 2], breg[i + 3]};
   }
-  if (p.hist != nullptr)
+  const bool counting = p.super_rows != nullptr;
+  if (counting)
     for (int e = tid; e < p.loc_n; e += BLOCK) hmask[e] = 0;
   __syncthreads();
 
@@ -449,7 +453,7 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>) route_kernel(RouteParams p) 
       ec.weights = p.weights;
       ec.weights_bf16 = p.weights_bf16 != 0;
       ec.renorm = p.renorm != 0;
-      ec.hist = p.hist != nullptr;
+      ec.hist = counting;
       ec.k = k;
       ec.loc_off = p.loc_off;
       ec.loc_n = p.loc_n;
@@ -486,85 +490,55 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>) route_kernel(RouteParams p) 
     wave_lds_sync();
   }
 
-  if (p.hist != nullptr) {
+  if (counting) {
     __syncthreads();
-    for (int e = tid; e < p.loc_n; e += BLOCK)
-      p.hist[(size_t)blk * p.loc_n + e] = __popcll(hmask[e]);
+    int32_t* srow = p.super_rows + (size_t)(blk / p.group_blocks) * p.loc_n;
+    for (int e = tid; e < p.loc_n; e += BLOCK) {
+      const int c = __popcll(hmask[e]);
+      if (p.hist != nullptr) p.hist[(size_t)blk * p.loc_n + e] = c;
+      if (c != 0) atomicAdd(srow + e, c);
+    }
   }
 }
 
-// Column-wise exclusive scan of hist [nb][El] in place; totals -> counts[El].
-// Block: 64 columns x 16 waves; wave w owns a contiguous run of rows.  Every
-// row of a run is requested before the first is used (one memory latency),
-// and the values stay in registers for the write-back.
-constexpr int kScanRowsPerWave = 32;
-
-__global__ void __launch_bounds__(1024) scan_kernel(int32_t* __restrict__ hist, int nb, int El,
-                                                    int32_t* __restrict__ counts) {
-  __shared__ int part[16][64];
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int col = blockIdx.x * 64 + lane;
-  const int per = (nb + 15) / 16;
-  const int r0 = w * per;
-  const int r1 = min(nb, r0 + per);
-  const bool cv = col < El;
-  int s = 0, pre = 0, tot = 0;
-  if (per <= kScanRowsPerWave) {
-    int v[kScanRowsPerWave];
-#pragma unroll
-    for (int i = 0; i < kScanRowsPerWave; ++i)
-      v[i] = (cv && r0 + i < r1) ? hist[(size_t)(r0 + i) * El + col] : 0;
-#pragma unroll
-    for (int i = 0; i < kScanRowsPerWave; ++i) s += v[i];
-    part[w][lane] = s;
-    __syncthreads();
-    for (int i = 0; i < 16; ++i) {
-      const int u = part[i][lane];
-      pre += i < w ? u : 0;
-      tot += u;
-    }
-    int run = pre;
-#pragma unroll
-    for (int i = 0; i < kScanRowsPerWave; ++i) {
-      if (cv && r0 + i < r1) hist[(size_t)(r0 + i) * El + col] = run;
-      run += v[i];
-    }
-  } else {
-    if (cv)
-      for (int r = r0; r < r1; ++r) s += hist[(size_t)r * El + col];
-    part[w][lane] = s;
-    __syncthreads();
-    for (int i = 0; i < 16; ++i) {
-      const int u = part[i][lane];
-      pre += i < w ? u : 0;
-      tot += u;
-    }
-    if (cv) {
-      int run = pre;
-      for (int r = r0; r < r1; ++r) {
-        const size_t a = (size_t)r * El + col;
-        const int u = hist[a];
-        hist[a] = run;
-        run += u;
-      }
-    }
+// Per-expert totals of moe_route: sums the counting rows and clears them.
+__global__ void counts_kernel(int32_t* __restrict__ super_rows, int num_super, int El,
+                              int32_t* __restrict__ counts) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= El) return;
+  int tot = 0;
+  for (int r = 0; r < num_super; ++r) {
+    int32_t* a = super_rows + (size_t)r * El + e;
+    tot += *a;
+    *a = 0;
   }
-  if (cv && w == 0) counts[col] = tot;
+  counts[e] = tot;
 }
 
 // Scatter: one block per 64-token block of the route kernel.
+//   1. expert totals and this block's base ranks from the counting rows (rows
+//      of earlier groups) and the per-block counts of earlier blocks of its
+//      own group; the block that finishes those reads last clears the rows;
+//   2. padded offsets (a scan over the experts), the block's token bitmask per
+//      expert, slot = offset + base + popcount of the lower token bits;
+//   3. the tiles of the experts [b*El/nb, (b+1)*El/nb): expert, row limit and
+//      the -1 padding of each segment's last tile.
 constexpr int kScatterThreads = 256;
+constexpr int kDoneLanes = 16;          // sub-counters of the block count
+constexpr int kDoneStride = 64;         // 256 bytes apart: separate cache lines
 constexpr int kScatterPairsPerThread = kTokensPerBlock * 64 / kScatterThreads;   // k <= 64
 
 __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int last_block;
   const int El = p.El;
   uint64_t* msk = reinterpret_cast<uint64_t*>(smem);
-  int* po = reinterpret_cast<int*>(msk + El);          // El + 1
-  int* base = po + El + 1;                              // El
+  int* po = reinterpret_cast<int*>(msk + El);           // El + 1
+  int* base = po + El + 1;                               // El
+  int* cnt = base + El;                                  // El
   const int tid = threadIdx.x;
   const int blk = blockIdx.x;
+  const int nb = gridDim.x;
   const int tile = p.tile;
   const int k = p.k;
   const int npairs = kTokensPerBlock * k;
@@ -578,14 +552,41 @@ __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams 
     const int q = tid + i * kScatterThreads;
     idv[i] = q < valid_pairs ? p.ids[(size_t)t0 * k + q] - p.off : -1;
   }
+  const int grp = blk / p.group_blocks;
+  const int g0 = grp * p.group_blocks;
   for (int e = tid; e < El; e += kScatterThreads) {
-    const int c = p.counts[e];
-    po[e] = (c + tile - 1) / tile * tile;
-    base[e] = p.excl[(size_t)blk * El + e];
+    int tot = 0, pre = 0;
+    // 16 counting rows and 16 per-block rows in flight at a time
+    for (int r0 = 0; r0 < p.num_super || g0 + r0 < blk; r0 += 16) {
+      int sv[16], hv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sv[i] = r0 + i < p.num_super ? p.super_rows[(size_t)(r0 + i) * El + e] : 0;
+        hv[i] = g0 + r0 + i < blk ? p.hist[(size_t)(g0 + r0 + i) * El + e] : 0;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        tot += sv[i];
+        pre += (r0 + i < grp ? sv[i] : 0) + hv[i];
+      }
+    }
+    cnt[e] = tot;
+    base[e] = pre;
+    po[e] = (tot + tile - 1) / tile * tile;
     msk[e] = 0;
   }
   if (tid == 0) po[El] = 0;
   __syncthreads();
+  // Every thread's counting-row reads have returned (their sums are in LDS):
+  // count this block, on one of kDoneLanes sub-counters (blocks b = j mod
+  // kDoneLanes) so that no address takes more than nb / kDoneLanes atomics;
+  // the last block of each sub-counter then counts on the top counter.  The
+  // return value is awaited only at the end, so that its latency overlaps the
+  // rest of the block's work.
+  const int dj = blk % kDoneLanes;
+  const unsigned dn = (unsigned)((nb - dj + kDoneLanes - 1) / kDoneLanes);   // blocks of sub-counter dj
+  unsigned done_before = 0u;
+  if (tid == kScatterThreads - 64) done_before = atomicAdd(p.done + (dj + 1) * kDoneStride, 1u);
 
   // wave 0: exclusive scan of the padded sizes; everyone: token bitmasks
   if (tid < 64) {
@@ -614,7 +615,6 @@ __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams 
   }
   __syncthreads();
   const int total = po[El];
-  const int ntiles = total / tile;
 
 #pragma unroll
   for (int i = 0; i < kScatterPairsPerThread; ++i) {
@@ -631,25 +631,44 @@ __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams 
     p.e2p[(size_t)t0 * k + q] = slot;
   }
 
-  for (int c = blk * kScatterThreads + tid; c < ntiles; c += gridDim.x * kScatterThreads) {
-    const int pos = c * tile;
-    int lo = 0, hi = El - 1;            // last e with po[e] <= pos
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (po[mid] <= pos) lo = mid; else hi = mid - 1;
+  // tiles of this block's experts
+  const int e_lo = (int)((int64_t)blk * El / nb);
+  const int e_hi = (int)((int64_t)(blk + 1) * El / nb);
+  for (int e = e_lo; e < e_hi; ++e) {
+    const int seg = po[e];
+    const int seg_end = seg + cnt[e];
+    const int ntile = (po[e + 1] - seg) / tile;
+    for (int j = tid; j < ntile; j += kScatterThreads) {
+      const int c = seg / tile + j;
+      p.batch_idx[c] = e;
+      p.mn_limit[c] = min(seg + (j + 1) * tile, seg_end);
     }
-    const int seg_end = po[lo] + p.counts[lo];
-    p.batch_idx[c] = lo;
-    p.mn_limit[c] = min(pos + tile, seg_end);
-    for (int s2 = max(pos, seg_end); s2 < pos + tile; ++s2) p.p2t[s2] = -1;
+    for (int s2 = seg_end + tid; s2 < po[e + 1]; s2 += kScatterThreads) p.p2t[s2] = -1;
   }
   if (blk == 0) {
-    for (int e = tid; e <= El; e += kScatterThreads) p.padded_offsets[e] = po[e];
+    for (int e = tid; e <= El; e += kScatterThreads) {
+      p.padded_offsets[e] = po[e];
+      if (e < El) p.counts[e] = cnt[e];
+    }
     if (tid == 0) {
       *p.total_out = total;
-      *p.nctas_out = ntiles;
+      *p.nctas_out = total / tile;
     }
   }
+  // the last block to finish reading the counting rows clears them
+  if (tid == kScatterThreads - 64) {
+    bool last = false;
+    if (done_before == dn - 1u) {                  // last of its sub-counter
+      p.done[(dj + 1) * kDoneStride] = 0u;         // nobody else touches it in this call
+      const unsigned nsub = (unsigned)min(nb, kDoneLanes);
+      last = atomicAdd(p.done, 1u) == nsub - 1u;
+      if (last) p.done[0] = 0u;
+    }
+    last_block = last;
+  }
+  __syncthreads();
+  if (last_block)
+    for (int i = tid; i < p.num_super * El; i += kScatterThreads) p.super_rows[i] = 0;
 }
 
 // T = 0: the bookkeeping outputs still hold their defined values.
@@ -710,12 +729,14 @@ hipError_t launch_route(const RouteParams& p, int lpt, int epl, bool bf16, int n
   return kRouteTable[bf16 ? 1 : 0][ei][li](p, nb, s);
 }
 
-hipError_t launch_scan(int32_t* hist, int nb, int El, int32_t* counts, hipStream_t s) {
-  MOE_LAUNCH(scan_kernel, dim3((El + 63) / 64), dim3(1024), 0, s, hist, nb, El, counts);
+hipError_t launch_counts(int32_t* super_rows, int num_super, int El, int32_t* counts,
+                         hipStream_t s) {
+  MOE_LAUNCH(counts_kernel, dim3((El + 255) / 256), dim3(256), 0, s, super_rows, num_super, El,
+             counts);
   return hipGetLastError();
 }
 
-size_t scatter_lds_bytes(int El) { return (size_t)El * 8 + (size_t)(El + 1) * 4 + (size_t)El * 4; }
+size_t scatter_lds_bytes(int El) { return (size_t)El * 8 + (size_t)(El + 1) * 4 + (size_t)El * 8; }
 
 hipError_t launch_scatter(const ScatterParams& p, int nb, hipStream_t s) {
   MOE_LAUNCH(scatter_kernel, dim3(nb), dim3(kScatterThreads), scatter_lds_bytes(p.El), s, p);
