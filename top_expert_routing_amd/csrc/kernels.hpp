@@ -97,7 +97,8 @@ __host__ __device__ inline RouteLds route_lds_layout(int lpt, int epl, int hmask
   L.row_stride = lpt * (epl + 4) + 4;          // floats, a multiple of 4
   L.cand_stride = cap + 2;                     // even: 16-byte aligned rows
   L.sel_stride = k + 1;
-  L.gs_stride = n_group > 0 ? n_group + 1 : 0;
+  // group scores are read four at a time over the whole cluster (n_group <= lpt)
+  L.gs_stride = n_group > 0 ? (((n_group > lpt ? n_group : lpt) + 3) & ~3) : 0;
   int off = 0;
   auto take = [&](int bytes) { const int o = off; off += (bytes + 15) & ~15; return o; };
   L.bias = take(lpt * epl * 4);

@@ -97,138 +97,108 @@ __device__ __forceinline__ float fast_rcp(float v) { return __builtin_amdgcn_rcp
 
 }  // namespace
 
-// Per-token context the emitters need.
+// Weights of the selected experts (uniform per call):
+//   plain      weight = score basis (sigmoid score, or the softmax probability
+//              when a bias forced the probabilities to be formed first),
+//              optionally renormalised over the k selected;
+//   exact_pre  softmax over all E without renormalisation: exp(r - m) / sum;
+//   soft_sel   softmax over the k selected (softmax after top-k, or softmax
+//              before top-k renormalised, which is the same distribution).
+enum { kEmitPlain = 0, kEmitExactPre = 1, kEmitSoftSel = 2 };
+
+// Per-token values the emission needs.
 struct EmitCtx {
   int32_t* ids;
   void* weights;
-  bool weights_bf16, renorm, hist;
-  int k, loc_off, loc_n;
+  bool weights_bf16, renorm, counting;
+  int mode, k, loc_off, loc_n;
   float scale;
   uint64_t* hmask;
-  const float* rowc;      // the cluster's score-basis row (padded per lane)
   int t, tl, lane_c;
-  bool tv, plain, exact_pre;
+  bool tv;
   float m, inv_s;
 };
 
-template <int EPL>
-__device__ __forceinline__ float row_at(const float* rowc, int e) {
-  return rowc[(e / EPL) * (EPL + 4) + (e % EPL)];
+// Rank the cluster's C candidates by counting among the first T entries of its
+// candidate list (entries C..T-1 hold 0, below every packed key).  Lane c
+// ranks entries c, c + LPT, ...; a candidate of rank n < k is recorded at
+// position n of the selection list.
+template <int LPT, int T>
+__device__ __forceinline__ void rank_tier(const uint64_t* mycand, const float* mycandr, int C,
+                                          int k, int lane_c, int* myselidx, float* myselr) {
+  constexpr int CHUNK = T < 32 ? T : 32;
+  uint64_t cv[CHUNK];
+  if constexpr (T <= 32) {
+#pragma unroll
+    for (int i = 0; i < T; i += 2) {
+      const u64x2 v = *reinterpret_cast<const u64x2*>(mycand + i);
+      cv[i] = v.x;
+      cv[i + 1] = v.y;
+    }
+  }
+  for (int j = lane_c; j < C; j += LPT) {
+    const uint64_t mine = mycand[j];
+    int rank = 0;
+    if constexpr (T <= 32) {
+#pragma unroll
+      for (int i = 0; i < T; ++i) rank += cv[i] > mine ? 1 : 0;
+    } else {
+      for (int i0 = 0; i0 < T; i0 += CHUNK) {
+#pragma unroll
+        for (int i = 0; i < CHUNK; i += 2) {
+          const u64x2 v = *reinterpret_cast<const u64x2*>(mycand + i0 + i);
+          rank += (v.x > mine ? 1 : 0) + (v.y > mine ? 1 : 0);
+        }
+      }
+    }
+    if (rank < k) {
+      myselidx[rank] = unpack_idx(mine);
+      myselr[rank] = mycandr[j];
+    }
+  }
 }
 
-// Weights and outputs for the S slots a lane holds: slot q has rank n[q]
-// (n < k is selected), expert e[q] and score basis r[q].
-template <int LPT, int S>
-__device__ __forceinline__ void emit_slots(const EmitCtx& c, const int (&n)[S], const int (&e)[S],
-                                           const float (&r)[S]) {
+// Weights, ids and the block bitmask for the k selected, by rank: lane c
+// handles ranks c, c + LPT, ... (contiguous stores across the cluster).
+template <int LPT>
+__device__ __forceinline__ void emit_selected(const EmitCtx& c, const int* myselidx,
+                                              const float* myselr) {
   const int k = c.k;
   float ref = 0.0f;
-  if (!c.plain && !c.exact_pre) {
-    float mx = -kInf;
-#pragma unroll
-    for (int q = 0; q < S; ++q) mx = n[q] < k ? fmaxf(mx, r[q]) : mx;
+  if (c.mode == kEmitSoftSel) {
+    float mx = -__builtin_huge_valf();
+    for (int n = c.lane_c; n < k; n += LPT) mx = fmaxf(mx, myselr[n]);
     ref = cl_max<LPT>(mx);
   }
-  float part = 0.0f;
-#pragma unroll
-  for (int q = 0; q < S; ++q)
-    part += n[q] < k ? (c.plain ? r[q] : (c.exact_pre ? 0.0f : exp_f32(r[q] - ref))) : 0.0f;
-  const float inv_den = fast_rcp(cl_sum<LPT>(part));
+  float inv_den = c.inv_s;
+  if (c.mode != kEmitExactPre) {
+    float part = 0.0f;
+    for (int n = c.lane_c; n < k; n += LPT)
+      part += c.mode == kEmitPlain ? myselr[n] : exp_f32(myselr[n] - ref);
+    inv_den = fast_rcp(cl_sum<LPT>(part));
+  }
   if (!c.tv) return;
-#pragma unroll
-  for (int q = 0; q < S; ++q) {
-    if (n[q] < k) {
-      float w;
-      if (c.plain)
-        w = c.renorm ? r[q] * inv_den : r[q];
-      else if (c.exact_pre)
-        w = exp_f32(r[q] - c.m) * c.inv_s;
-      else
-        w = exp_f32(r[q] - ref) * inv_den;
-      w *= c.scale;
-      const size_t o = (size_t)c.t * k + n[q];
-      c.ids[o] = e[q];
-      if (c.weights_bf16)
-        static_cast<uint16_t*>(c.weights)[o] = (uint16_t)f32_to_bf16_rne(w);
-      else
-        static_cast<float*>(c.weights)[o] = w;
-      if (c.hist) {
-        const int el = e[q] - c.loc_off;
-        if (el >= 0 && el < c.loc_n) atomicOr(&c.hmask[el], 1ull << c.tl);
-      }
+  const float sub = c.mode == kEmitExactPre ? c.m : ref;
+  for (int n = c.lane_c; n < k; n += LPT) {
+    const float r = myselr[n];
+    const int e = myselidx[n];
+    float w;
+    if (c.mode == kEmitPlain)
+      w = c.renorm ? r * inv_den : r;
+    else
+      w = exp_f32(r - sub) * inv_den;
+    w *= c.scale;
+    const size_t o = (size_t)c.t * k + n;
+    c.ids[o] = e;
+    if (c.weights_bf16)
+      static_cast<uint16_t*>(c.weights)[o] = (uint16_t)f32_to_bf16_rne(w);
+    else
+      static_cast<float*>(c.weights)[o] = w;
+    if (c.counting) {
+      const int el = e - c.loc_off;
+      if (el >= 0 && el < c.loc_n) atomicOr(&c.hmask[el], 1ull << c.tl);
     }
   }
-}
-
-// Candidate ranks by counting over a statically sized candidate list (NC
-// slots read with 16-byte broadcasts): rank = number of candidates ordered
-// before, over the first C slots.  Selected candidates (rank < k) are recorded
-// in rank order with their score basis.
-template <int LPT, int NC, int EPL>
-__device__ __forceinline__ void rank_static(const uint64_t* mycand, const float* rowc, int C,
-                                            int k, int lane_c, int* myselidx, float* myselr) {
-  uint64_t cv[NC];
-#pragma unroll
-  for (int q = 0; q < NC; q += 2) {
-    const u64x2 v = *reinterpret_cast<const u64x2*>(mycand + q);
-    cv[q] = v.x;
-    cv[q + 1] = v.y;
-  }
-#pragma unroll
-  for (int s0 = 0; s0 < NC; s0 += LPT) {
-    const int j = s0 + lane_c;
-    if (j < C) {
-      const uint64_t mine = mycand[j];
-      int rank = 0;
-#pragma unroll
-      for (int i = 0; i < NC; ++i) rank += (i < C && cv[i] > mine) ? 1 : 0;
-      if (rank < k) {
-        const int e = unpack_idx(mine);
-        myselidx[rank] = e;
-        myselr[rank] = row_at<EPL>(rowc, e);
-      }
-    }
-  }
-}
-
-// Rank the candidates by counting (static tiers of 16 and 32 slots, a loop
-// beyond), then emit from the rank-ordered selection list.
-template <int LPT, int EPL>
-__device__ __forceinline__ void counted_emit(const EmitCtx& c, const uint64_t* mycand, int C,
-                                             int* myselidx, float* myselr) {
-  const int k = c.k;
-  constexpr int EP = LPT * EPL;
-  if (C <= 16) {
-    rank_static<LPT, 16, EPL>(mycand, c.rowc, C, k, c.lane_c, myselidx, myselr);
-  } else if (EP > 16 && C <= 32) {
-    rank_static<LPT, (EP > 16 ? 32 : 16), EPL>(mycand, c.rowc, C, k, c.lane_c, myselidx, myselr);
-  } else {
-    for (int j = c.lane_c; j < C; j += LPT) {
-      const uint64_t mine = mycand[j];
-      int rank = 0;
-#pragma unroll 4
-      for (int i = 0; i < C; ++i) rank += mycand[i] > mine ? 1 : 0;
-      if (rank < k) {
-        const int e = unpack_idx(mine);
-        myselidx[rank] = e;
-        myselr[rank] = row_at<EPL>(c.rowc, e);
-      }
-    }
-  }
-  wave_lds_sync();
-  constexpr int KMAX = LPT * EPL < 64 ? LPT * EPL : 64;     // k <= min(E, 64)
-  constexpr int Q = (KMAX + LPT - 1) / LPT;
-  int n[Q], e[Q];
-  float r[Q];
-#pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    n[q] = c.lane_c + q * LPT;
-    const bool ok = n[q] < k;
-    e[q] = ok ? myselidx[n[q]] : 0;
-    r[q] = ok ? myselr[n[q]] : 0.0f;
-    if (!ok) n[q] = k;
-  }
-  emit_slots<LPT, Q>(c, n, e, r);
 }
 
 // One template instance per (lanes per token, experts per lane, logits dtype).
@@ -252,32 +222,7 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>) route_kernel(RouteParams p) 
   const int e0 = lane_c * EPL;
   const int E = p.E, k = p.k;
   const int blk = blockIdx.x;
-
-  // The first token's logits and this lane's bias are requested first.
-  RawRow<EPL, BF16> raw;
-  {
-    const int t = blk * kTokensPerBlock + cl;
-    load_raw<EPL, BF16>(raw, p.logits, (size_t)t * E, e0, E, p.vec, t < p.T);
-  }
-  float breg[EPL];
-  if (p.bias != nullptr && !p.bias_bf16 && p.bias_vec && e0 + EPL <= E) {
-    const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(p.bias) + e0);
-#pragma unroll
-    for (int v = 0; v < EPL / 4; ++v) {
-      const f32x4 q = src[v];
-      breg[4 * v] = q.x; breg[4 * v + 1] = q.y; breg[4 * v + 2] = q.z; breg[4 * v + 3] = q.w;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int e = e0 + i;
-      float b = e < E ? 0.0f : -kInf;
-      if (p.bias != nullptr && e < E)
-        b = p.bias_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(p.bias)[e])
-                        : static_cast<const float*>(p.bias)[e];
-      breg[i] = b;
-    }
-  }
+  const bool has_bias = p.bias != nullptr;
 
   const RouteLds L = route_lds_layout(LPT, EPL, p.hmask_len, p.cap, k, p.grouped ? p.n_group : 0);
   extern __shared__ __align__(16) unsigned char smem[];
@@ -290,21 +235,45 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>) route_kernel(RouteParams p) 
   float* myselr = reinterpret_cast<float*>(smem + L.sel_r) + cl * L.sel_stride;
   float* mygs = reinterpret_cast<float*>(smem + L.gscore) + cl * L.gs_stride;
 
-  if (cl == 0) {
-#pragma unroll
-    for (int i = 0; i < EPL; i += 4)
-      *reinterpret_cast<f32x4*>(bias_s + e0 + i) = f32x4{breg[i], breg[i + 1], breg[i + 2], breg[i + 3]};
+  // The bias is requested first (one block-wide pass into LDS), then the
+  // first token's logits; the bias lands in LDS while the logits are in flight.
+  float bload = 0.0f;
+  const bool bthread = tid < EP;
+  if (bthread) {
+    if (tid >= E)
+      bload = -kInf;
+    else if (has_bias)
+      bload = p.bias_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(p.bias)[tid])
+                          : static_cast<const float*>(p.bias)[tid];
+  }
+  RawRow<EPL, BF16> raw;
+  {
+    const int t = blk * kTokensPerBlock + cl;
+    load_raw<EPL, BF16>(raw, p.logits, (size_t)t * E, e0, E, p.vec, t < p.T);
+  }
+  for (int e = tid; e < EP; e += BLOCK) {          // EP > BLOCK only for very wide rows
+    float b = e == tid ? bload : (e >= E ? -kInf : 0.0f);
+    if (e != tid && e < E && has_bias)
+      b = p.bias_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(p.bias)[e])
+                      : static_cast<const float*>(p.bias)[e];
+    bias_s[e] = b;
   }
   const bool counting = p.super_rows != nullptr;
   if (counting)
     for (int e = tid; e < p.loc_n; e += BLOCK) hmask[e] = 0;
   __syncthreads();
+  float breg[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; i += 4) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(bias_s + e0 + i);
+    breg[i] = v.x; breg[i + 1] = v.y; breg[i + 2] = v.z; breg[i + 3] = v.w;
+  }
 
   const bool sigmoid = p.kind == kKindSigmoid;
   const bool pre = p.kind == kKindSoftmaxPre;
-  const bool has_bias = p.bias != nullptr;
   const bool need_ms = !sigmoid && ((pre && (has_bias || !p.renorm)) || p.scores != nullptr);
-  const uint32_t lane_bits = EPL == 32 ? 0xffffffffu : ((1u << EPL) - 1u);
+  const int mode = (sigmoid || (pre && has_bias)) ? kEmitPlain
+                   : ((pre && !p.renorm) ? kEmitExactPre : kEmitSoftSel);
 
   for (int it = 0; it < TPC; ++it) {
     const int tl = it * NCL + cl;               // token within the block
@@ -320,13 +289,14 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>) route_kernel(RouteParams p) 
     // ---- score basis r (kept in x) and selection key --------------------------
     float m = 0.0f, inv_s = 0.0f, ssum = 0.0f;
     if (sigmoid) {
-      float part = 0.0f;
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        x[i] = sigmoid_f32(x[i]);               // sigmoid(-inf) = 0
-        part += x[i];
+      for (int i = 0; i < EPL; ++i) x[i] = sigmoid_f32(x[i]);     // sigmoid(-inf) = 0
+      if (p.scores != nullptr) {
+        float part = 0.0f;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) part += x[i];
+        ssum = cl_sum<LPT>(part);
       }
-      if (p.scores != nullptr) ssum = cl_sum<LPT>(part);
     } else if (need_ms) {
       float mx = -kInf;
 #pragma unroll
@@ -371,9 +341,14 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>) route_kernel(RouteParams p) 
       wave_lds_sync();
       int rank = 0;
 #pragma unroll
-      for (int h = 0; h < LPT; ++h) {           // n_group <= LPT
-        const float gh = h < p.n_group ? mygs[h] : -kInf;
-        rank += (h < p.n_group && (gh > gs || (gh == gs && h < myg))) ? 1 : 0;
+      for (int h0 = 0; h0 < LPT; h0 += 4) {     // n_group <= LPT
+        const f32x4 v = *reinterpret_cast<const f32x4*>(mygs + h0);
+        const float gv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int u = 0; u < 4 && h0 + u < LPT; ++u) {
+          const int h = h0 + u;
+          rank += (h < p.n_group && (gv[u] > gs || (gv[u] == gs && h < myg))) ? 1 : 0;
+        }
       }
       kept = kept && myg < p.n_group && rank < p.topk_group;
     }
@@ -382,42 +357,38 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>) route_kernel(RouteParams p) 
     const int cnt_l = kept ? (m1 > -kInf ? 1 : 0) + (m2 > -kInf ? 1 : 0) : 0;
     float tau = cl_min<LPT>(cnt_l == 2 ? m2 : (cnt_l == 1 ? m1 : kInf));
     if (cl_sum_i<LPT>(cnt_l) < k) tau = kLowest;          // every finite key qualifies
-    // candidate bit i: key[i] - tau >= 0, read from the sign bit (no lane masks)
+    // candidate bits: key[i] >= tau.  The sign bit of key[i] - tau marks the
+    // keys below tau (-inf stays -inf; equal keys give +0); alignbit shifts it
+    // in, top element first, so that bit i belongs to element i.
     uint32_t below = 0;
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) below |= (__float_as_uint(key[i] - tau) >> 31) << i;
+    for (int i = EPL - 1; i >= 0; --i)
+      below = __builtin_amdgcn_alignbit(below, __float_as_uint(key[i] - tau), 31);
+    const uint32_t lane_bits = EPL == 32 ? 0xffffffffu : ((1u << EPL) - 1u);
     const uint32_t cmask = kept ? (~below & lane_bits) : 0u;
     const int pc = __builtin_popcount(cmask);
     const int coff = cl_excl_scan<LPT>(pc, lane_c);
     int C = cl_sum_i<LPT>(pc);
 
     if (C <= p.cap) {
-      // compact the candidates: four set bits per round, reads batched
+      // compact the candidates, two set bits per round
       uint32_t mm = cmask;
       int pos = coff;
       while (mm) {
-        int ii[4];
-        bool hv[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          hv[q] = mm != 0u;
-          ii[q] = hv[q] ? __builtin_ctz(mm) : 0;
-          mm &= hv[q] ? mm - 1u : mm;
+        const int i0 = __builtin_ctz(mm);
+        mm &= mm - 1u;
+        const bool h1 = mm != 0u;
+        const int i1 = h1 ? __builtin_ctz(mm) : i0;
+        mm &= h1 ? mm - 1u : mm;
+        const float r0 = myrow[i0], r1 = myrow[i1];
+        const float b0 = bias_s[e0 + i0], b1 = bias_s[e0 + i1];
+        mycand[pos] = pack_key(r0 + b0, e0 + i0);
+        mycandr[pos] = r0;
+        if (h1) {
+          mycand[pos + 1] = pack_key(r1 + b1, e0 + i1);
+          mycandr[pos + 1] = r1;
         }
-        float rr[4], bb[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          rr[q] = myrow[ii[q]];
-          bb[q] = bias_s[e0 + ii[q]];
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (hv[q]) {
-            mycand[pos] = pack_key(rr[q] + bb[q], e0 + ii[q]);
-            mycandr[pos] = rr[q];
-            ++pos;
-          }
-        }
+        pos += h1 ? 2 : 1;
       }
     } else {
       // many keys tie at tau: k rounds of a cluster-wide maximum instead
@@ -444,31 +415,45 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>) route_kernel(RouteParams p) 
       }
       C = k;
     }
+    // ranking tier: the smallest of 4..64 that holds every cluster's list in
+    // this wavefront (uniform, so the wavefront takes one path); the entries
+    // between C and the tier are zeroed
+    int tier;
+    if (__ballot(C > 4) == 0ull) tier = 4;
+    else if (__ballot(C > 8) == 0ull) tier = 8;
+    else if (__ballot(C > 16) == 0ull) tier = 16;
+    else if (__ballot(C > 32) == 0ull) tier = 32;
+    else tier = 64;
+    for (int j = C + lane_c; j < tier; j += LPT) mycand[j] = 0ull;
     wave_lds_sync();
 
     // ---- order the candidates, emit the top k ---------------------------------
+    if (tier == 4) rank_tier<LPT, 4>(mycand, mycandr, C, k, lane_c, myselidx, myselr);
+    else if (tier == 8) rank_tier<LPT, 8>(mycand, mycandr, C, k, lane_c, myselidx, myselr);
+    else if (tier == 16) rank_tier<LPT, 16>(mycand, mycandr, C, k, lane_c, myselidx, myselr);
+    else if (tier == 32) rank_tier<LPT, 32>(mycand, mycandr, C, k, lane_c, myselidx, myselr);
+    else rank_tier<LPT, 64>(mycand, mycandr, C, k, lane_c, myselidx, myselr);
+    wave_lds_sync();
     {
       EmitCtx ec;
       ec.ids = p.ids;
       ec.weights = p.weights;
       ec.weights_bf16 = p.weights_bf16 != 0;
       ec.renorm = p.renorm != 0;
-      ec.hist = counting;
+      ec.counting = counting;
+      ec.mode = mode;
       ec.k = k;
       ec.loc_off = p.loc_off;
       ec.loc_n = p.loc_n;
       ec.scale = p.scale;
       ec.hmask = hmask;
-      ec.rowc = myrow - lane_c * LSTR;
       ec.t = t;
       ec.tl = tl;
       ec.lane_c = lane_c;
       ec.tv = tv;
-      ec.plain = sigmoid || (pre && has_bias);       // weight = basis (s or p)
-      ec.exact_pre = pre && !has_bias && !p.renorm;
       ec.m = m;
       ec.inv_s = inv_s;
-      counted_emit<LPT, EPL>(ec, mycand, C, myselidx, myselr);
+      emit_selected<LPT>(ec, myselidx, myselr);
     }
     if (tv) {
       // ---- full-E scores for the aux loss --------------------------------------------
