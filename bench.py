@@ -59,7 +59,7 @@ def parse():
 def kernel_sources_digest() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "top_expert_routing_amd", "csrc")
-    for name in ("route_kernels.hip", "device_common.hpp", "kernels.hpp"):
+    for name in ("route_kernel.hpp", "route_sigmoid.hip", "device_common.hpp", "kernels.hpp"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()

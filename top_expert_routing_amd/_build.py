@@ -21,7 +21,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_DIR = os.path.join(HERE, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libmoe_route.so")
 
-SOURCES = ["route_kernels.hip", "aux_loss.hip", "front_end.hip", "api.cpp"]
+SOURCES = ["route_sigmoid.hip", "route_softmax.hip", "route_softmax_bias.hip",
+           "route_kernels.hip", "aux_loss.hip", "front_end.hip", "api.cpp"]
 ARCH = os.environ.get("MOE_ROUTE_ARCH", "gfx950")
 
 COMMON_FLAGS = [
@@ -59,7 +60,7 @@ def build(verbose: bool = False) -> str:
     """Compile every source and link the shared library; return its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     os.makedirs(LIB_DIR, exist_ok=True)
-    jobs = min(len(SOURCES), int(os.environ.get("MAX_JOBS", "4")))
+    jobs = min(len(SOURCES), int(os.environ.get("MAX_JOBS", "8")))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB_PATH + ".tmp"

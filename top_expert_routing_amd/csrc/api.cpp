@@ -103,6 +103,11 @@ hipError_t launch_with_profile(int kind, hipStream_t stream, F&& f, bool single_
 }
 
 bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+int log2_exact(int v) {   // v a power of two
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  return l;
+}
 int next_pow2(int v) {
   int p = 1;
   while (p < v) p <<= 1;
@@ -244,9 +249,10 @@ moe::RouteParams make_params(const moe_route_args& a, const Shape& sh, const voi
   p.T = a.num_tokens;
   p.E = a.num_experts;
   p.k = a.top_k;
-  p.kind = a.score_fn == MOE_SIGMOID
-               ? moe::kKindSigmoid
-               : (a.use_pre_softmax ? moe::kKindSoftmaxPre : moe::kKindSoftmaxPost);
+  p.variant = a.score_fn == MOE_SIGMOID
+                  ? moe::kVarSigmoid
+                  : (bias != nullptr ? moe::kVarSoftmaxBias : moe::kVarSoftmax);
+  p.pre = a.score_fn == MOE_SOFTMAX && a.use_pre_softmax != 0;
   p.bias_bf16 = a.bias_dtype == MOE_BF16;
   p.weights_bf16 = a.weights_dtype == MOE_BF16;
   p.grouped = grouping_on(a);
@@ -254,6 +260,7 @@ moe::RouteParams make_params(const moe_route_args& a, const Shape& sh, const voi
   p.topk_group = a.topk_group;
   p.topn = a.group_score_topn;
   p.lg = sh.lg;
+  p.lg_shift = log2_exact(sh.lg);
   p.renorm = a.renormalize != 0;
   p.scale = a.routed_scaling_factor;
   const size_t esz = a.logits_dtype == MOE_BF16 ? 2 : 4;
@@ -269,7 +276,8 @@ moe::RouteParams make_params(const moe_route_args& a, const Shape& sh, const voi
 
 moe_status launch_route_checked(const moe::RouteParams& p, const Shape& sh, bool bf16,
                                 hipStream_t stream) {
-  const size_t lds = moe::route_lds_bytes(sh.lpt, sh.epl, p.hmask_len, p.cap, p.k,
+  const int rwpl = (p.variant == moe::kVarSoftmax && bf16) ? sh.epl / 2 : sh.epl;
+  const size_t lds = moe::route_lds_bytes(sh.lpt, rwpl, sh.epl, p.hmask_len, p.cap, p.k,
                                           p.grouped ? p.n_group : 0);
   if (lds > 160 * 1024)
     return fail(MOE_EUNSUPPORTED, "route kernel needs %zu bytes of LDS", lds);
@@ -459,6 +467,8 @@ moe_status moe_route_permute(const moe_route_args* args, int32_t tile, int32_t l
   q.El = loc_n;
   q.off = loc_off;
   q.tile = tile;
+  q.tile_shift = log2_exact(tile);
+  q.k_magic = (uint32_t)(((1u << 20) + (uint32_t)a.top_k - 1u) / (uint32_t)a.top_k);
   q.super_rows = rows;
   q.hist = hist;
   q.done = ws_done(workspace);

@@ -39,7 +39,9 @@ constexpr int kMaxSuperRows = 64;
 template <int LPT>
 constexpr int kRouteBlock = (LPT * 64 < 512) ? LPT * 64 : 512;
 
-enum { kKindSigmoid = 0, kKindSoftmaxPre = 1, kKindSoftmaxPost = 2 };
+// Score variants, one kernel instance each: sigmoid (bias optional), softmax
+// without bias, softmax with bias (before or after top-k is a run-time flag).
+enum { kVarSigmoid = 0, kVarSoftmax = 1, kVarSoftmaxBias = 2 };
 
 struct RouteParams {
   const void* logits;
@@ -51,10 +53,11 @@ struct RouteParams {
   int32_t* hist;          // nullable [nb, loc_n]: per-block counts, for the permutation
   int group_blocks;       // blocks that add into one counting row
   int T, E, k;
-  int kind;
+  int variant;            // kVar*
+  int pre;                // softmax before top-k
   int bias_bf16;
   int weights_bf16;
-  int grouped, n_group, topk_group, topn, lg;
+  int grouped, n_group, topk_group, topn, lg, lg_shift;   // lg = 1 << lg_shift lanes per group
   int renorm;
   float scale;
   int vec;                // 16-byte vector loads of logits allowed
@@ -67,6 +70,8 @@ struct RouteParams {
 struct ScatterParams {
   const int32_t* ids;
   int T, k, El, off, tile;
+  int tile_shift;         // tile = 1 << tile_shift
+  uint32_t k_magic;       // ceil(2^20 / k): (q * k_magic) >> 20 = q / k for q < 4096
   int32_t* super_rows;    // [num_super, El], cleared by the last block
   const int32_t* hist;    // [nb, El] per-block counts
   uint32_t* done;         // block counters ([0] top, [64 * (j + 1)] sub-counter j), reset by
@@ -83,37 +88,36 @@ struct ScatterParams {
 };
 
 // Byte offsets of the route kernel's LDS regions (shared by host and device).
-// Per-cluster strides are padded so that the clusters of one wavefront fall
-// on different LDS banks.
+// Per cluster: the row (rwpl 32-bit words per lane: raw logits or float32
+// score basis, padded so that the clusters of one wavefront fall on different
+// LDS banks), the packed candidate keys, the experts of the selection by rank,
+// and the packed group keys.
 struct RouteLds {
-  int bias, hmask, row, cand, cand_r, sel_idx, sel_r, gscore, total;
+  int bias, hmask, row, cand, sel_idx, gscore, total;
   int row_stride, cand_stride, sel_stride, gs_stride;   // in elements
 };
-__host__ __device__ inline RouteLds route_lds_layout(int lpt, int epl, int hmask_len, int cap, int k,
-                                                    int n_group) {
+__host__ __device__ inline RouteLds route_lds_layout(int lpt, int rwpl, int epl, int hmask_len,
+                                                    int cap, int k, int n_group) {
   RouteLds L{};
   const int block = lpt * 64 < 512 ? lpt * 64 : 512;
   const int ncl = block / lpt;
-  L.row_stride = lpt * (epl + 4) + 4;          // floats, a multiple of 4
+  L.row_stride = ((lpt * rwpl + 3) & ~3) + 4;  // words, a multiple of 4
   L.cand_stride = cap + 2;                     // even: 16-byte aligned rows
   L.sel_stride = k + 1;
-  // group scores are read four at a time over the whole cluster (n_group <= lpt)
-  L.gs_stride = n_group > 0 ? (((n_group > lpt ? n_group : lpt) + 3) & ~3) : 0;
+  L.gs_stride = n_group > 0 ? ((lpt + 1) & ~1) : 0;   // u64 group keys, read two at a time
   int off = 0;
   auto take = [&](int bytes) { const int o = off; off += (bytes + 15) & ~15; return o; };
   L.bias = take(lpt * epl * 4);
   L.hmask = take(hmask_len * 8);
   L.row = take(ncl * L.row_stride * 4);
   L.cand = take(ncl * L.cand_stride * 8);
-  L.cand_r = take(ncl * L.cand_stride * 4);
   L.sel_idx = take(ncl * L.sel_stride * 4);
-  L.sel_r = take(ncl * L.sel_stride * 4);
-  L.gscore = take(ncl * L.gs_stride * 4);
+  L.gscore = take(ncl * L.gs_stride * 8);
   L.total = off;
   return L;
 }
 
-size_t route_lds_bytes(int lpt, int epl, int hmask_len, int cap, int k, int n_group);
+size_t route_lds_bytes(int lpt, int rwpl, int epl, int hmask_len, int cap, int k, int n_group);
 size_t scatter_lds_bytes(int El);
 hipError_t launch_route(const RouteParams& p, int lpt, int epl, bool bf16, int nb, hipStream_t s);
 hipError_t launch_counts(int32_t* super_rows, int num_super, int El, int32_t* counts,

@@ -1,0 +1,660 @@
+// The gfx950 route kernel: score function, bias, group-limited top-k, top-k,
+// weights and the per-block expert bitmask, for one token per cluster of LPT
+// lanes (EPL experts per lane).
+//
+// Method (page title, section):
+//   score function, pre/post-softmax order, group top-k, expert bias, scaling:
+//     TransformerEngine Fused Router, Description + I/O Contract;
+//   n_group / topk_group, routing bias, routed_scaling_factor, norm_topk_prob,
+//   local experts: flashinfer trtllm_gen_routing, Parameters, Notes;
+//   float32 sigmoid, selection by score + correction bias, unbiased weights:
+//     MAX SigmoidTopKRouter, routing steps 2-4.
+//
+// Per token: the logits stream HBM -> VGPRs once (16-byte loads) and are kept
+// raw in LDS as well; keys, group scores and a lower bound tau on the k-th key
+// are formed in registers; the few keys >= tau are compacted into LDS as
+// packed (key, index) words, ranked by counting, and the k best are emitted
+// by rank, their score recomputed from the raw logit.  Per block of 64 tokens
+// an LDS bitmask per expert records which tokens chose it; its popcounts are
+// the block's counts row, added into a counting row shared by a group of
+// blocks.
+//
+// One instance per (lanes per token, experts per lane, logits dtype, score
+// variant); this header is included by one translation unit per variant.
+#pragma once
+
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr float kInf = __builtin_huge_valf();
+
+// Raw row slice of one lane: EPL logits as packed 32-bit words (two bf16 or
+// one float32 per word), decoded later so that the loads can be issued before
+// anything else.  Padded experts hold -inf.
+template <int EPL, bool BF16>
+struct RawRow {
+  static constexpr int kWords = BF16 ? EPL / 2 : EPL;
+  uint32_t w[kWords];
+};
+
+template <int EPL, bool BF16>
+__device__ __forceinline__ void load_raw(RawRow<EPL, BF16>& r, const void* __restrict__ base,
+                                         size_t row_elems, int e0, int E, bool vec, bool tv) {
+  constexpr int NW = RawRow<EPL, BF16>::kWords;
+  if (tv && vec && e0 + EPL <= E && NW % 4 == 0) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(
+        static_cast<const char*>(base) + (row_elems + e0) * (BF16 ? 2 : 4));
+#pragma unroll
+    for (int v = 0; v < NW / 4; ++v) {
+      const u32x4 q = __builtin_nontemporal_load(src + v);
+      r.w[4 * v] = q.x; r.w[4 * v + 1] = q.y; r.w[4 * v + 2] = q.z; r.w[4 * v + 3] = q.w;
+    }
+  } else if constexpr (BF16) {
+    const uint16_t* src = static_cast<const uint16_t*>(base) + row_elems;
+#pragma unroll
+    for (int i = 0; i < EPL; i += 2) {
+      const int e = e0 + i;
+      const uint32_t lo = e < E ? (tv ? (uint32_t)src[e] : 0u) : 0xFF80u;
+      const uint32_t hi = e + 1 < E ? (tv ? (uint32_t)src[e + 1] : 0u) : 0xFF80u;
+      r.w[i / 2] = lo | (hi << 16);
+    }
+  } else {
+    const uint32_t* src = static_cast<const uint32_t*>(base) + row_elems;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = e0 + i;
+      r.w[i] = e < E ? (tv ? src[e] : 0u) : 0xFF800000u;
+    }
+  }
+}
+
+template <int EPL, bool BF16>
+__device__ __forceinline__ void decode_raw(const RawRow<EPL, BF16>& r, float (&x)[EPL]) {
+  if constexpr (BF16) {
+#pragma unroll
+    for (int i = 0; i < EPL / 2; ++i) {
+      x[2 * i] = bf16_lo(r.w[i]);
+      x[2 * i + 1] = bf16_hi(r.w[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) x[i] = __uint_as_float(r.w[i]);
+  }
+}
+
+// The cluster's row in LDS, dynamically indexable: for the softmax variant the
+// raw logit words (two bf16 or one float32 per word; the logit is the score
+// basis there), otherwise the float32 score basis of every expert.
+template <int VAR, bool BF16>
+constexpr bool kRawRow = VAR == kVarSoftmax;
+
+template <int VAR, bool BF16>
+__device__ __forceinline__ float row_basis(const uint32_t* rowc, int e) {
+  if constexpr (kRawRow<VAR, BF16> && BF16) {
+    const uint32_t w = rowc[e >> 1];
+    return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+  } else {
+    return __uint_as_float(rowc[e]);
+  }
+}
+
+__device__ __forceinline__ float fast_rcp(float v) { return __builtin_amdgcn_rcpf(v); }
+
+}  // namespace
+
+// Weights of the selected experts (uniform per call):
+//   plain      weight = score basis (sigmoid score, or the softmax probability
+//              when a bias forced the probabilities to be formed first),
+//              optionally renormalised over the k selected;
+//   exact_pre  softmax over all E without renormalisation: exp(r - m) / sum;
+//   soft_sel   softmax over the k selected (softmax after top-k, or softmax
+//              before top-k renormalised, which is the same distribution).
+enum { kEmitPlain = 0, kEmitExactPre = 1, kEmitSoftSel = 2 };
+
+// Rank the cluster's C candidates by counting among the first T entries of its
+// candidate list (entries C..T-1 hold 0, below every packed key).  Lane c
+// ranks entries c, c + LPT, ...; the expert of rank n < k is recorded at
+// position n of the selection list.
+template <int LPT, int T>
+__device__ __forceinline__ void rank_tier(const uint64_t* mycand, int C, int k, int lane_c,
+                                          int* myselidx) {
+  constexpr int CHUNK = T < 32 ? T : 32;
+  uint64_t cv[CHUNK];
+  if constexpr (T <= 32) {
+#pragma unroll
+    for (int i = 0; i < T; i += 2) {
+      const u64x2 v = *reinterpret_cast<const u64x2*>(mycand + i);
+      cv[i] = v.x;
+      cv[i + 1] = v.y;
+    }
+  }
+  constexpr int Q = (T + LPT - 1) / LPT;      // slots per lane
+  if constexpr (T <= 32 && Q <= 8) {
+    uint64_t mine[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) mine[q] = lane_c + q * LPT < T ? mycand[lane_c + q * LPT] : 0ull;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int j = lane_c + q * LPT;
+      int rank = 0;
+#pragma unroll
+      for (int i = 0; i < T; ++i) rank += cv[i] > mine[q] ? 1 : 0;
+      if (j < C && rank < k) myselidx[rank] = unpack_idx(mine[q]);
+    }
+    return;
+  }
+  for (int j = lane_c; j < C; j += LPT) {
+    const uint64_t mine = mycand[j];
+    int rank = 0;
+    if constexpr (T <= 32) {
+#pragma unroll
+      for (int i = 0; i < T; ++i) rank += cv[i] > mine ? 1 : 0;
+    } else {
+      for (int i0 = 0; i0 < T; i0 += CHUNK) {
+#pragma unroll
+        for (int i = 0; i < CHUNK; i += 2) {
+          const u64x2 v = *reinterpret_cast<const u64x2*>(mycand + i0 + i);
+          rank += (v.x > mine ? 1 : 0) + (v.y > mine ? 1 : 0);
+        }
+      }
+    }
+    if (rank < k) myselidx[rank] = unpack_idx(mine);
+  }
+}
+
+// Per-token values the emission needs.
+struct EmitCtx {
+  int32_t* ids;
+  void* weights;
+  bool weights_bf16, renorm, counting, pre;
+  int mode, k, loc_off, loc_n;
+  float scale;
+  uint64_t* hmask;
+  int t, tl, lane_c;
+  bool tv;
+  float m, inv_s;
+};
+
+// Weights, ids and the block bitmask for the k selected, by rank: lane c
+// handles ranks c, c + LPT, ... (contiguous stores across the cluster).  The
+// score basis of each selected expert is recomputed from its raw logit.
+template <int LPT, bool BF16, int VAR>
+__device__ __forceinline__ void emit_selected(const EmitCtx& c, const int* myselidx,
+                                              const uint32_t* rowc) {
+  const int k = c.k;
+  if (k <= LPT) {                             // one rank per lane
+    const bool v = c.lane_c < k;
+    const int e = v ? myselidx[c.lane_c] : 0;
+    const float r = row_basis<VAR, BF16>(rowc, e);
+    float ref = 0.0f;
+    if (c.mode == kEmitSoftSel) ref = cl_max<LPT>(v ? r : -kInf);
+    float inv_den = c.inv_s;
+    if (c.mode != kEmitExactPre)
+      inv_den = fast_rcp(cl_sum<LPT>(v ? (c.mode == kEmitPlain ? r : exp_f32(r - ref)) : 0.0f));
+    if (!c.tv || !v) return;
+    float w;
+    if (c.mode == kEmitPlain)
+      w = c.renorm ? r * inv_den : r;
+    else
+      w = exp_f32(r - (c.mode == kEmitExactPre ? c.m : ref)) * inv_den;
+    w *= c.scale;
+    const size_t o = (size_t)c.t * k + c.lane_c;
+    c.ids[o] = e;
+    if (c.weights_bf16)
+      static_cast<uint16_t*>(c.weights)[o] = (uint16_t)f32_to_bf16_rne(w);
+    else
+      static_cast<float*>(c.weights)[o] = w;
+    if (c.counting) {
+      const int el = e - c.loc_off;
+      if (el >= 0 && el < c.loc_n) atomicOr(&c.hmask[el], 1ull << c.tl);
+    }
+    return;
+  }
+  constexpr int KQ = 4;
+  if (k <= KQ * LPT) {                        // up to four ranks per lane, held in registers
+    int e[KQ];
+    float r[KQ];
+#pragma unroll
+    for (int q = 0; q < KQ; ++q) {
+      const int n = c.lane_c + q * LPT;
+      e[q] = n < k ? myselidx[n] : 0;
+    }
+#pragma unroll
+    for (int q = 0; q < KQ; ++q)
+      r[q] = row_basis<VAR, BF16>(rowc, e[q]);
+    float ref = 0.0f;
+    if (c.mode == kEmitSoftSel) {
+      float mx = -kInf;
+#pragma unroll
+      for (int q = 0; q < KQ; ++q) mx = c.lane_c + q * LPT < k ? fmaxf(mx, r[q]) : mx;
+      ref = cl_max<LPT>(mx);
+    }
+    float inv_den = c.inv_s;
+    if (c.mode != kEmitExactPre) {
+      float part = 0.0f;
+#pragma unroll
+      for (int q = 0; q < KQ; ++q)
+        if (c.lane_c + q * LPT < k) part += c.mode == kEmitPlain ? r[q] : exp_f32(r[q] - ref);
+      inv_den = fast_rcp(cl_sum<LPT>(part));
+    }
+    if (!c.tv) return;
+    const float sub = c.mode == kEmitExactPre ? c.m : ref;
+#pragma unroll
+    for (int q = 0; q < KQ; ++q) {
+      const int n = c.lane_c + q * LPT;
+      if (n < k) {
+        float w;
+        if (c.mode == kEmitPlain)
+          w = c.renorm ? r[q] * inv_den : r[q];
+        else
+          w = exp_f32(r[q] - sub) * inv_den;
+        w *= c.scale;
+        const size_t o = (size_t)c.t * k + n;
+        c.ids[o] = e[q];
+        if (c.weights_bf16)
+          static_cast<uint16_t*>(c.weights)[o] = (uint16_t)f32_to_bf16_rne(w);
+        else
+          static_cast<float*>(c.weights)[o] = w;
+        if (c.counting) {
+          const int el = e[q] - c.loc_off;
+          if (el >= 0 && el < c.loc_n) atomicOr(&c.hmask[el], 1ull << c.tl);
+        }
+      }
+    }
+    return;
+  }
+  float ref = 0.0f;
+  if (c.mode == kEmitSoftSel) {
+    float mx = -kInf;
+    for (int n = c.lane_c; n < k; n += LPT)
+      mx = fmaxf(mx, row_basis<VAR, BF16>(rowc, myselidx[n]));
+    ref = cl_max<LPT>(mx);
+  }
+  float inv_den = c.inv_s;
+  if (c.mode != kEmitExactPre) {
+    float part = 0.0f;
+    for (int n = c.lane_c; n < k; n += LPT) {
+      const float r = row_basis<VAR, BF16>(rowc, myselidx[n]);
+      part += c.mode == kEmitPlain ? r : exp_f32(r - ref);
+    }
+    inv_den = fast_rcp(cl_sum<LPT>(part));
+  }
+  if (!c.tv) return;
+  const float sub = c.mode == kEmitExactPre ? c.m : ref;
+  for (int n = c.lane_c; n < k; n += LPT) {
+    const int e = myselidx[n];
+    const float r = row_basis<VAR, BF16>(rowc, e);
+    float w;
+    if (c.mode == kEmitPlain)
+      w = c.renorm ? r * inv_den : r;
+    else
+      w = exp_f32(r - sub) * inv_den;
+    w *= c.scale;
+    const size_t o = (size_t)c.t * k + n;
+    c.ids[o] = e;
+    if (c.weights_bf16)
+      static_cast<uint16_t*>(c.weights)[o] = (uint16_t)f32_to_bf16_rne(w);
+    else
+      static_cast<float*>(c.weights)[o] = w;
+    if (c.counting) {
+      const int el = e - c.loc_off;
+      if (el >= 0 && el < c.loc_n) atomicOr(&c.hmask[el], 1ull << c.tl);
+    }
+  }
+}
+
+// Padded experts (e >= E) carry logit -inf and bias -inf, so their keys are
+// -inf and no per-element validity masks are needed anywhere.
+template <int LPT, int EPL, bool BF16, int VAR>
+__global__ void __launch_bounds__(kRouteBlock<LPT>) route_kernel(RouteParams p) {
+  constexpr int BLOCK = kRouteBlock<LPT>;
+  constexpr int NCL = BLOCK / LPT;          // clusters (tokens in flight) per block
+  constexpr int TPC = kTokensPerBlock / NCL;
+  constexpr int EP = LPT * EPL;             // padded row length
+  constexpr int WPL = RawRow<EPL, BF16>::kWords;
+  constexpr bool kRaw = kRawRow<VAR, BF16>;
+  constexpr int RWPL = kRaw ? WPL : EPL;     // row words per lane
+  static_assert(TPC * NCL == kTokensPerBlock, "block shape");
+  static_assert(EPL <= 32, "lane masks are 32-bit");
+  constexpr bool kBias = VAR != kVarSoftmax;   // the softmax variant has no bias
+  constexpr float kLowest = -3.402823466e38f;
+
+  const int tid = threadIdx.x;
+  const int lane_c = tid % LPT;
+  const int cl = tid / LPT;
+  const int e0 = lane_c * EPL;
+  const int E = p.E, k = p.k;
+  const int blk = blockIdx.x;
+  const bool pre = p.pre != 0;
+
+  const RouteLds L = route_lds_layout(LPT, RWPL, EPL, p.hmask_len, p.cap, k,
+                                      p.grouped ? p.n_group : 0);
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* bias_s = reinterpret_cast<float*>(smem + L.bias);
+  uint64_t* hmask = reinterpret_cast<uint64_t*>(smem + L.hmask);
+  uint32_t* rowc = reinterpret_cast<uint32_t*>(smem + L.row) + cl * L.row_stride;
+  uint32_t* myrow = rowc + lane_c * RWPL;
+  uint64_t* mycand = reinterpret_cast<uint64_t*>(smem + L.cand) + cl * L.cand_stride;
+  int* myselidx = reinterpret_cast<int*>(smem + L.sel_idx) + cl * L.sel_stride;
+  uint64_t* mygs = reinterpret_cast<uint64_t*>(smem + L.gscore) + cl * L.gs_stride;
+
+  // The bias is requested first (one block-wide pass into LDS), then the
+  // first token's logits; the bias lands in LDS while the logits are in flight.
+  float bload = 0.0f;
+  if (kBias && tid < EP) {
+    if (tid >= E)
+      bload = -kInf;
+    else if (p.bias != nullptr)
+      bload = p.bias_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(p.bias)[tid])
+                          : static_cast<const float*>(p.bias)[tid];
+  }
+  RawRow<EPL, BF16> raw;
+  {
+    const int t = blk * kTokensPerBlock + cl;
+    load_raw<EPL, BF16>(raw, p.logits, (size_t)t * E, e0, E, p.vec, t < p.T);
+  }
+  if constexpr (kBias) {
+    for (int e = tid; e < EP; e += BLOCK) {          // EP > BLOCK only for very wide rows
+      float b = e == tid ? bload : (e >= E ? -kInf : 0.0f);
+      if (e != tid && e < E && p.bias != nullptr)
+        b = p.bias_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(p.bias)[e])
+                        : static_cast<const float*>(p.bias)[e];
+      bias_s[e] = b;
+    }
+  }
+  const bool counting = p.super_rows != nullptr;
+  if (counting)
+    for (int e = tid; e < p.loc_n; e += BLOCK) hmask[e] = 0;
+  __syncthreads();
+  float breg[EPL];
+  if constexpr (kBias) {
+#pragma unroll
+    for (int i = 0; i < EPL; i += 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(bias_s + e0 + i);
+      breg[i] = v.x; breg[i + 1] = v.y; breg[i + 2] = v.z; breg[i + 3] = v.w;
+    }
+  }
+
+  const bool need_ms =
+      VAR == kVarSigmoid ? false
+                         : ((VAR == kVarSoftmax ? (pre && !p.renorm) : pre) || p.scores != nullptr);
+  const int mode = (VAR == kVarSigmoid || (VAR == kVarSoftmaxBias && pre))
+                       ? kEmitPlain
+                       : ((VAR == kVarSoftmax && pre && !p.renorm) ? kEmitExactPre : kEmitSoftSel);
+
+  for (int it = 0; it < TPC; ++it) {
+    const int tl = it * NCL + cl;               // token within the block
+    const int t = blk * kTokensPerBlock + tl;
+    const bool tv = t < p.T;
+    if constexpr (kRaw) {                      // the raw row, dynamically indexable
+      if constexpr (WPL % 4 == 0) {
+#pragma unroll
+        for (int v = 0; v < WPL; v += 4)
+          *reinterpret_cast<u32x4*>(myrow + v) =
+              u32x4{raw.w[v], raw.w[v + 1], raw.w[v + 2], raw.w[v + 3]};
+      } else {
+#pragma unroll
+        for (int v = 0; v < WPL; ++v) myrow[v] = raw.w[v];
+      }
+    }
+    float x[EPL];
+    decode_raw<EPL, BF16>(raw, x);
+    if (it + 1 < TPC) {                         // prefetch the cluster's next token
+      const int tn = t + NCL;
+      load_raw<EPL, BF16>(raw, p.logits, (size_t)tn * E, e0, E, p.vec, tn < p.T);
+    }
+
+    // ---- score basis r (kept in x) and selection key --------------------------
+    float m = 0.0f, inv_s = 0.0f, ssum = 0.0f;
+    if constexpr (VAR == kVarSigmoid) {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) x[i] = sigmoid_f32(x[i]);     // sigmoid(-inf) = 0
+      if (p.scores != nullptr) {
+        float part = 0.0f;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) part += x[i];
+        ssum = cl_sum<LPT>(part);
+      }
+    } else {
+      if (need_ms) {
+        float mx = -kInf;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) mx = fmaxf(mx, x[i]);
+        m = cl_max<LPT>(mx);
+        float s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) s += exp_f32(x[i] - m);     // exp(-inf) = 0
+        inv_s = fast_rcp(cl_sum<LPT>(s));
+      }
+      if constexpr (VAR == kVarSoftmaxBias) {
+        if (pre) {
+#pragma unroll
+          for (int i = 0; i < EPL; ++i) x[i] = exp_f32(x[i] - m) * inv_s;
+        }
+      }
+    }
+    if constexpr (!kRaw) {                     // the score basis, dynamically indexable
+#pragma unroll
+      for (int i = 0; i < EPL; i += 4)
+        *reinterpret_cast<f32x4*>(myrow + i) = f32x4{x[i], x[i + 1], x[i + 2], x[i + 3]};
+    }
+    float key[EPL];
+    // top two keys of the lane, as two interleaved chains merged at the end
+    float m1a = -kInf, m2a = -kInf, m1b = -kInf, m2b = -kInf;
+#pragma unroll
+    for (int i = 0; i < EPL; i += 2) {
+      key[i] = kBias ? x[i] + breg[i] : x[i];   // -inf for padded experts
+      key[i + 1] = kBias ? x[i + 1] + breg[i + 1] : x[i + 1];
+      m2a = __builtin_amdgcn_fmed3f(m1a, m2a, key[i]);
+      m1a = fmaxf(m1a, key[i]);
+      m2b = __builtin_amdgcn_fmed3f(m1b, m2b, key[i + 1]);
+      m1b = fmaxf(m1b, key[i + 1]);
+    }
+    const float m1 = fmaxf(m1a, m1b);
+    const float m2 = fmaxf(fminf(m1a, m1b), fmaxf(m2a, m2b));
+
+    // ---- group-limited selection (a group spans p.lg whole lanes) ----------
+    bool kept = m1 > -kInf;
+    if (p.grouped) {
+      float g1 = m1, g2 = m2;
+      for (int o = 1; o < p.lg; o <<= 1) {
+        const float a1 = __shfl_xor(g1, o, LPT);
+        const float a2 = __shfl_xor(g2, o, LPT);
+        const float n2 = fmaxf(fminf(g1, a1), fmaxf(g2, a2));
+        g1 = fmaxf(g1, a1);
+        g2 = n2;
+      }
+      const float gs = p.topn == 1 ? g1 : g1 + g2;
+      const int myg = lane_c >> p.lg_shift;
+      // group order as packed (score, group) words: slots n_group..LPT-1 hold 0
+      const uint64_t gk = pack_key(gs, myg);
+      if ((lane_c & (p.lg - 1)) == 0 && myg < p.n_group) mygs[myg] = gk;
+      if (lane_c >= p.n_group) mygs[lane_c] = 0ull;
+      wave_lds_sync();
+      int rank = 0;
+#pragma unroll
+      for (int h = 0; h < LPT; h += 2) {        // n_group <= LPT
+        const u64x2 v = *reinterpret_cast<const u64x2*>(mygs + h);
+        rank += (v.x > gk ? 1 : 0) + (h + 1 < LPT && v.y > gk ? 1 : 0);
+      }
+      kept = kept && myg < p.n_group && rank < p.topk_group;
+    }
+
+    // ---- tau: a lower bound on the k-th eligible key ---------------------------
+    const int cnt_l = kept ? (m1 > -kInf ? 1 : 0) + (m2 > -kInf ? 1 : 0) : 0;
+    float tau = cl_min<LPT>(cnt_l == 2 ? m2 : (cnt_l == 1 ? m1 : kInf));
+    if (cl_sum_i<LPT>(cnt_l) < k) tau = kLowest;          // every finite key qualifies
+    // candidate bits: key[i] >= tau.  The sign bit of key[i] - tau marks the
+    // keys below tau (-inf stays -inf; equal keys give +0); alignbit shifts it
+    // in, top element first, so that bit i belongs to element i.
+    uint32_t below_hi = 0, below_lo = 0;
+#pragma unroll
+    for (int i = EPL / 2 - 1; i >= 0; --i) {
+      below_hi = __builtin_amdgcn_alignbit(below_hi, __float_as_uint(key[i + EPL / 2] - tau), 31);
+      below_lo = __builtin_amdgcn_alignbit(below_lo, __float_as_uint(key[i] - tau), 31);
+    }
+    const uint32_t below = (below_hi << (EPL / 2)) | below_lo;
+    const uint32_t lane_bits = EPL == 32 ? 0xffffffffu : ((1u << EPL) - 1u);
+    const uint32_t cmask = kept ? (~below & lane_bits) : 0u;
+    const int pc = __builtin_popcount(cmask);
+    const int coff = cl_excl_scan<LPT>(pc, lane_c);
+    int C = cl_sum_i<LPT>(pc);
+
+    if (C <= p.cap) {
+      // compact the candidates, two set bits per round; the key is formed
+      // again from the raw logit (bit-identical to the register copy)
+      uint32_t mm = cmask;
+      int pos = coff;
+      while (mm) {                              // two set bits per round, reads batched
+        const int i0 = __builtin_ctz(mm);
+        mm &= mm - 1u;
+        const bool h1 = mm != 0u;
+        const int i1 = h1 ? __builtin_ctz(mm) : i0;
+        mm &= h1 ? mm - 1u : mm;
+        float k0 = row_basis<VAR, BF16>(rowc, e0 + i0);
+        float k1 = row_basis<VAR, BF16>(rowc, e0 + i1);
+        if constexpr (kBias) {
+          k0 += bias_s[e0 + i0];
+          k1 += bias_s[e0 + i1];
+        }
+        mycand[pos] = pack_key(k0, e0 + i0);
+        if (h1) mycand[pos + 1] = pack_key(k1, e0 + i1);
+        pos += h1 ? 2 : 1;
+      }
+    } else {
+      // many keys tie at tau: k rounds of a cluster-wide maximum instead
+      uint32_t taken = 0;
+      for (int rr = 0; rr < k; ++rr) {
+        uint64_t best = 0;
+        if (kept) {
+#pragma unroll
+          for (int i = 0; i < EPL; ++i) {
+            const uint64_t c = pack_key(key[i], e0 + i);
+            best = (!((taken >> i) & 1u) && c > best) ? c : best;
+          }
+        }
+        const uint64_t win = cl_max_u64<LPT>(best);
+        const int wi = unpack_idx(win) - e0;
+        if (wi >= 0 && wi < EPL) {
+          taken |= 1u << wi;
+          mycand[rr] = win;
+        }
+      }
+      C = k;
+    }
+    // ranking tier: the smallest of 4..64 that holds every cluster's list in
+    // this wavefront (uniform, so the wavefront takes one path); the entries
+    // between C and the tier are zeroed
+    int tier;
+    if (__ballot(C > 4) == 0ull) tier = 4;
+    else if (__ballot(C > 8) == 0ull) tier = 8;
+    else if (__ballot(C > 16) == 0ull) tier = 16;
+    else if (__ballot(C > 32) == 0ull) tier = 32;
+    else tier = 64;
+    for (int j = C + lane_c; j < tier; j += LPT) mycand[j] = 0ull;
+    wave_lds_sync();
+
+    // ---- order the candidates, emit the top k ---------------------------------
+    if (tier == 4) rank_tier<LPT, 4>(mycand, C, k, lane_c, myselidx);
+    else if (tier == 8) rank_tier<LPT, 8>(mycand, C, k, lane_c, myselidx);
+    else if (tier == 16) rank_tier<LPT, 16>(mycand, C, k, lane_c, myselidx);
+    else if (tier == 32) rank_tier<LPT, 32>(mycand, C, k, lane_c, myselidx);
+    else rank_tier<LPT, 64>(mycand, C, k, lane_c, myselidx);
+    wave_lds_sync();
+    {
+      EmitCtx ec;
+      ec.ids = p.ids;
+      ec.weights = p.weights;
+      ec.weights_bf16 = p.weights_bf16 != 0;
+      ec.renorm = p.renorm != 0;
+      ec.counting = counting;
+      ec.pre = pre;
+      ec.mode = mode;
+      ec.k = k;
+      ec.loc_off = p.loc_off;
+      ec.loc_n = p.loc_n;
+      ec.scale = p.scale;
+      ec.hmask = hmask;
+      ec.t = t;
+      ec.tl = tl;
+      ec.lane_c = lane_c;
+      ec.tv = tv;
+      ec.m = m;
+      ec.inv_s = inv_s;
+      emit_selected<LPT, BF16, VAR>(ec, myselidx, rowc);
+    }
+    if (tv) {
+      // ---- full-E scores for the aux loss --------------------------------------------
+      if (p.scores != nullptr) {
+        float* srow = p.scores + (size_t)t * E;
+        const float inv_ss = VAR == kVarSigmoid ? fast_rcp(ssum) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+          if (e0 + i < E) {
+            float v;
+            if constexpr (VAR == kVarSigmoid) v = x[i] * inv_ss;
+            else if (VAR == kVarSoftmaxBias && pre) v = x[i];
+            else v = exp_f32(x[i] - m) * inv_s;
+            srow[e0 + i] = v;
+          }
+        }
+      }
+    }
+    wave_lds_sync();
+  }
+
+  if (counting) {
+    __syncthreads();
+    int32_t* srow = p.super_rows + (size_t)(blk / p.group_blocks) * p.loc_n;
+    for (int e = tid; e < p.loc_n; e += BLOCK) {
+      const int c = __popcll(hmask[e]);
+      if (p.hist != nullptr) p.hist[(size_t)blk * p.loc_n + e] = c;
+      if (c != 0) atomicAdd(srow + e, c);
+    }
+  }
+}
+
+template <int LPT, int EPL, bool BF16, int VAR>
+hipError_t launch_route_inst(const RouteParams& p, int nb, hipStream_t s) {
+  constexpr int BLOCK = kRouteBlock<LPT>;
+  const size_t lds = route_lds_bytes(LPT, kRawRow<VAR, BF16> ? RawRow<EPL, BF16>::kWords : EPL,
+                                     EPL, p.hmask_len, p.cap, p.k, p.grouped ? p.n_group : 0);
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&route_kernel<LPT, EPL, BF16, VAR>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  MOE_LAUNCH((route_kernel<LPT, EPL, BF16, VAR>), dim3(nb), dim3(BLOCK), lds, s, p);
+  return hipGetLastError();
+}
+
+using RouteLaunchFn = hipError_t (*)(const RouteParams&, int, hipStream_t);
+
+#define MOE_LPT_LIST(EPL, BF, VAR)                                                        \
+  {launch_route_inst<1, EPL, BF, VAR>, launch_route_inst<2, EPL, BF, VAR>,                \
+   launch_route_inst<4, EPL, BF, VAR>, launch_route_inst<8, EPL, BF, VAR>,                \
+   launch_route_inst<16, EPL, BF, VAR>, launch_route_inst<32, EPL, BF, VAR>,              \
+   launch_route_inst<64, EPL, BF, VAR>}
+
+// Launch of one variant: table over (logits dtype, experts per lane 4..32,
+// lanes per token 1..64).
+template <int VAR>
+hipError_t launch_route_variant(const RouteParams& p, int li, int ei, bool bf16, int nb,
+                                hipStream_t s) {
+  static const RouteLaunchFn table[2][4][7] = {
+      {MOE_LPT_LIST(4, false, VAR), MOE_LPT_LIST(8, false, VAR), MOE_LPT_LIST(16, false, VAR),
+       MOE_LPT_LIST(32, false, VAR)},
+      {MOE_LPT_LIST(4, true, VAR), MOE_LPT_LIST(8, true, VAR), MOE_LPT_LIST(16, true, VAR),
+       MOE_LPT_LIST(32, true, VAR)},
+  };
+  return table[bf16 ? 1 : 0][ei][li](p, nb, s);
+}
+
+#undef MOE_LPT_LIST
+
+}  // namespace moe

@@ -1,0 +1,7 @@
+// Route kernel instances of one score variant (kVarSoftmaxBias); see route_kernel.hpp.
+#include "route_kernel.hpp"
+
+namespace moe {
+template hipError_t launch_route_variant<kVarSoftmaxBias>(const RouteParams&, int, int, bool, int,
+                                                hipStream_t);
+}  // namespace moe
