@@ -321,6 +321,9 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>) route_kernel(RouteParams p) 
   static_assert(TPC * NCL == kTokensPerBlock, "block shape");
   static_assert(EPL <= 32, "lane masks are 32-bit");
   constexpr bool kBias = VAR != kVarSoftmax;   // the softmax variant has no bias
+  // tau from per-lane top four (ungrouped, 2..8 lanes per token): close to the
+  // k-th key, so that few candidates remain to rank
+  constexpr bool kRefineTau = LPT >= 2 && LPT <= 8;
   constexpr float kLowest = -3.402823466e38f;
 
   const int tid = threadIdx.x;
@@ -379,6 +382,7 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>) route_kernel(RouteParams p) 
     }
   }
 
+  const bool refine = !p.grouped && k <= 4 * LPT && k > 2;
   const bool need_ms =
       VAR == kVarSigmoid ? false
                          : ((VAR == kVarSoftmax ? (pre && !p.renorm) : pre) || p.scores != nullptr);
@@ -443,19 +447,34 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>) route_kernel(RouteParams p) 
         *reinterpret_cast<f32x4*>(myrow + i) = f32x4{x[i], x[i + 1], x[i + 2], x[i + 3]};
     }
     float key[EPL];
-    // top two keys of the lane, as two interleaved chains merged at the end
-    float m1a = -kInf, m2a = -kInf, m1b = -kInf, m2b = -kInf;
 #pragma unroll
-    for (int i = 0; i < EPL; i += 2) {
-      key[i] = kBias ? x[i] + breg[i] : x[i];   // -inf for padded experts
-      key[i + 1] = kBias ? x[i + 1] + breg[i + 1] : x[i + 1];
-      m2a = __builtin_amdgcn_fmed3f(m1a, m2a, key[i]);
-      m1a = fmaxf(m1a, key[i]);
-      m2b = __builtin_amdgcn_fmed3f(m1b, m2b, key[i + 1]);
-      m1b = fmaxf(m1b, key[i + 1]);
+    for (int i = 0; i < EPL; ++i) key[i] = kBias ? x[i] + breg[i] : x[i];   // -inf if padded
+    // top keys of the lane: four (sorted insertion with med3) when tau is
+    // refined below, else two, as two interleaved chains merged at the end
+    float m1, m2, m3 = -kInf, m4 = -kInf;
+    if (kRefineTau && refine) {
+      float a = -kInf, b = -kInf, c = -kInf, d = -kInf;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const float v = key[i];
+        d = __builtin_amdgcn_fmed3f(c, d, v);
+        c = __builtin_amdgcn_fmed3f(b, c, v);
+        b = __builtin_amdgcn_fmed3f(a, b, v);
+        a = fmaxf(a, v);
+      }
+      m1 = a; m2 = b; m3 = c; m4 = d;
+    } else {
+      float m1a = -kInf, m2a = -kInf, m1b = -kInf, m2b = -kInf;
+#pragma unroll
+      for (int i = 0; i < EPL; i += 2) {
+        m2a = __builtin_amdgcn_fmed3f(m1a, m2a, key[i]);
+        m1a = fmaxf(m1a, key[i]);
+        m2b = __builtin_amdgcn_fmed3f(m1b, m2b, key[i + 1]);
+        m1b = fmaxf(m1b, key[i + 1]);
+      }
+      m1 = fmaxf(m1a, m1b);
+      m2 = fmaxf(fminf(m1a, m1b), fmaxf(m2a, m2b));
     }
-    const float m1 = fmaxf(m1a, m1b);
-    const float m2 = fmaxf(fminf(m1a, m1b), fmaxf(m2a, m2b));
 
     // ---- group-limited selection (a group spans p.lg whole lanes) ----------
     bool kept = m1 > -kInf;
@@ -485,9 +504,35 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>) route_kernel(RouteParams p) 
     }
 
     // ---- tau: a lower bound on the k-th eligible key ---------------------------
-    const int cnt_l = kept ? (m1 > -kInf ? 1 : 0) + (m2 > -kInf ? 1 : 0) : 0;
-    float tau = cl_min<LPT>(cnt_l == 2 ? m2 : (cnt_l == 1 ? m1 : kInf));
-    if (cl_sum_i<LPT>(cnt_l) < k) tau = kLowest;          // every finite key qualifies
+    float tau;
+    if (kRefineTau && refine) {
+      // the k-th largest of the cluster's per-lane top four (a subset of the
+      // keys, so at most the k-th largest key): each lane counts the values
+      // >= each of its own; the largest own value with count >= k is a bound
+      float* tv = reinterpret_cast<float*>(mycand);        // cluster scratch, LPT x 4
+      *reinterpret_cast<f32x4*>(tv + 4 * lane_c) = f32x4{m1, m2, m3, m4};
+      wave_lds_sync();
+      const float mine[4] = {m1, m2, m3, m4};
+      int cnt[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < LPT; ++j) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(tv + 4 * j);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          cnt[q] += (v.x >= mine[q] ? 1 : 0) + (v.y >= mine[q] ? 1 : 0) +
+                    (v.z >= mine[q] ? 1 : 0) + (v.w >= mine[q] ? 1 : 0);
+      }
+      float tl = -kInf;
+#pragma unroll
+      for (int q = 3; q >= 0; --q) tl = (mine[q] > -kInf && cnt[q] >= k) ? mine[q] : tl;
+      tau = cl_max<LPT>(tl);
+      if (!(tau > -kInf)) tau = kLowest;                  // fewer than k finite keys
+      wave_lds_sync();                                     // scratch is reused below
+    } else {
+      const int cnt_l = kept ? (m1 > -kInf ? 1 : 0) + (m2 > -kInf ? 1 : 0) : 0;
+      tau = cl_min<LPT>(cnt_l == 2 ? m2 : (cnt_l == 1 ? m1 : kInf));
+      if (cl_sum_i<LPT>(cnt_l) < k) tau = kLowest;        // every finite key qualifies
+    }
     // candidate bits: key[i] >= tau.  The sign bit of key[i] - tau marks the
     // keys below tau (-inf stays -inf; equal keys give +0); alignbit shifts it
     // in, top element first, so that bit i belongs to element i.
