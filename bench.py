@@ -45,8 +45,10 @@ def parse():
     ap.add_argument("--workload", default="deepseek_v3_like")
     ap.add_argument("--rotate-mb", type=int, default=2 * 256 + 64,
                     help="bytes spanned by the rotating buffer sets (MiB)")
-    ap.add_argument("--warm", action="store_true",
-                    help="also time a single buffer set (cache-warm), reported separately")
+    ap.add_argument("--no-warm", action="store_true",
+                    help="skip the single-buffer-set (cache-warm) number")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the other workloads (reported under other_configs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--json-out", default=None)
@@ -82,6 +84,132 @@ def load_traffic(workload: str):
         return None
     v = fields.get("traffic_bytes_per_launch")
     return int(v) if v is not None else None
+
+
+def graph_ms(torch, step, K, warmup=3):
+    """Average milliseconds of step(i), i = 0..K-1, captured into one HIP graph."""
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=cap):
+        for i in range(K):
+            step(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / K
+
+
+def n_sets(set_bytes, rotate_mb):
+    return max(2, min(256, math.ceil(max(rotate_mb * 2 ** 20, 2 * MALL_BYTES + 1) / set_bytes)))
+
+
+def route_permute_bytes(w, T, total, ntiles):
+    lsz = 2 if w.logits_dtype == "bf16" else 4
+    return (T * w.E * lsz + (w.E * 4 if w.has_bias else 0) + 3 * T * w.k * 4 + total * 4 +
+            2 * ntiles * 4 + w.E * 4 + (w.E + 1) * 4 + 8)
+
+
+def other_configs(mr, torch, np, dev, rotate_mb, K):
+    """The other workloads, each cold (rotating sets past 2x the MALL): ms per
+    call and algorithmic GB/s."""
+    from workloads import WORKLOADS, FRONT_END, front_end_inputs, route_inputs
+    res = {}
+
+    def dev_logits(w, arr):
+        if w.logits_dtype == "bf16":
+            return torch.from_numpy(arr.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(arr).to(dev)
+
+    for name in ("tiny_softmax_post", "mixtral_like", "qwen_moe_like"):
+        w = WORKLOADS[name]
+        logits, bias = route_inputs(w)
+        x0 = dev_logits(w, logits)
+        b0 = None if bias is None else torch.from_numpy(bias).to(dev)
+        args = mr.make_route_args(w.T, w.E, w.k, score_fn=w.score_fn, pre_softmax=w.pre_softmax,
+                                  n_group=w.n_group, topk_group=w.topk_group,
+                                  group_topn=w.group_topn, renorm=w.renorm, scale=w.scale,
+                                  logits_dtype=w.logits_dtype, bias_dtype=w.bias_dtype)
+        with_scores = w.aux_coeff is not None
+        o0 = mr.alloc_route_outputs(args, dev, permute=True, tile=w.tile, scores=with_scores)
+        sb = x0.numel() * x0.element_size() + sum(
+            t.numel() * t.element_size() for t in vars(o0).values() if isinstance(t, torch.Tensor))
+        R = n_sets(sb, rotate_mb)
+        sets = [(x0 if r == 0 else x0.clone(),
+                 o0 if r == 0 else mr.alloc_route_outputs(args, dev, permute=True, tile=w.tile,
+                                                          scores=with_scores))
+                for r in range(R)]
+
+        def step(i, scores=False):
+            x, o = sets[i % R]
+            sc = o.scores
+            o.scores = o.scores if scores else None
+            mr.route_permute(args, x, b0, tile=w.tile, out=o)
+            o.scores = sc
+
+        ms = graph_ms(torch, step, K)
+        total = int(o0.total_num_padded_tokens.item())
+        ntiles = int(o0.num_non_exiting_ctas.item())
+        nbytes = route_permute_bytes(w, w.T, total, ntiles)
+        entry = {"workload": w.description, "us_per_call": ms * 1e3, "tokens_per_s": w.T / (ms * 1e-3),
+                 "algorithmic_bytes": nbytes, "gbs": nbytes / (ms * 1e-3) / 1e9, "buffer_sets": R}
+        if with_scores:
+            ms_s = graph_ms(torch, lambda i: step(i, True), K)
+            sbytes = nbytes + w.T * w.E * 4
+            entry["with_scores"] = {"us_per_call": ms_s * 1e3, "algorithmic_bytes": sbytes,
+                                    "gbs": sbytes / (ms_s * 1e-3) / 1e9}
+            # aux loss forward (reads probs) and backward (writes the gradient)
+            probs = [o.scores for _, o in sets]
+            counts = o0.expert_counts
+            loss = torch.empty(1, dtype=torch.float32, device=dev)
+            wsa = torch.empty(max(mr.moe_aux_loss_workspace_size(w.T, w.E), 1), dtype=torch.uint8,
+                              device=dev)
+            grads = [torch.empty((w.T, w.E), dtype=torch.float32, device=dev) for _ in range(R)]
+            fwd = graph_ms(torch, lambda i: mr.moe_aux_loss(probs[i % R], counts, w.T, w.T, w.E, w.k,
+                                                            w.aux_coeff, loss=loss, workspace=wsa), K)
+            bwd = graph_ms(torch, lambda i: mr.moe_aux_loss(None, counts, w.T, w.T, w.E, w.k,
+                                                            w.aux_coeff, grad_probs=grads[i % R]), K)
+            ab = w.T * w.E * 4 + w.E * 4
+            entry["aux_forward"] = {"us_per_call": fwd * 1e3, "gbs": ab / (fwd * 1e-3) / 1e9}
+            entry["aux_backward"] = {"us_per_call": bwd * 1e3, "gbs": ab / (bwd * 1e-3) / 1e9}
+            del grads, probs
+        res[name] = entry
+        del sets, o0
+
+    f = FRONT_END
+    hidden, gamma, W, _ = front_end_inputs(f)
+    def bf(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    h0, g0, w0 = bf(hidden), bf(gamma), bf(W)
+    set_b = (2 * f.T * f.H + f.H * f.E) * 2 + f.T * f.k * 4 + f.T * f.E * 2
+    R = n_sets(set_b, rotate_mb)
+    fsets = []
+    for r in range(R):
+        fsets.append((h0.clone(), w0.clone(), torch.empty((f.T, f.H), dtype=torch.bfloat16, device=dev),
+                      torch.empty((f.T, f.k), dtype=torch.int32, device=dev),
+                      torch.empty((f.T, f.E), dtype=torch.bfloat16, device=dev)))
+    wsf = torch.empty(max(mr.rmsnorm_gate_route_workspace_size(f.T, f.H, f.E), 1), dtype=torch.uint8,
+                      device=dev)
+
+    def fstep(i):
+        h, wt, nm, ids, aff = fsets[i % R]
+        mr.rmsnorm_gate_route(h, g0, wt, None, mr.MOE_BF16, f.T, f.H, f.E, f.eps, f.k,
+                              mr.MOE_SIGMOID, nm, ids, aff, workspace=wsf)
+
+    ms = graph_ms(torch, fstep, K)
+    fb = 2 * f.T * f.H * 2 + f.H * 2 + f.H * f.E * 2 + f.T * f.k * 4 + f.T * f.E * 2
+    flops = 2 * f.T * f.H * f.E
+    res["decode_front_end"] = {"workload": f.description, "us_per_call": ms * 1e3,
+                               "tokens_per_s": f.T / (ms * 1e-3), "algorithmic_bytes": fb,
+                               "gbs": fb / (ms * 1e-3) / 1e9, "mfma_tflops": flops / (ms * 1e-3) / 1e12,
+                               "buffer_sets": R}
+    return res
 
 
 def cpu_baseline(w, sample_T: int, seconds: float):
@@ -201,7 +329,7 @@ def main():
     traffic = load_traffic(a.workload)
 
     warm = None
-    if a.warm:
+    if not a.no_warm:
         gw = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gw, stream=cap):
             for i in range(K):
@@ -215,6 +343,10 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         warm = e0.elapsed_time(e1) / K
+
+    others = None
+    if not a.no_other_configs and a.workload == "deepseek_v3_like":
+        others = other_configs(mr, torch, np, dev, a.rotate_mb, min(K, 50))
 
     cpu = None
     if not a.no_cpu_baseline:
@@ -264,6 +396,8 @@ def main():
     }
     if warm is not None:
         line["warm_single_set_ms_per_step"] = warm
+    if others is not None:
+        line["other_configs"] = others
     if a.copy_calibration_mb:
         n = a.copy_calibration_mb * 2 ** 20 // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
