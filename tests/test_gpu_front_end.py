@@ -24,10 +24,13 @@ DEV = "cuda:0"
 
 
 def _kchunk(H):
-    if H % 512 == 0 and H // 512 >= 8:
-        return 512
-    if H % 256 == 0 and H // 256 >= 8:
-        return 256
+    # the library's k-chunk (fixes the fp32 summation depth of the projection)
+    for kc in range(512, 127, -32):
+        if H % kc == 0 and (H // kc) % 8 == 0:
+            return kc
+    for kc in range(512, 127, -32):
+        if H % kc == 0 and H // kc >= 8:
+            return kc
     return 128
 
 

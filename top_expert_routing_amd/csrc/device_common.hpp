@@ -138,6 +138,29 @@ __device__ __forceinline__ uint64_t cl_max_u64(uint64_t v) {
   return cl_reduce<W>(v, [](uint64_t a, uint64_t b) { return a > b ? a : b; });
 }
 
+// Wavefront-wide maximum of an unsigned 64-bit value, uniform in every lane:
+// DPP inside each 16-lane row, then row_bcast:15 (rows 1 and 3 take the last
+// lane of the row before) and row_bcast:31 (rows 2 and 3 take lane 31); lane
+// 63 ends with the maximum, which is read into scalar registers.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_u64_keep(uint64_t x) {   // disabled rows keep x
+  const int lo = __builtin_amdgcn_update_dpp((int)(uint32_t)x, (int)(uint32_t)x, CTRL, ROW_MASK,
+                                             0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp((int)(uint32_t)(x >> 32), (int)(uint32_t)(x >> 32),
+                                             CTRL, ROW_MASK, 0xF, false);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = cl_max_u64<16>(v);
+  uint64_t t = dpp_u64_keep<0x142, 0xA>(v);    // row_bcast:15 into rows 1 and 3
+  v = t > v ? t : v;
+  t = dpp_u64_keep<0x143, 0xC>(v);             // row_bcast:31 into rows 2 and 3
+  v = t > v ? t : v;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // Value of lane (lane ^ D) for D in {1, 2, 4, 8} (inside a 16-lane row).  For
 // D = 4 and 8 both row shifts are executed by every lane, then selected.
 template <int D>

@@ -43,6 +43,7 @@ __device__ __forceinline__ uint16_t f2h(float v) {
 }
 
 constexpr int kNormThreads = 256;
+constexpr int kNormVecs = 8;        // H <= 16384: 16384 / 8 / 256 vectors per thread
 
 }  // namespace
 
@@ -53,11 +54,20 @@ __global__ void __launch_bounds__(kNormThreads)
   __shared__ float red[kNormThreads / 64];
   const int t = blockIdx.x;
   const uint16_t* x = hidden + (size_t)t * H;
+  const int nv = H / 8;                                   // 16-byte vectors (H % 128 == 0)
+  // every vector of the row and of gamma is requested before any is used
+  u32x4 xv[kNormVecs], gv[kNormVecs];
+#pragma unroll
+  for (int j = 0; j < kNormVecs; ++j) {
+    const int v = threadIdx.x + j * kNormThreads;
+    xv[j] = v < nv ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x) + v)
+                   : u32x4{0, 0, 0, 0};
+    gv[j] = v < nv ? reinterpret_cast<const u32x4*>(gamma)[v] : u32x4{0, 0, 0, 0};
+  }
   float ss = 0.0f;
-  // H % 128 == 0: 16-byte vectors of 8 elements
-  for (int v = threadIdx.x; v < H / 8; v += kNormThreads) {
-    const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x) + v);
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int j = 0; j < kNormVecs; ++j) {
+    const uint32_t w[4] = {xv[j].x, xv[j].y, xv[j].z, xv[j].w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float a = h2f<F16>((uint16_t)(w[i] & 0xffffu));
@@ -73,16 +83,17 @@ __global__ void __launch_bounds__(kNormThreads)
   for (int i = 0; i < kNormThreads / 64; ++i) tot += red[i];
   const float r = 1.0f / sqrtf(tot / (float)H + eps);
   uint16_t* y = normed + (size_t)t * H;
-  for (int v = threadIdx.x; v < H / 8; v += kNormThreads) {
-    const u32x4 q = reinterpret_cast<const u32x4*>(x)[v];
-    const u32x4 g = reinterpret_cast<const u32x4*>(gamma)[v];
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-    const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+  for (int j = 0; j < kNormVecs; ++j) {
+    const int v = threadIdx.x + j * kNormThreads;
+    if (v >= nv) break;
+    const uint32_t w[4] = {xv[j].x, xv[j].y, xv[j].z, xv[j].w};
+    const uint32_t g[4] = {gv[j].x, gv[j].y, gv[j].z, gv[j].w};
     uint32_t o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float a = h2f<F16>((uint16_t)(w[i] & 0xffffu)) * r * h2f<F16>((uint16_t)(gw[i] & 0xffffu));
-      const float b = h2f<F16>((uint16_t)(w[i] >> 16)) * r * h2f<F16>((uint16_t)(gw[i] >> 16));
+      const float a = h2f<F16>((uint16_t)(w[i] & 0xffffu)) * r * h2f<F16>((uint16_t)(g[i] & 0xffffu));
+      const float b = h2f<F16>((uint16_t)(w[i] >> 16)) * r * h2f<F16>((uint16_t)(g[i] >> 16));
       o[i] = (uint32_t)f2h<F16>(a) | ((uint32_t)f2h<F16>(b) << 16);
     }
     reinterpret_cast<u32x4*>(y)[v] = u32x4{o[0], o[1], o[2], o[3]};
@@ -91,16 +102,47 @@ __global__ void __launch_bounds__(kNormThreads)
 
 constexpr int kGemmThreads = 256;   // 4 waves x 32 token rows
 constexpr int kGemmN = 16;          // experts per block
+constexpr int kXcds = 8;            // accelerator complex dies of the MI355X
+constexpr int kGemmPrefetch = 16;   // 32-wide k steps of a chunk held in registers (kc <= 512)
 
 template <bool F16>
 __global__ void __launch_bounds__(kGemmThreads)
     gemm_kernel(const uint16_t* __restrict__ normed, const uint16_t* __restrict__ W, int T, int H,
                 int E, int kc, float* __restrict__ partial) {
   extern __shared__ __align__(16) uint16_t wt[];         // [16][kc] transposed tile
-  const int nt = blockIdx.x;                              // n-tile
-  const int ch = blockIdx.y;                              // k-chunk
+  // Blocks are dispatched to the 8 XCDs round-robin (block b on XCD b % 8).
+  // When the chunk count is a multiple of 8, every n-tile of chunk c runs on
+  // XCD c % 8, so that the chunk's A rows and the W lines its n-tiles share
+  // come into one L2 once.
+  const int ntiles = E / kGemmN;
+  const int nchunks = H / kc;
+  const int b = blockIdx.x;
+  int nt, ch;
+  if (nchunks % kXcds == 0) {
+    const int x = b % kXcds, i = b / kXcds;               // i-th block of XCD x
+    ch = x + kXcds * (i / ntiles);
+    nt = i % ntiles;
+  } else {
+    ch = b / ntiles;
+    nt = b % ntiles;
+  }
   const int n0 = nt * kGemmN, k0 = ch * kc;
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;          // k-group of 8
+  f32x4v acc[2] = {f32x4v{0, 0, 0, 0}, f32x4v{0, 0, 0, 0}};
+  const int rows[2] = {wv * 32 + col, wv * 32 + 16 + col};
+  // the A operand of the whole k-chunk (kc <= 32 * kGemmPrefetch) is
+  // requested first, then the W tile; both latencies overlap
+  u32x4 av[kGemmPrefetch][2];
+#pragma unroll
+  for (int u = 0; u < kGemmPrefetch; ++u)
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      av[u][s] = (rows[s] < T && 32 * u < kc)
+                     ? *reinterpret_cast<const u32x4*>(normed + (size_t)rows[s] * H + k0 + 32 * u +
+                                                       grp * 8)
+                     : u32x4{0, 0, 0, 0};
   // stage W[k0 : k0+kc, n0 : n0+16] transposed: 16-byte loads of 8 experts
   for (int v = tid; v < kc * 2; v += kGemmThreads) {
     const int kk = v >> 1, half = v & 1;
@@ -113,17 +155,14 @@ __global__ void __launch_bounds__(kGemmThreads)
     }
   }
   __syncthreads();
-  const int lane = tid & 63, wv = tid >> 6;
-  const int col = lane & 15, grp = lane >> 4;          // k-group of 8
-  f32x4v acc[2] = {f32x4v{0, 0, 0, 0}, f32x4v{0, 0, 0, 0}};
-  const int rows[2] = {wv * 32 + col, wv * 32 + 16 + col};
-  for (int kk = 0; kk < kc; kk += 32) {
+#pragma unroll
+  for (int u = 0; u < kGemmPrefetch; ++u) {
+    const int kk = 32 * u;
+    if (kk >= kc) break;
     const u32x4 b = *reinterpret_cast<const u32x4*>(wt + col * kc + kk + grp * 8);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      u32x4 a = u32x4{0, 0, 0, 0};
-      if (rows[s] < T)
-        a = *reinterpret_cast<const u32x4*>(normed + (size_t)rows[s] * H + k0 + kk + grp * 8);
+      const u32x4 a = av[u][s];
       if constexpr (F16)
         acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                        __builtin_bit_cast(f16x8, b), acc[s], 0, 0, 0);
@@ -144,9 +183,10 @@ __global__ void __launch_bounds__(kGemmThreads)
 }
 
 constexpr int kSelectThreads = 256;  // one wavefront per token
-constexpr int kSelectMaxPerLane = 8; // E <= 512
 
-template <bool F16>
+// One wavefront per token; J = ceil(E / 64) experts per lane (expert
+// lane + 64 j).
+template <bool F16, int J>
 __global__ void __launch_bounds__(kSelectThreads)
     select_kernel(const float* __restrict__ partial, int nchunks, const uint16_t* __restrict__ rbias,
                   int T, int E, int k, int act_sigmoid, int32_t* __restrict__ ids,
@@ -154,49 +194,71 @@ __global__ void __launch_bounds__(kSelectThreads)
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (kSelectThreads / 64) + (threadIdx.x >> 6);
   if (t >= T) return;                                  // whole wavefront leaves together
-  float z[kSelectMaxPerLane];
+  // chunk partials, summed in chunk order: a per-chunk base and fixed
+  // per-slot offsets, every load of the token requested before the sums
+  const float* pt = partial + (size_t)t * E + lane;
+  const size_t cstride = (size_t)T * E;
+  float z[J];
 #pragma unroll
-  for (int j = 0; j < kSelectMaxPerLane; ++j) {
-    const int e = lane + 64 * j;
-    float s = -__builtin_huge_valf();
-    if (e < E) {
-      s = 0.0f;
-      for (int c = 0; c < nchunks; ++c) s += partial[((size_t)c * T + t) * E + e];
-      if (rbias != nullptr) s += h2f<F16>(rbias[e]);
+  for (int j = 0; j < J; ++j) z[j] = 0.0f;
+  constexpr int CU = 16;                               // chunks in flight
+  for (int c0 = 0; c0 < nchunks; c0 += CU) {
+    float pv[CU][J];
+#pragma unroll
+    for (int u = 0; u < CU; ++u) {
+      const float* pc = pt + (size_t)(c0 + u) * cstride;
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+        pv[u][j] = (c0 + u < nchunks && lane + 64 * j < E) ? pc[64 * j] : 0.0f;
     }
-    z[j] = s;
+#pragma unroll
+    for (int u = 0; u < CU; ++u)
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+        if (c0 + u < nchunks) z[j] += pv[u][j];
   }
-  // top-k on the raw logits: k rounds of a wavefront-wide maximum of
-  // (key, lower index first) packed into 64 bits
+  uint64_t pk[J];                                      // (key, lower index first); 0 = taken
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int e = lane + 64 * j;
+    if (e < E) {
+      if (rbias != nullptr) z[j] += h2f<F16>(rbias[e]);
+      pk[j] = pack_key(z[j] + 0.0f, e);
+    } else {
+      z[j] = -__builtin_huge_valf();
+      pk[j] = 0ull;
+    }
+  }
+  // top-k on the raw logits: k rounds of a wavefront-wide maximum
   uint32_t taken = 0;
   float zmax = 0.0f;
   for (int r = 0; r < k; ++r) {
-    uint64_t best = 0;
+    uint64_t m[J];
 #pragma unroll
-    for (int j = 0; j < kSelectMaxPerLane; ++j) {
-      const int e = lane + 64 * j;
-      const uint64_t c = pack_key(z[j] + 0.0f, e);
-      best = (e < E && !((taken >> j) & 1u) && c > best) ? c : best;
-    }
+    for (int j = 0; j < J; ++j) m[j] = pk[j];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const uint64_t w = __shfl_xor(best, o, 64);
-      best = w > best ? w : best;
-    }
+    for (int w = 1; w < J; w <<= 1)                    // tree over the lane's slots
+#pragma unroll
+      for (int j = 0; j + w < J; j += 2 * w) m[j] = m[j + w] > m[j] ? m[j + w] : m[j];
+    const uint64_t best = wave_max_u64(m[0]);
     const int e = unpack_idx(best);
     if (lane == 0) ids[(size_t)t * k + r] = e;
-    if ((e & 63) == lane) taken |= 1u << (e >> 6);
+    if ((e & 63) == lane) {
+      taken |= 1u << (e >> 6);
+#pragma unroll
+      for (int j = 0; j < J; ++j) pk[j] = j == (e >> 6) ? 0ull : pk[j];
+    }
     if (r == 0) zmax = unord_key((uint32_t)(best >> 32));   // the largest logit
   }
-  float my_aff_num[kSelectMaxPerLane];
+  float num[J];
   // activation on the chosen experts only
   float part = 0.0f;
 #pragma unroll
-  for (int j = 0; j < kSelectMaxPerLane; ++j) {
-    my_aff_num[j] = 0.0f;
+  for (int j = 0; j < J; ++j) {
+    num[j] = 0.0f;
     if ((taken >> j) & 1u) {
-      my_aff_num[j] = act_sigmoid ? sigmoid_f32(z[j]) : exp_f32(z[j] - zmax);
-      part += my_aff_num[j];
+      num[j] = act_sigmoid ? sigmoid_f32(z[j]) : exp_f32(z[j] - zmax);
+      part += num[j];
     }
   }
   float denom = 1.0f;
@@ -206,19 +268,23 @@ __global__ void __launch_bounds__(kSelectThreads)
   }
   const float inv = 1.0f / denom;
 #pragma unroll
-  for (int j = 0; j < kSelectMaxPerLane; ++j) {
+  for (int j = 0; j < J; ++j) {
     const int e = lane + 64 * j;
     if (e < E) {
-      const float v = ((taken >> j) & 1u) ? my_aff_num[j] * inv : 0.0f;
+      const float v = ((taken >> j) & 1u) ? num[j] * inv : 0.0f;
       aff[(size_t)t * E + e] = (uint16_t)f32_to_bf16_rne(v);
     }
   }
 }
 
 int front_end_kchunk(int H) {
-  // 512, 256 or 128 elements per k-chunk, keeping at least ~14 chunks of work
-  if (H % 512 == 0 && H / 512 >= 8) return 512;
-  if (H % 256 == 0 && H / 256 >= 8) return 256;
+  // The largest multiple of 32 (one MFMA k step), at most 512, that divides H
+  // into a multiple of 8 chunks (one group of n-tiles per XCD); else the
+  // largest that divides H into at least 8 chunks; else 128 (H % 128 == 0).
+  for (int kc = 512; kc >= 128; kc -= 32)
+    if (H % kc == 0 && (H / kc) % kXcds == 0) return kc;
+  for (int kc = 512; kc >= 128; kc -= 32)
+    if (H % kc == 0 && H / kc >= 8) return kc;
   return 128;
 }
 
@@ -237,7 +303,7 @@ hipError_t launch_front_end(const FrontEndParams& q, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t lds = (size_t)kGemmN * kc * sizeof(uint16_t);
-  dim3 grid(q.E / kGemmN, nchunks);
+  dim3 grid((q.E / kGemmN) * nchunks);
   if (q.f16)
     hipLaunchKernelGGL(gemm_kernel<true>, grid, dim3(kGemmThreads), lds, s,
                        (const uint16_t*)q.normed, (const uint16_t*)q.W, q.T, q.H, q.E, kc,
@@ -249,14 +315,23 @@ hipError_t launch_front_end(const FrontEndParams& q, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nb = (q.T + kSelectThreads / 64 - 1) / (kSelectThreads / 64);
-  if (q.f16)
-    hipLaunchKernelGGL(select_kernel<true>, dim3(nb), dim3(kSelectThreads), 0, s, q.partial,
-                       nchunks, (const uint16_t*)q.rbias, q.T, q.E, q.k, q.act_sigmoid, q.ids,
-                       (uint16_t*)q.aff);
-  else
-    hipLaunchKernelGGL(select_kernel<false>, dim3(nb), dim3(kSelectThreads), 0, s, q.partial,
-                       nchunks, (const uint16_t*)q.rbias, q.T, q.E, q.k, q.act_sigmoid, q.ids,
-                       (uint16_t*)q.aff);
+  const int J = (q.E + 63) / 64;                     // E <= 512
+#define MOE_SELECT(F, JJ)                                                                       \
+  hipLaunchKernelGGL((select_kernel<F, JJ>), dim3(nb), dim3(kSelectThreads), 0, s, q.partial,  \
+                     nchunks, (const uint16_t*)q.rbias, q.T, q.E, q.k, q.act_sigmoid, q.ids,    \
+                     (uint16_t*)q.aff)
+  if (q.f16) {
+    if (J <= 1) MOE_SELECT(true, 1);
+    else if (J <= 2) MOE_SELECT(true, 2);
+    else if (J <= 4) MOE_SELECT(true, 4);
+    else MOE_SELECT(true, 8);
+  } else {
+    if (J <= 1) MOE_SELECT(false, 1);
+    else if (J <= 2) MOE_SELECT(false, 2);
+    else if (J <= 4) MOE_SELECT(false, 4);
+    else MOE_SELECT(false, 8);
+  }
+#undef MOE_SELECT
   return hipGetLastError();
 }
 
