@@ -25,10 +25,10 @@ DEV = "cuda:0"
 
 def _kchunk(H):
     # the library's k-chunk (fixes the fp32 summation depth of the projection)
-    for kc in range(512, 127, -32):
+    for kc in range(480, 127, -32):
         if H % kc == 0 and (H // kc) % 8 == 0:
             return kc
-    for kc in range(512, 127, -32):
+    for kc in range(480, 127, -32):
         if H % kc == 0 and H // kc >= 8:
             return kc
     return 128

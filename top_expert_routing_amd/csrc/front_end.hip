@@ -4,13 +4,13 @@
 //   norm_kernel    one block per token: r_t = (mean_h x^2 + eps)^-1/2 in
 //                  float32, normed = round(x * r_t * gamma) stored in the
 //                  input dtype (RNE).
-//   gemm_kernel    split-K router projection on MFMA: block (n-tile of 16
-//                  experts, k-chunk) computes all T <= 128 tokens x 16 experts
-//                  over its k-chunk with v_mfma_f32_16x16x32_{bf16,f16} and
-//                  writes float32 partials [chunks, T, E].  A (normed) comes
-//                  from global memory (shared by every n-tile through L2); the
-//                  W tile is staged transposed in LDS.  The MFMA consumes
-//                  exactly the stored normed values.
+//   gemm_kernel    split-K router projection on MFMA: block (k-chunk, 64
+//                  experts) computes all T <= 128 tokens x 64 experts over
+//                  its k-chunk with v_mfma_f32_16x16x32_{bf16,f16} and writes
+//                  float32 partials [chunks, T, E].  A (normed) comes from
+//                  global memory into registers; the W tile is staged
+//                  transposed in LDS.  The MFMA consumes exactly the stored
+//                  normed values.
 //   select_kernel  one wavefront per token: z = sum of the partials in chunk
 //                  order (+ router bias) -- deterministic; top-k on the raw
 //                  logits (lower index on ties); activation on the chosen
@@ -100,86 +100,132 @@ __global__ void __launch_bounds__(kNormThreads)
   }
 }
 
-constexpr int kGemmThreads = 256;   // 4 waves x 32 token rows
-constexpr int kGemmN = 16;          // experts per block
+constexpr int kGemmThreads = 256;   // 4 waves
+constexpr int kGemmSteps = 16;      // 32-wide k steps of a chunk held in registers (kc <= 512)
 constexpr int kXcds = 8;            // accelerator complex dies of the MI355X
-constexpr int kGemmPrefetch = 16;   // 32-wide k steps of a chunk held in registers (kc <= 512)
 
-template <bool F16>
+// Tile shape of the projection: experts per block = 16 * MOE_FE_GEMM_NS,
+// tokens per block = 64 * MOE_FE_GEMM_S, k-chunk = the largest multiple of 32
+// up to MOE_FE_GEMM_KC_MAX (see front_end_kchunk).
+#ifndef MOE_FE_GEMM_NS
+#define MOE_FE_GEMM_NS 2
+#endif
+#ifndef MOE_FE_GEMM_S
+#define MOE_FE_GEMM_S 1
+#endif
+#ifndef MOE_FE_GEMM_KC_MAX
+#define MOE_FE_GEMM_KC_MAX 480
+#endif
+
+__host__ __device__ inline int gemm_tile_stride(int kc) { return kc + 8; }   // u16, padded
+
+// Split-K router projection: block = (k-chunk, 16*NS experts, 64*S tokens).
+// Wave w computes tokens [64*S*tb + 16*S*w, +16*S) x the block's experts with
+// v_mfma_f32_16x16x32_{bf16,f16}.  A comes from global memory straight into
+// registers, requested first.  The W tile is staged transposed in LDS
+// ([16*NS][kc + 8]: the padding spreads the 16 columns an MFMA reads over the
+// LDS banks); each thread transposes 8 k-rows x 8 experts in registers with
+// byte permutes so that the LDS writes are 16 bytes wide.
+template <bool F16, int NS, int S>
 __global__ void __launch_bounds__(kGemmThreads)
     gemm_kernel(const uint16_t* __restrict__ normed, const uint16_t* __restrict__ W, int T, int H,
                 int E, int kc, float* __restrict__ partial) {
-  extern __shared__ __align__(16) uint16_t wt[];         // [16][kc] transposed tile
-  // Blocks are dispatched to the 8 XCDs round-robin (block b on XCD b % 8).
-  // When the chunk count is a multiple of 8, every n-tile of chunk c runs on
-  // XCD c % 8, so that the chunk's A rows and the W lines its n-tiles share
-  // come into one L2 once.
-  const int ntiles = E / kGemmN;
+  extern __shared__ __align__(16) uint16_t wt[];
+  constexpr int kN = 16 * NS, kRows = 64 * S;
+  const int ngroups = (E + kN - 1) / kN;
+  const int ntb = (T + kRows - 1) / kRows;
   const int nchunks = H / kc;
+  const int per_chunk = ngroups * ntb;
+  // Blocks are dispatched to the 8 XCDs round-robin (block b on XCD b % 8).
+  // When the chunk count is a multiple of 8, every block of chunk c runs on
+  // XCD c % 8, so that the chunk's A rows and W tiles come into one L2 once.
   const int b = blockIdx.x;
-  int nt, ch;
+  int ch, r;
   if (nchunks % kXcds == 0) {
-    const int x = b % kXcds, i = b / kXcds;               // i-th block of XCD x
-    ch = x + kXcds * (i / ntiles);
-    nt = i % ntiles;
+    const int x = b % kXcds, i = b / kXcds;             // i-th block of XCD x
+    ch = x + kXcds * (i / per_chunk);
+    r = i % per_chunk;
   } else {
-    ch = b / ntiles;
-    nt = b % ntiles;
+    ch = b / per_chunk;
+    r = b % per_chunk;
   }
-  const int n0 = nt * kGemmN, k0 = ch * kc;
+  const int ng = r / ntb, tb = r % ntb;
+  const int n0 = ng * kN, k0 = ch * kc;
+  const int nsub = min(NS, (E - n0) / 16);              // E % 16 == 0
+  const int nw = nsub * 16;                             // experts in this block
+  const int ts = gemm_tile_stride(kc);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-  const int col = lane & 15, grp = lane >> 4;          // k-group of 8
-  f32x4v acc[2] = {f32x4v{0, 0, 0, 0}, f32x4v{0, 0, 0, 0}};
-  const int rows[2] = {wv * 32 + col, wv * 32 + 16 + col};
-  // the A operand of the whole k-chunk (kc <= 32 * kGemmPrefetch) is
-  // requested first, then the W tile; both latencies overlap
-  u32x4 av[kGemmPrefetch][2];
+  const int col = lane & 15, grp = lane >> 4;           // k-group of 8
+  const int row0 = tb * kRows + wv * 16 * S;
+  u32x4 av[kGemmSteps][S];
 #pragma unroll
-  for (int u = 0; u < kGemmPrefetch; ++u)
+  for (int u = 0; u < kGemmSteps; ++u)
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
-      av[u][s] = (rows[s] < T && 32 * u < kc)
-                     ? *reinterpret_cast<const u32x4*>(normed + (size_t)rows[s] * H + k0 + 32 * u +
+    for (int s = 0; s < S; ++s) {
+      const int row = row0 + 16 * s + col;
+      av[u][s] = (row < T && 32 * u < kc)
+                     ? *reinterpret_cast<const u32x4*>(normed + (size_t)row * H + k0 + 32 * u +
                                                        grp * 8)
                      : u32x4{0, 0, 0, 0};
-  // stage W[k0 : k0+kc, n0 : n0+16] transposed: 16-byte loads of 8 experts
-  for (int v = tid; v < kc * 2; v += kGemmThreads) {
-    const int kk = v >> 1, half = v & 1;
-    const u32x4 q = *reinterpret_cast<const u32x4*>(W + (size_t)(k0 + kk) * E + n0 + half * 8);
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    }
+  // W[k0 : k0+kc, n0 : n0+nw] -> wt[n][k]: 8 x 8 blocks, one per thread per round
+  const int nb8 = (kc / 8) * (nw / 8);
+  for (int q = tid; q < nb8; q += kGemmThreads) {
+    const int kb = (q / (nw / 8)) * 8, nb = (q % (nw / 8)) * 8;
+    u32x4 w8[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      wt[(half * 8 + 2 * i) * kc + kk] = (uint16_t)(w[i] & 0xffffu);
-      wt[(half * 8 + 2 * i + 1) * kc + kk] = (uint16_t)(w[i] >> 16);
+    for (int i = 0; i < 8; ++i)
+      w8[i] = *reinterpret_cast<const u32x4*>(W + (size_t)(k0 + kb + i) * E + n0 + nb);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const int wi = n >> 1;
+      const uint32_t sel = (n & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
+      uint32_t o[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        o[j] = __builtin_amdgcn_perm(w8[2 * j + 1][wi], w8[2 * j][wi], sel);   // k = 2j, 2j+1
+      *reinterpret_cast<u32x4*>(wt + (nb + n) * ts + kb) = u32x4{o[0], o[1], o[2], o[3]};
     }
   }
   __syncthreads();
+  f32x4v acc[S][NS];
 #pragma unroll
-  for (int u = 0; u < kGemmPrefetch; ++u) {
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int n = 0; n < NS; ++n) acc[s][n] = f32x4v{0, 0, 0, 0};
+#pragma unroll
+  for (int u = 0; u < kGemmSteps; ++u) {
     const int kk = 32 * u;
     if (kk >= kc) break;
-    const u32x4 b = *reinterpret_cast<const u32x4*>(wt + col * kc + kk + grp * 8);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const u32x4 a = av[u][s];
-      if constexpr (F16)
-        acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
-                                                       __builtin_bit_cast(f16x8, b), acc[s], 0, 0, 0);
-      else
-        acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                        __builtin_bit_cast(bf16x8, b), acc[s], 0, 0, 0);
+    for (int n = 0; n < NS; ++n) {
+      if (n >= nsub) break;
+      const u32x4 bv = *reinterpret_cast<const u32x4*>(wt + (16 * n + col) * ts + kk + grp * 8);
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        if constexpr (F16)
+          acc[s][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              __builtin_bit_cast(f16x8, av[u][s]), __builtin_bit_cast(f16x8, bv), acc[s][n], 0, 0, 0);
+        else
+          acc[s][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, av[u][s]), __builtin_bit_cast(bf16x8, bv), acc[s][n], 0, 0,
+              0);
+      }
     }
   }
   // D layout: lane holds column (lane & 15), rows 4 * (lane >> 4) + i
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < S; ++s)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = wv * 32 + 16 * s + 4 * grp + i;
-      if (row < T) partial[((size_t)ch * T + row) * E + n0 + col] = acc[s][i];
+    for (int n = 0; n < NS; ++n) {
+      if (n >= nsub) break;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = row0 + 16 * s + 4 * grp + i;
+        if (row < T) partial[((size_t)ch * T + row) * E + n0 + 16 * n + col] = acc[s][n][i];
+      }
     }
-  }
 }
 
 constexpr int kSelectThreads = 256;  // one wavefront per token
@@ -278,12 +324,15 @@ __global__ void __launch_bounds__(kSelectThreads)
 }
 
 int front_end_kchunk(int H) {
-  // The largest multiple of 32 (one MFMA k step), at most 512, that divides H
-  // into a multiple of 8 chunks (one group of n-tiles per XCD); else the
-  // largest that divides H into at least 8 chunks; else 128 (H % 128 == 0).
-  for (int kc = 512; kc >= 128; kc -= 32)
+  // The largest multiple of 32 (one MFMA k step), at most MOE_FE_GEMM_KC_MAX
+  // (<= 480: a padded 64-expert W tile then fits in 64 KiB of LDS), that
+  // divides H into a multiple of 8 chunks (one group of blocks per XCD);
+  // else the largest that divides H into at least 8 chunks; else 128
+  // (H % 128 == 0).
+  static_assert(MOE_FE_GEMM_KC_MAX <= 480 && MOE_FE_GEMM_KC_MAX % 32 == 0, "k-chunk bound");
+  for (int kc = MOE_FE_GEMM_KC_MAX; kc >= 128; kc -= 32)
     if (H % kc == 0 && (H / kc) % kXcds == 0) return kc;
-  for (int kc = 512; kc >= 128; kc -= 32)
+  for (int kc = MOE_FE_GEMM_KC_MAX; kc >= 128; kc -= 32)
     if (H % kc == 0 && H / kc >= 8) return kc;
   return 128;
 }
@@ -302,14 +351,17 @@ hipError_t launch_front_end(const FrontEndParams& q, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t lds = (size_t)kGemmN * kc * sizeof(uint16_t);
-  dim3 grid((q.E / kGemmN) * nchunks);
+  constexpr int kNS = MOE_FE_GEMM_NS, kS = MOE_FE_GEMM_S;
+  static_assert((kNS == 1 || kNS == 2 || kNS == 4) && (kS == 1 || kS == 2), "gemm tile shape");
+  const size_t lds = (size_t)16 * kNS * gemm_tile_stride(kc) * sizeof(uint16_t);
+  const int blocks = ((q.E + 16 * kNS - 1) / (16 * kNS)) * ((q.T + 64 * kS - 1) / (64 * kS)) *
+                     nchunks;
   if (q.f16)
-    hipLaunchKernelGGL(gemm_kernel<true>, grid, dim3(kGemmThreads), lds, s,
+    hipLaunchKernelGGL((gemm_kernel<true, kNS, kS>), dim3(blocks), dim3(kGemmThreads), lds, s,
                        (const uint16_t*)q.normed, (const uint16_t*)q.W, q.T, q.H, q.E, kc,
                        q.partial);
   else
-    hipLaunchKernelGGL(gemm_kernel<false>, grid, dim3(kGemmThreads), lds, s,
+    hipLaunchKernelGGL((gemm_kernel<false, kNS, kS>), dim3(blocks), dim3(kGemmThreads), lds, s,
                        (const uint16_t*)q.normed, (const uint16_t*)q.W, q.T, q.H, q.E, kc,
                        q.partial);
   e = hipGetLastError();
