@@ -194,7 +194,7 @@ def other_configs(mr, torch, np, dev, rotate_mb, K):
         fsets.append((h0.clone(), w0.clone(), torch.empty((f.T, f.H), dtype=torch.bfloat16, device=dev),
                       torch.empty((f.T, f.k), dtype=torch.int32, device=dev),
                       torch.empty((f.T, f.E), dtype=torch.bfloat16, device=dev)))
-    wsf = torch.empty(max(mr.rmsnorm_gate_route_workspace_size(f.T, f.H, f.E), 1), dtype=torch.uint8,
+    wsf = torch.zeros(max(mr.rmsnorm_gate_route_workspace_size(f.T, f.H, f.E), 1), dtype=torch.uint8,
                       device=dev)
 
     def fstep(i):

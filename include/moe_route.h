@@ -17,14 +17,16 @@
  *   caller.  The library never allocates, frees, synchronises, or copies device
  *   memory to the host.  Scratch memory comes from the caller's `workspace`
  *   (device memory, 256-byte aligned, at least the size the matching
- *   *_workspace_size() helper returns).  For moe_aux_loss and
- *   rmsnorm_gate_route its contents on entry are ignored.  The ROUTING
- *   workspace (moe_route with expert_counts, moe_route_permute) starts with a
- *   counting region (the first moe_route_count_region_bytes() bytes) that must
- *   be zero-filled before the workspace's first use; every call leaves it
+ *   *_workspace_size() helper returns).  For moe_aux_loss its contents on
+ *   entry are ignored.  The ROUTING workspace (moe_route with expert_counts,
+ *   moe_route_permute) starts with a counting region (the first
+ *   moe_route_count_region_bytes() bytes), and the FRONT-END workspace
+ *   (rmsnorm_gate_route) with a synchronisation region (the first
+ *   rmsnorm_gate_route_sync_region_bytes() bytes).  That region must be
+ *   zero-filled before the workspace's first use; every call leaves it
  *   zero-filled again when its work completes, so one workspace serves any
- *   sequence of routing calls of any sizes on one stream.  After an MOE_EHIP
- *   failure mid-call, zero it again.  All arrays are dense and row-major.
+ *   sequence of calls of any sizes on one stream.  After an MOE_EHIP failure
+ *   mid-call, zero it again.  All arrays are dense and row-major.
  * Streams: all work is enqueued on `stream` (0 = the null stream); outputs are
  *   valid once that work completes.  Calls on different streams that share a
  *   workspace race.  Calls are otherwise re-entrant and thread-safe.
@@ -225,7 +227,7 @@ moe_status moe_aux_loss(const float* probs, const int32_t* tokens_per_expert, in
  * Parameters, Returns, Notes):
  *
  *   r_t        = (mean_h hidden[t,h]^2 + eps)^(-1/2)           (float32)
- *   normed     = round_to_dtype(hidden * r_t * gamma)          out [T, H]
+ *   normed     = round_to_dtype((hidden * gamma) * r_t)        out [T, H]
  *   z          = normed @ router_weights (+ router_bias)       (MFMA, float32
  *                accumulation; consumes exactly the stored normed values)
  *   topk_ids   = the k largest z per token, lower index on ties   out [T, k]
@@ -238,7 +240,15 @@ moe_status moe_aux_loss(const float* probs, const int32_t* tokens_per_expert, in
  *              128 <= H <= 16384; 1 <= E <= 512 with E % 16 == 0;
  *              1 <= top_k <= min(E, 64).
  * router_bias  nullable [E].
- * workspace    >= rmsnorm_gate_route_workspace_size(T, H, E) bytes. */
+ * workspace    >= rmsnorm_gate_route_workspace_size(T, H, E) bytes, starting
+ *              with the zero-filled synchronisation region (conventions above).
+ *
+ * Two launches: normalisation and projection in one, whose projection blocks
+ * wait in-kernel (polling the synchronisation region) for the normalisation
+ * scale of their tokens; then the selection.  Should a wait ever exceed its
+ * spin limit (it cannot while blocks are dispatched in index order), the call
+ * still completes and writes -1 into topk_ids; zero the region again after
+ * that. */
 moe_status rmsnorm_gate_route(const void* hidden, const void* gamma, const void* router_weights,
                               const void* router_bias, int32_t dtype, int32_t T, int32_t H,
                               int32_t E, float eps, int32_t top_k, int32_t act_fn, void* normed,
@@ -248,12 +258,15 @@ moe_status rmsnorm_gate_route(const void* hidden, const void* gamma, const void*
 /* Workspace sizes in bytes (0 = none needed).  Pure host functions.
  * moe_route_workspace_size() covers both routing entry points; its first
  * moe_route_count_region_bytes() bytes are the counting region described in
- * the conventions above (a constant, independent of the sizes). */
+ * the conventions above, and rmsnorm_gate_route_sync_region_bytes() is the
+ * front end's synchronisation region (both constants, independent of the
+ * sizes). */
 size_t moe_route_workspace_size(const moe_route_args* args, int32_t tile_tokens_dim,
                                 int32_t local_num_experts);
 size_t moe_route_count_region_bytes(void);
 size_t moe_aux_loss_workspace_size(int64_t rows, int32_t num_experts);
 size_t rmsnorm_gate_route_workspace_size(int32_t T, int32_t H, int32_t E);
+size_t rmsnorm_gate_route_sync_region_bytes(void);
 
 /* Output-size helpers for moe_route_permute ([FI] Returns): an upper bound on
  * total_num_padded_tokens, T*k + E_loc*(tile-1), and on the tile count,

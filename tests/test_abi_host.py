@@ -140,3 +140,42 @@ def test_status_strings():
     for s in range(5):
         assert _lib.lib.moe_status_string(s).decode().startswith(_lib.STATUS_NAMES[s])
     assert b"unknown" in _lib.lib.moe_status_string(99)
+
+
+def _front(T=128, H=7168, E=256, k=8, dtype=None, act=None, eps=1e-6, ws=FAKE, ws_bytes=1 << 30,
+           hidden=FAKE, ids=FAKE):
+    dtype = mr.MOE_BF16 if dtype is None else dtype
+    act = mr.MOE_SIGMOID if act is None else act
+    return _lib.lib.rmsnorm_gate_route(hidden, FAKE, FAKE, None, dtype, T, H, E,
+                                       ctypes.c_float(eps), k, act, FAKE, ids, FAKE, ws,
+                                       ctypes.c_size_t(ws_bytes), None)
+
+
+def test_front_end_validation():
+    # every call below fails on the host, before anything is launched
+    assert _front(T=0) == mr.MOE_EINVAL
+    assert _front(T=129) == mr.MOE_EINVAL              # single-tile decode: T <= 128
+    assert _front(H=7000) == mr.MOE_EINVAL             # H % 128 != 0
+    assert _front(E=24) == mr.MOE_EUNSUPPORTED         # E % 16 != 0
+    assert _front(k=257) == mr.MOE_EINVAL              # k > E
+    assert _front(k=0) == mr.MOE_EINVAL
+    assert _front(dtype=mr.MOE_F32) == mr.MOE_EINVAL
+    assert _front(act=7) == mr.MOE_EINVAL
+    assert _front(eps=float("nan")) == mr.MOE_EINVAL
+    assert _front(hidden=None) == mr.MOE_EINVAL
+    assert _front(ids=None) == mr.MOE_EINVAL
+    assert _front(ws_bytes=16) == mr.MOE_EWORKSPACE
+    assert _front(ws=None) == mr.MOE_EWORKSPACE
+    # the synchronisation region is reused across calls: 256-byte alignment
+    assert _front(ws=ctypes.c_void_p(0x1010)) == mr.MOE_EINVAL
+
+
+def test_front_end_workspace_size():
+    region = mr.rmsnorm_gate_route_sync_region_bytes()
+    assert region == 1024                              # fixed: independent of the sizes
+    # sync region + float32 partials [H / 448, T, E]
+    assert mr.rmsnorm_gate_route_workspace_size(128, 7168, 256) == region + 16 * 128 * 256 * 4
+    for T, H, E in [(1, 128, 16), (37, 2048, 256), (128, 384, 32)]:
+        n = mr.rmsnorm_gate_route_workspace_size(T, H, E)
+        assert n % 256 == 0 and n >= region + T * E * 4
+    assert mr.rmsnorm_gate_route_workspace_size(0, 7168, 256) == 0

@@ -25,10 +25,10 @@ DEV = "cuda:0"
 
 def _kchunk(H):
     # the library's k-chunk (fixes the fp32 summation depth of the projection)
-    for kc in range(480, 127, -32):
+    for kc in (448, 384, 256, 128):
         if H % kc == 0 and (H // kc) % 8 == 0:
             return kc
-    for kc in range(480, 127, -32):
+    for kc in (448, 384, 256, 128):
         if H % kc == 0 and H // kc >= 8:
             return kc
     return 128
@@ -40,7 +40,8 @@ def _decode(bits, dtype):
     return bits.view(np.float16).astype(np.float64)
 
 
-def run_front_end(f: FrontEndWorkload, T, H, E, seed, act="sigmoid", dtype="bf16", rbias=False):
+def run_front_end(f: FrontEndWorkload, T, H, E, seed, act="sigmoid", dtype="bf16", rbias=False,
+                  ws=None):
     f2 = FrontEndWorkload(name="fe", seed=seed, T=T, H=H, E=E, k=f.k if f.k <= E else E,
                           act=act, dtype="bf16", router_bias_std=0.05 if rbias else None)
     hidden, gamma, W, rb = front_end_inputs(f2)
@@ -59,12 +60,16 @@ def run_front_end(f: FrontEndWorkload, T, H, E, seed, act="sigmoid", dtype="bf16
     normed = torch.empty((T, H), dtype=tdt, device=DEV)
     ids = torch.full((T, k), -7, dtype=torch.int32, device=DEV)
     aff = torch.full((T, E), 7.0, dtype=torch.bfloat16, device=DEV)
-    ws = torch.empty(max(mr.rmsnorm_gate_route_workspace_size(T, H, E), 1), dtype=torch.uint8,
-                     device=DEV)
+    if ws is None:
+        ws = torch.zeros(max(mr.rmsnorm_gate_route_workspace_size(T, H, E), 1), dtype=torch.uint8,
+                         device=DEV)
     mr.rmsnorm_gate_route(h_d, g_d, w_d, b_d, mr.MOE_BF16 if dtype == "bf16" else mr.MOE_F16,
                           T, H, E, f2.eps, k, mr.MOE_SIGMOID if act == "sigmoid" else mr.MOE_SOFTMAX,
                           normed, ids, aff, workspace=ws)
     torch.cuda.synchronize()
+    # the in-launch handshake leaves the synchronisation region zero-filled again
+    region = mr.rmsnorm_gate_route_sync_region_bytes()
+    assert int(torch.count_nonzero(ws[:region])) == 0, "sync region not left zero-filled"
     normed_bits = normed.view(torch.int16).cpu().numpy().view(np.uint16)
     # 1. RMSNorm
     ref_y, ref_bits = oracle.rmsnorm(hidden, gamma, f2.eps, dtype=dtype)
@@ -132,7 +137,7 @@ def test_front_end_deterministic():
         normed = torch.empty((64, f.H), dtype=torch.bfloat16, device=DEV)
         ids = torch.empty((64, f.k), dtype=torch.int32, device=DEV)
         aff = torch.empty((64, f.E), dtype=torch.bfloat16, device=DEV)
-        ws = torch.empty(mr.rmsnorm_gate_route_workspace_size(64, f.H, f.E), dtype=torch.uint8,
+        ws = torch.zeros(mr.rmsnorm_gate_route_workspace_size(64, f.H, f.E), dtype=torch.uint8,
                          device=DEV)
         mr.rmsnorm_gate_route(h_d, g_d, w_d, None, mr.MOE_BF16, 64, f.H, f.E, f.eps, f.k,
                               mr.MOE_SIGMOID, normed, ids, aff, workspace=ws)
@@ -140,3 +145,13 @@ def test_front_end_deterministic():
         outs.append((normed.clone(), ids.clone(), aff.clone()))
     for a, b in zip(outs[0], outs[1]):
         assert torch.equal(a, b)
+
+
+def test_front_end_workspace_reuse_across_sizes():
+    # one zero-filled workspace, sized for the largest call, serves a sequence
+    # of calls of different sizes (each call leaves it zero-filled)
+    ws = torch.zeros(mr.rmsnorm_gate_route_workspace_size(128, 7168, 512), dtype=torch.uint8,
+                     device=DEV)
+    for (T, H, E, act) in [(128, 7168, 256, "sigmoid"), (37, 2048, 512, "softmax"),
+                           (1, 128, 16, "sigmoid"), (128, 7168, 512, "sigmoid")]:
+        run_front_end(FRONT_END, T, H, E, seed=900 + T + E, act=act, ws=ws)

@@ -28,7 +28,8 @@ __all__ = [
     "moe_route", "moe_route_permute", "moe_aux_loss", "rmsnorm_gate_route",
     "moe_route_workspace_size", "moe_route_count_region_bytes", "moe_aux_loss_workspace_size",
     "moe_profile_begin", "moe_profile_end", "moe_profile_read",
-    "rmsnorm_gate_route_workspace_size", "moe_max_padded_tokens", "moe_max_tiles",
+    "rmsnorm_gate_route_workspace_size", "rmsnorm_gate_route_sync_region_bytes",
+    "moe_max_padded_tokens", "moe_max_tiles",
     "make_route_args", "route", "route_permute", "MoeError", "moe_route_args", "LIB_PATH",
     "MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_EWORKSPACE", "MOE_EHIP",
     "MOE_F32", "MOE_BF16", "MOE_F16", "MOE_SOFTMAX", "MOE_SIGMOID",
@@ -136,6 +137,10 @@ def moe_aux_loss_workspace_size(rows: int, num_experts: int) -> int:
 
 def rmsnorm_gate_route_workspace_size(T: int, H: int, E: int) -> int:
     return int(_lib.lib.rmsnorm_gate_route_workspace_size(T, H, E))
+
+
+def rmsnorm_gate_route_sync_region_bytes() -> int:
+    return int(_lib.lib.rmsnorm_gate_route_sync_region_bytes())
 
 
 def moe_max_padded_tokens(T: int, k: int, local_num_experts: int, tile: int) -> int:

@@ -22,7 +22,8 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EUNSUPPORTED", 3: "MOE_EWO
 EXPORTED = [
     "moe_route", "moe_route_permute", "moe_aux_loss", "rmsnorm_gate_route",
     "moe_route_workspace_size", "moe_route_count_region_bytes", "moe_aux_loss_workspace_size",
-    "rmsnorm_gate_route_workspace_size", "moe_max_padded_tokens", "moe_max_tiles",
+    "rmsnorm_gate_route_workspace_size", "rmsnorm_gate_route_sync_region_bytes",
+    "moe_max_padded_tokens", "moe_max_tiles",
     "moe_status_string", "moe_last_error_message", "moe_last_hip_error",
     "moe_profile_begin", "moe_profile_end", "moe_profile_read",
 ]
@@ -99,6 +100,8 @@ def _load():
     lib.moe_aux_loss_workspace_size.restype = sz
     lib.rmsnorm_gate_route_workspace_size.argtypes = [i32, i32, i32]
     lib.rmsnorm_gate_route_workspace_size.restype = sz
+    lib.rmsnorm_gate_route_sync_region_bytes.argtypes = []
+    lib.rmsnorm_gate_route_sync_region_bytes.restype = sz
     lib.moe_max_padded_tokens.argtypes = [i32, i32, i32, i32]
     lib.moe_max_padded_tokens.restype = i64
     lib.moe_max_tiles.argtypes = [i32, i32, i32, i32]

@@ -536,9 +536,10 @@ moe_status moe_aux_loss(const float* probs, const int32_t* tokens_per_expert, in
 
 size_t rmsnorm_gate_route_workspace_size(int32_t T, int32_t H, int32_t E) {
   if (T < 1 || H < 128 || H % 128 || E < 1) return 0;
-  const int nchunks = H / moe::front_end_kchunk(H);
-  return align256((size_t)nchunks * T * E * sizeof(float));
+  return align256(moe::front_end_workspace_bytes(T, H, E));
 }
+
+size_t rmsnorm_gate_route_sync_region_bytes(void) { return moe::kFrontEndSyncBytes; }
 
 moe_status rmsnorm_gate_route(const void* hidden, const void* gamma, const void* router_weights,
                               const void* router_bias, int32_t dtype, int32_t T, int32_t H,
@@ -566,6 +567,7 @@ moe_status rmsnorm_gate_route(const void* hidden, const void* gamma, const void*
   const size_t need = rmsnorm_gate_route_workspace_size(T, H, E);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(MOE_EWORKSPACE, "workspace needs %zu bytes", need);
+  if (!aligned(workspace, 256)) return fail(MOE_EINVAL, "workspace must be 256-byte aligned");
   moe::FrontEndParams q{};
   q.hidden = hidden;
   q.gamma = gamma;
@@ -581,7 +583,7 @@ moe_status rmsnorm_gate_route(const void* hidden, const void* gamma, const void*
   q.normed = normed;
   q.ids = topk_ids;
   q.aff = affinities;
-  q.partial = static_cast<float*>(workspace);
+  q.workspace = workspace;
   hipError_t e = launch_with_profile(
       MOE_KERNEL_FRONT_END, stream, [&] { return moe::launch_front_end(q, stream); },
       /*single_kernel=*/false);

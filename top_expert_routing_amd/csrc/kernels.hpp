@@ -138,9 +138,13 @@ struct FrontEndParams {
   void* normed;
   int32_t* ids;
   void* aff;
-  float* partial;         // workspace [H / kchunk, T, E]
+  void* workspace;        // sync region (failure word, r_t slots), partials [H / kchunk, T, E]
 };
+// The front-end workspace starts with a synchronisation region of this many
+// bytes: zero before the first call, zero again after every call.
+constexpr int kFrontEndSyncBytes = 1024;
 int front_end_kchunk(int H);
+size_t front_end_workspace_bytes(int T, int H, int E);
 hipError_t launch_front_end(const FrontEndParams& q, hipStream_t s);
 
 int aux_fwd_blocks(int64_t rows, int E);
