@@ -482,6 +482,12 @@ __global__ void __launch_bounds__(64)
   const int t = blockIdx.x;
   const int e0 = J * lane;
   const bool owner = e0 < E;                           // E % J == 0: whole vectors
+  // the failure word and the router bias first: their latency overlaps the
+  // partials'
+  const bool failed = *fail != 0u;
+  float bias[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) bias[j] = (owner && rbias != nullptr) ? h2f<F16>(rbias[e0 + j]) : 0.0f;
   // chunk partials, summed in chunk order, every load of the token requested
   // before the sums
   const float* pt = partial + (size_t)t * E + e0;
@@ -508,12 +514,11 @@ __global__ void __launch_bounds__(64)
         if (c0 + u < nchunks) z[j] += pv[u][j];
   }
   if (lane == 0) rstd[t] = 0u;                         // back to "not yet written"
-  const bool failed = *fail != 0u;
   uint64_t pk[J];                                      // (key, lower index first); 0 = none
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     if (owner) {
-      if (rbias != nullptr) z[j] += h2f<F16>(rbias[e0 + j]);
+      if (rbias != nullptr) z[j] += bias[j];
       pk[j] = pack_key(z[j] + 0.0f, e0 + j);
     } else {
       z[j] = -__builtin_huge_valf();
