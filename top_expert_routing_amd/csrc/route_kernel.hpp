@@ -637,15 +637,25 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>) route_kernel(RouteParams p) 
       if (p.scores != nullptr) {
         float* srow = p.scores + (size_t)t * E;
         const float inv_ss = VAR == kVarSigmoid ? fast_rcp(ssum) : 0.0f;
+        float v[EPL];
 #pragma unroll
         for (int i = 0; i < EPL; ++i) {
-          if (e0 + i < E) {
-            float v;
-            if constexpr (VAR == kVarSigmoid) v = x[i] * inv_ss;
-            else if (VAR == kVarSoftmaxBias && pre) v = x[i];
-            else v = exp_f32(x[i] - m) * inv_s;
-            srow[e0 + i] = v;
-          }
+          if constexpr (VAR == kVarSigmoid) v[i] = x[i] * inv_ss;
+          else if (VAR == kVarSoftmaxBias && pre) v[i] = x[i];
+          else v[i] = exp_f32(x[i] - m) * inv_s;
+        }
+        // 16-byte stores when rows are 16-byte aligned (E % 4 == 0; e0 and
+        // EPL are multiples of 4, so a group of four is all in or all out):
+        // a lane's scalar stores would each touch another cache line.
+        if ((E & 3) == 0) {
+#pragma unroll
+          for (int i = 0; i < EPL; i += 4)
+            if (e0 + i < E)
+              *reinterpret_cast<f32x4*>(srow + e0 + i) = f32x4{v[i], v[i + 1], v[i + 2], v[i + 3]};
+        } else {
+#pragma unroll
+          for (int i = 0; i < EPL; ++i)
+            if (e0 + i < E) srow[e0 + i] = v[i];
         }
       }
     }
