@@ -22,6 +22,7 @@ namespace moe {
 namespace {
 constexpr int kAuxBlock = 256;
 constexpr int kAuxMaxE = 2048;
+constexpr int kAuxUnroll = 8;   // 16-byte loads in flight per thread (32 KiB per block)
 }
 
 __global__ void __launch_bounds__(kAuxBlock)
@@ -37,15 +38,25 @@ __global__ void __launch_bounds__(kAuxBlock)
   const int64_t begin = r0 * E, end = r1 * E;
   float acc = 0.0f;
   if (vec) {
-    // E % 4 == 0 and probs 16-byte aligned: element groups of 4 share a row
+    // E % 4 == 0 and probs 16-byte aligned: element groups of 4 share a row.
+    // kAuxUnroll groups per thread are requested before any is used.
     const int64_t stride = (int64_t)kAuxBlock * 4;
-    int col = (int)((begin + threadIdx.x * 4) % E);
     const int step = (int)(stride % E);
-    for (int64_t i = begin + threadIdx.x * 4; i < end; i += stride) {
-      const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(probs + i));
-      acc += v.x * cs[col] + v.y * cs[col + 1] + v.z * cs[col + 2] + v.w * cs[col + 3];
-      col += step;
-      if (col >= E) col -= E;
+    int64_t i = begin + threadIdx.x * 4;
+    int col = (int)(i % E);
+    for (; i < end; i += stride * kAuxUnroll) {
+      f32x4 v[kAuxUnroll];
+#pragma unroll
+      for (int u = 0; u < kAuxUnroll; ++u)
+        v[u] = i + u * stride < end
+                   ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(probs + i + u * stride))
+                                    : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int u = 0; u < kAuxUnroll; ++u) {
+        acc += v[u].x * cs[col] + v[u].y * cs[col + 1] + v[u].z * cs[col + 2] + v[u].w * cs[col + 3];
+        col += step;
+        if (col >= E) col -= E;
+      }
     }
   } else {
     for (int64_t i = begin + threadIdx.x; i < end; i += kAuxBlock)
