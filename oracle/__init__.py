@@ -23,6 +23,7 @@ permutation  tile-padded per-expert offsets, expanded->permuted and
              permuted->token maps, per-tile expert map and row limit
 aux_loss     load-balancing loss forward and backward
 front_end    RMSNorm -> router projection -> top-k on raw logits -> activation
+backward     gradient of the routing weights and aux-loss scores w.r.t. logits
 
 Parity pins: every function here is pinned by ``tests/test_oracle_*.py`` against
 closed forms, invariants, brute force on tiny inputs or library routines; see
@@ -32,10 +33,12 @@ from .routing import route, RouteResult, decode_input, selection_keys32, exact_k
 from .permutation import permute, PermuteResult, max_padded_tokens, max_tiles
 from .aux_loss import aux_loss_fwd, aux_loss_bwd
 from .front_end import rmsnorm, front_end_route, bf16_round_bits, FrontEndResult
+from .backward import route_backward
 
 __all__ = [
     "route", "RouteResult", "decode_input", "selection_keys32", "exact_keys64",
     "permute", "PermuteResult", "max_padded_tokens", "max_tiles",
     "aux_loss_fwd", "aux_loss_bwd",
     "rmsnorm", "front_end_route", "bf16_round_bits", "FrontEndResult",
+    "route_backward",
 ]

@@ -45,7 +45,11 @@ def decode_input(values, dtype: str) -> np.ndarray:
 
     ``f32``: float32 array.  ``bf16``: uint16 bit patterns; a bfloat16 value is
     the float32 whose upper 16 bits are those bits and whose lower 16 are zero.
+    ``f64``: float64 values as given (the finite-difference pins of the
+    backward perturb logits below float32 resolution).
     """
+    if dtype == "f64":
+        return np.array(values, dtype=np.float64)
     if dtype == "f32":
         return np.asarray(values, dtype=np.float32).astype(np.float64)
     if dtype == "bf16":

@@ -9,6 +9,7 @@ import pytest
 
 import oracle
 import test_oracle_aux_front as T_AF
+import test_oracle_backward as T_B
 import test_oracle_golden as T_G
 import test_oracle_permutation as T_P
 import test_oracle_routing as T_R
@@ -24,6 +25,7 @@ PINS = [
     T_AF.pin_bf16_rounding, T_AF.pin_identity_projection,
     T_G.pin_golden_routing, T_G.pin_golden_permutation, T_G.pin_golden_aux_loss,
     T_G.pin_golden_rmsnorm,
+    T_B.pin_backward_finite_differences, T_B.pin_backward_invariants,
 ]
 
 # (module, text in the oracle, planted replacement, what the mistake is)
@@ -80,6 +82,19 @@ MUTATIONS = [
     ("front_end", "    z = a @ w\n", "    z = a[:, ::-1] @ w\n", "hidden features reversed in the projection"),
     ("front_end", "        sel = 1.0 / (1.0 + np.exp(-zs))", "        sel = 1.0 / (1.0 + np.exp(-zs)); sel = sel / sel.sum(axis=1, keepdims=True)",
      "sigmoid affinities renormalised"),
+    ("backward", "                ds = (g - c) / S", "                ds = g / S",
+     "backward: renormalisation's coupling term dropped"),
+    ("backward", "            dsig = s * (1.0 - s)\n            np.add.at(grad",
+     "            dsig = s\n            np.add.at(grad", "backward: sigmoid derivative taken as sigma"),
+    ("backward", "            grad += p * (dp - c2)", "            grad += p * (dp + c2)",
+     "backward: softmax Jacobian with the wrong sign"),
+    ("backward", "        g = float(scale) * np.asarray(grad_weights", "        g = np.asarray(grad_weights",
+     "backward: routed scaling factor not applied"),
+    ("backward", "            grad += dsig * (h - c) / Z", "            grad += dsig * (h - c)",
+     "backward: sigmoid scores' normaliser dropped"),
+    ("backward", "            np.add.at(grad, (rows, ids), w * (g - c))",
+     "            np.add.at(grad, (rows, ids[:, ::-1]), w * (g - c))",
+     "backward: gradient scattered to the chosen experts in reverse order"),
 ]
 
 
