@@ -223,6 +223,34 @@ moe_status moe_aux_loss(const float* probs, const int32_t* tokens_per_expert, in
                         float coeff, float* loss, const float* grad_loss, float* grad_probs,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Backward of moe_route's outputs with respect to the logits ([TE]
+ * Description: fused_topk_with_score_function and
+ * fused_compute_score_for_moe_aux_loss each have a backward).  The pages
+ * print no formula; this is the derivative of the forward with the chosen
+ * experts held fixed (the top-k choice passes no gradient; the bias, which
+ * only enters the choice, receives none):
+ *
+ *   grad_logits = d/dlogits ( sum_j grad_weights[t, j] * topk_weights[t, j]
+ *                             + sum_e grad_scores[t, e] * scores[t, e] )
+ *
+ * through the score function of args (sigmoid; softmax before or after top-k),
+ * the renormalisation (args->renormalize) and args->routed_scaling_factor.
+ *
+ * args           the forward's arguments: num_tokens, num_experts (<= 512),
+ *                top_k, score_fn, use_pre_softmax, renormalize,
+ *                routed_scaling_factor, logits_dtype are used; the grouping
+ *                and bias fields are not (the choice is given by topk_ids).
+ * logits         [T, E], logits_dtype (the forward's input).
+ * topk_ids       [T, k] int32, the forward's ids (required with grad_weights);
+ *                ids outside [0, E) contribute nothing.
+ * grad_weights   nullable [T, k] float32, the gradient of topk_weights.
+ * grad_scores    nullable [T, E] float32, the gradient of the full-E scores.
+ * grad_logits    out [T, E] float32, every element written.
+ * At least one of grad_weights / grad_scores must be given.  No workspace. */
+moe_status moe_route_backward(const moe_route_args* args, const void* logits,
+                              const int32_t* topk_ids, const float* grad_weights,
+                              const float* grad_scores, float* grad_logits, hipStream_t stream);
+
 /* Fused decode front end ([NKI] rmsnorm_router_topk_a2av: Background,
  * Parameters, Returns, Notes):
  *
@@ -290,7 +318,8 @@ typedef enum moe_kernel_kind {
   MOE_KERNEL_AUX_FWD = 3,
   MOE_KERNEL_AUX_BWD = 4,
   MOE_KERNEL_FRONT_END = 5,
-  MOE_KERNEL_KINDS = 6
+  MOE_KERNEL_ROUTE_BWD = 6,
+  MOE_KERNEL_KINDS = 7
 } moe_kernel_kind;
 moe_status moe_profile_begin(void);
 moe_status moe_profile_end(void);

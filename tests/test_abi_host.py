@@ -179,3 +179,26 @@ def test_front_end_workspace_size():
         n = mr.rmsnorm_gate_route_workspace_size(T, H, E)
         assert n % 256 == 0 and n >= region + T * E * 4
     assert mr.rmsnorm_gate_route_workspace_size(0, 7168, 256) == 0
+
+
+def test_route_backward_validation():
+    B = _lib.lib.moe_route_backward
+    args = mr.make_route_args(64, 256, 8, score_fn="sigmoid", logits_dtype="bf16")
+    ok = (ctypes.byref(args), FAKE, FAKE, FAKE, None, FAKE, None)
+    # every call below fails on the host, before anything is launched
+    assert B(None, *ok[1:]) == mr.MOE_EINVAL
+    assert B(ctypes.byref(args), FAKE, FAKE, None, None, FAKE, None) == mr.MOE_EINVAL   # no gradient
+    assert B(ctypes.byref(args), None, FAKE, FAKE, None, FAKE, None) == mr.MOE_EINVAL   # no logits
+    assert B(ctypes.byref(args), FAKE, None, FAKE, None, FAKE, None) == mr.MOE_EINVAL   # ids needed
+    assert B(ctypes.byref(args), FAKE, FAKE, FAKE, None, None, None) == mr.MOE_EINVAL   # no output
+    assert B(ctypes.byref(args), FAKE, FAKE, ctypes.c_void_p(0x1002), None, FAKE, None) == mr.MOE_EINVAL
+    big = mr.make_route_args(64, 1024, 8)
+    assert B(ctypes.byref(big), *ok[1:]) == mr.MOE_EUNSUPPORTED
+    bad_k = mr.make_route_args(64, 16, 17)
+    assert B(ctypes.byref(bad_k), *ok[1:]) == mr.MOE_EINVAL
+    bad_fn = mr.make_route_args(64, 16, 2)
+    bad_fn.score_fn = 5
+    assert B(ctypes.byref(bad_fn), *ok[1:]) == mr.MOE_EINVAL
+    # T = 0 is valid and launches nothing, even with placeholder pointers
+    empty = mr.make_route_args(0, 16, 2)
+    assert B(ctypes.byref(empty), None, None, None, FAKE, None, None) == mr.MOE_OK

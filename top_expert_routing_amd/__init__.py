@@ -22,10 +22,10 @@ from ._lib import (MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHI
                    MOE_F32, MOE_BF16, MOE_F16, MOE_SOFTMAX, MOE_SIGMOID, MoeError,
                    moe_route_args, LIB_PATH, MOE_KERNEL_ROUTE, MOE_KERNEL_COUNTS,
                    MOE_KERNEL_SCATTER, MOE_KERNEL_AUX_FWD, MOE_KERNEL_AUX_BWD,
-                   MOE_KERNEL_FRONT_END)
+                   MOE_KERNEL_FRONT_END, MOE_KERNEL_ROUTE_BWD)
 
 __all__ = [
-    "moe_route", "moe_route_permute", "moe_aux_loss", "rmsnorm_gate_route",
+    "moe_route", "moe_route_permute", "moe_aux_loss", "rmsnorm_gate_route", "moe_route_backward",
     "moe_route_workspace_size", "moe_route_count_region_bytes", "moe_aux_loss_workspace_size",
     "moe_profile_begin", "moe_profile_end", "moe_profile_read",
     "rmsnorm_gate_route_workspace_size", "rmsnorm_gate_route_sync_region_bytes",
@@ -109,6 +109,13 @@ def moe_aux_loss(probs, tokens_per_expert, rows: int, total_num_tokens: int, num
         ctypes.c_int64(total_num_tokens), num_experts, top_k, ctypes.c_float(coeff),
         _ptr(loss), _ptr(grad_loss), _ptr(grad_probs), _ptr(workspace),
         ctypes.c_size_t(ws_bytes), _stream(stream)))
+
+
+def moe_route_backward(args: moe_route_args, logits, topk_ids, grad_weights, grad_scores,
+                       grad_logits, stream=None) -> None:
+    _check(_lib.lib.moe_route_backward(ctypes.byref(args), _ptr(logits), _ptr(topk_ids),
+                                       _ptr(grad_weights), _ptr(grad_scores), _ptr(grad_logits),
+                                       _stream(stream)))
 
 
 def rmsnorm_gate_route(hidden, gamma, router_weights, router_bias, dtype: int, T: int, H: int,

@@ -20,7 +20,7 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EUNSUPPORTED", 3: "MOE_EWO
 
 # Every symbol the header declares.
 EXPORTED = [
-    "moe_route", "moe_route_permute", "moe_aux_loss", "rmsnorm_gate_route",
+    "moe_route", "moe_route_permute", "moe_aux_loss", "rmsnorm_gate_route", "moe_route_backward",
     "moe_route_workspace_size", "moe_route_count_region_bytes", "moe_aux_loss_workspace_size",
     "rmsnorm_gate_route_workspace_size", "rmsnorm_gate_route_sync_region_bytes",
     "moe_max_padded_tokens", "moe_max_tiles",
@@ -30,6 +30,7 @@ EXPORTED = [
 
 MOE_KERNEL_ROUTE, MOE_KERNEL_COUNTS, MOE_KERNEL_SCATTER = 0, 1, 2
 MOE_KERNEL_AUX_FWD, MOE_KERNEL_AUX_BWD, MOE_KERNEL_FRONT_END = 3, 4, 5
+MOE_KERNEL_ROUTE_BWD = 6
 
 
 class MoeError(RuntimeError):
@@ -89,6 +90,8 @@ def _load():
     lib.moe_route_permute.restype = i32
     lib.moe_aux_loss.argtypes = [vp, vp, i64, i64, i32, i32, f32, vp, vp, vp, vp, sz, vp]
     lib.moe_aux_loss.restype = i32
+    lib.moe_route_backward.argtypes = [args_p, vp, vp, vp, vp, vp, vp]
+    lib.moe_route_backward.restype = i32
     lib.rmsnorm_gate_route.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, i32, vp, vp,
                                        vp, vp, sz, vp]
     lib.rmsnorm_gate_route.restype = i32

@@ -534,6 +534,55 @@ moe_status moe_aux_loss(const float* probs, const int32_t* tokens_per_expert, in
   return MOE_OK;
 }
 
+moe_status moe_route_backward(const moe_route_args* args, const void* logits,
+                              const int32_t* topk_ids, const float* grad_weights,
+                              const float* grad_scores, float* grad_logits, hipStream_t stream) {
+  clear_error();
+  if (args == nullptr) return fail(MOE_EINVAL, "args is NULL");
+  const moe_route_args& a = *args;
+  if (a.num_tokens < 0) return fail(MOE_EINVAL, "num_tokens < 0");
+  if (a.num_experts < 1) return fail(MOE_EINVAL, "num_experts < 1");
+  if (a.num_experts > 512) return fail(MOE_EUNSUPPORTED, "num_experts > 512");
+  if (a.top_k < 1 || a.top_k > a.num_experts)
+    return fail(MOE_EINVAL, "top_k must be in [1, num_experts]");
+  if (a.top_k > kMaxTopK) return fail(MOE_EUNSUPPORTED, "top_k > %d", kMaxTopK);
+  if (a.score_fn != MOE_SOFTMAX && a.score_fn != MOE_SIGMOID)
+    return fail(MOE_EINVAL, "score_fn must be MOE_SOFTMAX or MOE_SIGMOID");
+  if (a.logits_dtype != MOE_F32 && a.logits_dtype != MOE_BF16)
+    return fail(MOE_EINVAL, "logits_dtype must be MOE_F32 or MOE_BF16");
+  if (!std::isfinite(a.routed_scaling_factor))
+    return fail(MOE_EINVAL, "routed_scaling_factor is not finite");
+  if (grad_weights == nullptr && grad_scores == nullptr)
+    return fail(MOE_EINVAL, "one of grad_weights / grad_scores is required");
+  if (a.num_tokens == 0) return MOE_OK;
+  if (logits == nullptr || grad_logits == nullptr)
+    return fail(MOE_EINVAL, "logits and grad_logits are required");
+  if (grad_weights != nullptr && topk_ids == nullptr)
+    return fail(MOE_EINVAL, "topk_ids is required with grad_weights");
+  const int esz = a.logits_dtype == MOE_BF16 ? 2 : 4;
+  if (!aligned(logits, esz) || !aligned(grad_logits, 4) || !aligned(grad_scores, 4) ||
+      !aligned(grad_weights, 4) || !aligned(topk_ids, 4))
+    return fail(MOE_EINVAL, "misaligned pointer");
+  moe::RouteBwdParams p{};
+  p.logits = logits;
+  p.ids = topk_ids;
+  p.grad_weights = grad_weights;
+  p.grad_scores = grad_scores;
+  p.grad_logits = grad_logits;
+  p.T = a.num_tokens;
+  p.E = a.num_experts;
+  p.k = a.top_k;
+  p.mode = a.score_fn == MOE_SIGMOID ? moe::kBwdSigmoid
+                                     : (a.use_pre_softmax ? moe::kBwdSoftmaxPre : moe::kBwdSoftmaxPost);
+  p.renorm = a.renormalize != 0;
+  p.scale = a.routed_scaling_factor;
+  hipError_t e = launch_with_profile(MOE_KERNEL_ROUTE_BWD, stream, [&] {
+    return moe::launch_route_backward(p, a.logits_dtype == MOE_BF16, stream);
+  });
+  if (e != hipSuccess) return hip_fail(e, "route_bwd_kernel launch");
+  return MOE_OK;
+}
+
 size_t rmsnorm_gate_route_workspace_size(int32_t T, int32_t H, int32_t E) {
   if (T < 1 || H < 128 || H % 128 || E < 1) return 0;
   return align256(moe::front_end_workspace_bytes(T, H, E));

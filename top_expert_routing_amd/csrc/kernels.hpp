@@ -126,6 +126,21 @@ hipError_t launch_scatter(const ScatterParams& p, int nb, hipStream_t s);
 hipError_t launch_empty_outputs(int32_t* counts, int El, int32_t* padded_offsets, int32_t* total,
                                 int32_t* nctas, hipStream_t s);
 
+// Backward of the routing outputs (see route_backward.hip).
+enum { kBwdSigmoid = 0, kBwdSoftmaxPre = 1, kBwdSoftmaxPost = 2 };
+struct RouteBwdParams {
+  const void* logits;        // [T, E] f32 or bf16
+  const int32_t* ids;        // [T, k] (with grad_weights)
+  const float* grad_weights; // nullable [T, k]
+  const float* grad_scores;  // nullable [T, E]
+  float* grad_logits;        // [T, E]
+  int T, E, k;
+  int mode;                  // kBwd*
+  int renorm;
+  float scale;
+};
+hipError_t launch_route_backward(const RouteBwdParams& p, bool bf16, hipStream_t s);
+
 struct FrontEndParams {
   const void* hidden;
   const void* gamma;

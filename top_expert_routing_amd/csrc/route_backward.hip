@@ -1,0 +1,273 @@
+// gfx950 kernel for the backward of the routing outputs with respect to the
+// router logits (TransformerEngine Fused Router, Description: the fused top-k
+// with score function op and the scores-for-aux-loss op each have a
+// backward).  The gradient is that of the forward with the chosen experts
+// held fixed -- the top-k choice passes no gradient and the expert bias, used
+// only to choose, receives none:
+//
+//   weights  w' = scale * w;  sigmoid: w = s_sel (or s_sel / sum s_sel);
+//            softmax before top-k: w = p_sel (or p_sel / sum p_sel), p over E;
+//            softmax after top-k: w = softmax of the chosen logits
+//   scores   sigmoid: s / sum_E s;  softmax: softmax over E
+//
+//   grad_logits = d/dx ( sum_j g_j w'_j + sum_e h_e scores_e )
+//
+// One wavefront per token (4 per block), lane l holding experts
+// [J l, J l + J): the logits row, the score gradient row and the output row
+// move with one vector access per lane; the chosen experts' weight gradients
+// reach their owner lanes by readlane; per-token sums are wavefront
+// reductions.  HBM-bound: per token it reads the logits row (+ the score
+// gradient row) and k ids and weight gradients, and writes one float32 row.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kBwdThreads = 256;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ float wsum(float v) { return cl_sum<64>(v); }
+__device__ __forceinline__ float wmax(float v) { return cl_max<64>(v); }
+
+// J consecutive elements at p (VEC: one vector access, p aligned to its size)
+template <int J, bool VEC>
+__device__ __forceinline__ void load_f32(const float* p, int n_valid, float (&v)[J]) {
+  if constexpr (VEC && J >= 4) {
+#pragma unroll
+    for (int h = 0; h < J / 4; ++h) {
+      const f32x4 q = reinterpret_cast<const f32x4*>(p)[h];
+      v[4 * h] = q.x; v[4 * h + 1] = q.y; v[4 * h + 2] = q.z; v[4 * h + 3] = q.w;
+    }
+  } else if constexpr (VEC && J == 2) {
+    const float2 q = *reinterpret_cast<const float2*>(p);
+    v[0] = q.x; v[1] = q.y;
+  } else {
+#pragma unroll
+    for (int j = 0; j < J; ++j) v[j] = j < n_valid ? p[j] : 0.0f;
+  }
+}
+
+template <int J, bool VEC>
+__device__ __forceinline__ void load_bf16(const uint16_t* p, int n_valid, float (&v)[J]) {
+  if constexpr (VEC && J == 8) {
+    const u32x4 q = *reinterpret_cast<const u32x4*>(p);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) { v[2 * h] = bf16_lo(w[h]); v[2 * h + 1] = bf16_hi(w[h]); }
+  } else if constexpr (VEC && J == 4) {
+    const uint2 q = *reinterpret_cast<const uint2*>(p);
+    v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
+  } else if constexpr (VEC && J == 2) {
+    const uint32_t q = *reinterpret_cast<const uint32_t*>(p);
+    v[0] = bf16_lo(q); v[1] = bf16_hi(q);
+  } else {
+#pragma unroll
+    for (int j = 0; j < J; ++j) v[j] = j < n_valid ? bf16_bits_to_f32(p[j]) : 0.0f;
+  }
+}
+
+template <int J, bool VEC>
+__device__ __forceinline__ void store_f32(float* p, int n_valid, const float (&v)[J]) {
+  if constexpr (VEC && J >= 4) {
+#pragma unroll
+    for (int h = 0; h < J / 4; ++h)
+      reinterpret_cast<f32x4*>(p)[h] = f32x4{v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]};
+  } else if constexpr (VEC && J == 2) {
+    *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+      if (j < n_valid) p[j] = v[j];
+  }
+}
+
+}  // namespace
+
+template <bool BF16, int J, bool VEC>
+__global__ void __launch_bounds__(kBwdThreads) route_bwd_kernel(RouteBwdParams p) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kBwdThreads / 64) + (threadIdx.x >> 6);
+  if (t >= p.T) return;                                  // whole wavefront leaves together
+  const int E = p.E, k = p.k;
+  const int e0 = J * lane;
+  const int nv = min(J, max(0, E - e0));                 // this lane's experts
+  // every read of the token first
+  float x[J], h[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) { x[j] = 0.0f; h[j] = 0.0f; }
+  if (nv > 0) {                                          // lanes past E read nothing
+    if constexpr (BF16)
+      load_bf16<J, VEC>(static_cast<const uint16_t*>(p.logits) + (size_t)t * E + e0, nv, x);
+    else
+      load_f32<J, VEC>(static_cast<const float*>(p.logits) + (size_t)t * E + e0, nv, x);
+    if (p.grad_scores != nullptr) load_f32<J, VEC>(p.grad_scores + (size_t)t * E + e0, nv, h);
+  }
+  int my_id = -1;
+  float my_g = 0.0f;
+  if (p.grad_weights != nullptr && lane < k) {
+    my_id = p.ids[(size_t)t * k + lane];
+    my_g = p.grad_weights[(size_t)t * k + lane] * p.scale;
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+    if (j >= nv) x[j] = kNegInf;                        // outside E: no softmax mass
+  float dx[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) dx[j] = 0.0f;
+
+  const bool sigmoid = p.mode == kBwdSigmoid;
+  // sigmoid scores s (0 outside E) and their derivative s (1 - s), formed as
+  // e s^2 (e = exp(-x)) where s >= 1/2, so that 1 - s is not a cancellation
+  float s[J], ds[J];
+  if (sigmoid) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const float e = exp_f32(-x[j]);
+      s[j] = j < nv ? __builtin_amdgcn_rcpf(1.0f + e) : 0.0f;
+      ds[j] = j < nv ? (s[j] >= 0.5f ? e * s[j] * s[j] : s[j] * (1.0f - s[j])) : 0.0f;
+    }
+  }
+  float pz[J];                                           // softmax over E (0 outside E)
+  if (!sigmoid && (p.mode == kBwdSoftmaxPre || p.grad_scores != nullptr)) {
+    float m = kNegInf;
+#pragma unroll
+    for (int j = 0; j < J; ++j) m = fmaxf(m, x[j]);
+    m = wmax(m);
+    float z = 0.0f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) { pz[j] = exp_f32(x[j] - m); z += pz[j]; }
+    const float inv = 1.0f / wsum(z);
+#pragma unroll
+    for (int j = 0; j < J; ++j) pz[j] *= inv;
+  }
+
+  if (p.grad_weights != nullptr) {
+    // the chosen experts' scaled weight gradients, at their owner lanes
+    float g[J];
+    uint32_t sel = 0;
+#pragma unroll
+    for (int j = 0; j < J; ++j) g[j] = 0.0f;
+    for (int i = 0; i < k; ++i) {
+      const int e = __builtin_amdgcn_readlane(my_id, i);
+      const float gi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_g), i));
+      if (e >= 0 && e < E && e / J == lane) {
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+          if (e % J == j) { g[j] = gi; sel |= 1u << j; }
+      }
+    }
+    if (sigmoid) {
+      float gs_[J];
+      if (p.renorm) {                                    // w = s / S over the chosen
+        float S = 0.0f, gs = 0.0f;
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+          if ((sel >> j) & 1u) { S += s[j]; gs += g[j] * s[j]; }
+        S = wsum(S);
+        gs = wsum(gs);
+        const float invS = 1.0f / S, c = gs * invS;      // c = sum_j g_j w_j
+#pragma unroll
+        for (int j = 0; j < J; ++j) gs_[j] = (g[j] - c) * invS;
+      } else {
+#pragma unroll
+        for (int j = 0; j < J; ++j) gs_[j] = g[j];
+      }
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+        if ((sel >> j) & 1u) dx[j] += gs_[j] * ds[j];
+    } else if (p.mode == kBwdSoftmaxPre) {
+      float dp[J];
+      if (p.renorm) {                                    // w = p_sel / S
+        float S = 0.0f, gp = 0.0f;
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+          if ((sel >> j) & 1u) { S += pz[j]; gp += g[j] * pz[j]; }
+        S = wsum(S);
+        gp = wsum(gp);
+        const float invS = 1.0f / S, c = gp * invS;
+#pragma unroll
+        for (int j = 0; j < J; ++j) dp[j] = ((sel >> j) & 1u) ? (g[j] - c) * invS : 0.0f;
+      } else {
+#pragma unroll
+        for (int j = 0; j < J; ++j) dp[j] = g[j];         // zero where not chosen
+      }
+      float c2 = 0.0f;                                   // softmax Jacobian, transposed
+#pragma unroll
+      for (int j = 0; j < J; ++j) c2 += pz[j] * dp[j];
+      c2 = wsum(c2);
+#pragma unroll
+      for (int j = 0; j < J; ++j) dx[j] += pz[j] * (dp[j] - c2);
+    } else {                                             // softmax of the chosen logits
+      float ms = kNegInf;
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+        if ((sel >> j) & 1u) ms = fmaxf(ms, x[j]);
+      ms = wmax(ms);
+      float w[J], zs = 0.0f;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        w[j] = ((sel >> j) & 1u) ? exp_f32(x[j] - ms) : 0.0f;
+        zs += w[j];
+      }
+      const float invz = 1.0f / wsum(zs);
+      float c = 0.0f;
+#pragma unroll
+      for (int j = 0; j < J; ++j) { w[j] *= invz; c += w[j] * g[j]; }
+      c = wsum(c);
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+        if ((sel >> j) & 1u) dx[j] += w[j] * (g[j] - c);
+    }
+  }
+
+  if (p.grad_scores != nullptr) {
+    if (sigmoid) {                                       // q = s / sum_E s
+      float Z = 0.0f;
+#pragma unroll
+      for (int j = 0; j < J; ++j) Z += s[j];
+      Z = wsum(Z);
+      const float invZ = 1.0f / Z;
+      float c = 0.0f;
+#pragma unroll
+      for (int j = 0; j < J; ++j) c += h[j] * s[j];
+      c = wsum(c) * invZ;                                // sum_e h_e q_e
+#pragma unroll
+      for (int j = 0; j < J; ++j) dx[j] += ds[j] * (h[j] - c) * invZ;
+    } else {                                             // q = softmax over E
+      float c = 0.0f;
+#pragma unroll
+      for (int j = 0; j < J; ++j) c += h[j] * pz[j];
+      c = wsum(c);
+#pragma unroll
+      for (int j = 0; j < J; ++j) dx[j] += pz[j] * (h[j] - c);
+    }
+  }
+  if (nv > 0) store_f32<J, VEC>(p.grad_logits + (size_t)t * E + e0, nv, dx);
+}
+
+template <bool BF16, int J>
+static hipError_t launch_bwd_j(const RouteBwdParams& p, bool vec, hipStream_t s) {
+  const dim3 grid((p.T + kBwdThreads / 64 - 1) / (kBwdThreads / 64));
+  if (vec) MOE_LAUNCH((route_bwd_kernel<BF16, J, true>), grid, dim3(kBwdThreads), 0, s, p);
+  else MOE_LAUNCH((route_bwd_kernel<BF16, J, false>), grid, dim3(kBwdThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_backward(const RouteBwdParams& p, bool bf16, hipStream_t s) {
+  const int J = p.E <= 64 ? 1 : p.E <= 128 ? 2 : p.E <= 256 ? 4 : 8;   // E <= 512
+  // vector accesses when every lane's J elements are whole and aligned
+  const int esz = bf16 ? 2 : 4;
+  const bool vec = J > 1 && p.E % J == 0 &&
+                   (uintptr_t)p.logits % (J * esz) == 0 && (uintptr_t)p.grad_logits % (J * 4) == 0 &&
+                   (p.grad_scores == nullptr || (uintptr_t)p.grad_scores % (J * 4) == 0);
+  switch (J) {
+    case 1: return bf16 ? launch_bwd_j<true, 1>(p, false, s) : launch_bwd_j<false, 1>(p, false, s);
+    case 2: return bf16 ? launch_bwd_j<true, 2>(p, vec, s) : launch_bwd_j<false, 2>(p, vec, s);
+    case 4: return bf16 ? launch_bwd_j<true, 4>(p, vec, s) : launch_bwd_j<false, 4>(p, vec, s);
+    default: return bf16 ? launch_bwd_j<true, 8>(p, vec, s) : launch_bwd_j<false, 8>(p, vec, s);
+  }
+}
+
+}  // namespace moe
