@@ -182,6 +182,31 @@ def other_configs(mr, torch, np, dev, rotate_mb, K):
         res[name] = entry
         del sets, o0
 
+    # backward of the routing outputs (DeepSeek-V3-like: weights gradient;
+    # Qwen-like: weights and full-E scores gradients), cold like the rest
+    for name, with_s in (("deepseek_v3_like", False), ("qwen_moe_like", True)):
+        w = WORKLOADS[name]
+        logits, _ = route_inputs(w)
+        x0 = dev_logits(w, logits)
+        args = mr.make_route_args(w.T, w.E, w.k, score_fn=w.score_fn, pre_softmax=w.pre_softmax,
+                                  renorm=w.renorm, scale=w.scale, logits_dtype=w.logits_dtype)
+        gen = torch.Generator(device="cpu").manual_seed(w.seed + 1)
+        ids0 = torch.randint(0, w.E, (w.T, w.k), generator=gen, dtype=torch.int32).to(dev)
+        gw0 = torch.randn((w.T, w.k), generator=gen, dtype=torch.float32).to(dev)
+        gs0 = torch.randn((w.T, w.E), generator=gen, dtype=torch.float32).to(dev) if with_s else None
+        set_b = (x0.numel() * x0.element_size() + ids0.numel() * 4 + gw0.numel() * 4 +
+                 (gs0.numel() * 4 if with_s else 0) + w.T * w.E * 4)
+        R = n_sets(set_b, rotate_mb)
+        bsets = [(x0.clone(), ids0.clone(), gw0.clone(), None if gs0 is None else gs0.clone(),
+                  torch.empty((w.T, w.E), dtype=torch.float32, device=dev)) for _ in range(R)]
+        ms = graph_ms(torch, lambda i: mr.moe_route_backward(args, *bsets[i % R]), K)
+        res[name + "_backward"] = {
+            "workload": w.description + ("; grad of weights and scores" if with_s else
+                                         "; grad of weights") + " -> grad of logits",
+            "us_per_call": ms * 1e3, "algorithmic_bytes": set_b,
+            "gbs": set_b / (ms * 1e-3) / 1e9, "buffer_sets": R}
+        del bsets
+
     f = FRONT_END
     hidden, gamma, W, _ = front_end_inputs(f)
     def bf(a):

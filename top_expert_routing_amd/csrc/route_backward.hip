@@ -12,9 +12,9 @@
 //
 //   grad_logits = d/dx ( sum_j g_j w'_j + sum_e h_e scores_e )
 //
-// One wavefront per token (4 per block), lane l holding experts
-// [J l, J l + J): the logits row, the score gradient row and the output row
-// move with one vector access per lane; the chosen experts' weight gradients
+// Four tokens per wavefront, their inputs requested together; lane l holds
+// experts [J l, J l + J): the logits row, the score gradient row and the
+// output row move with one vector access per lane; the chosen experts' weight gradients
 // reach their owner lanes by readlane; per-token sums are wavefront
 // reductions.  HBM-bound: per token it reads the logits row (+ the score
 // gradient row) and k ids and weight gradients, and writes one float32 row.
@@ -26,6 +26,7 @@ namespace moe {
 namespace {
 
 constexpr int kBwdThreads = 256;
+constexpr int kBwdTokens = 1;       // tokens per wavefront
 constexpr float kNegInf = -__builtin_huge_valf();
 
 __device__ __forceinline__ float wsum(float v) { return cl_sum<64>(v); }
@@ -73,7 +74,8 @@ __device__ __forceinline__ void store_f32(float* p, int n_valid, const float (&v
   if constexpr (VEC && J >= 4) {
 #pragma unroll
     for (int h = 0; h < J / 4; ++h)
-      reinterpret_cast<f32x4*>(p)[h] = f32x4{v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]};
+      __builtin_nontemporal_store(f32x4{v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]},
+                                  reinterpret_cast<f32x4*>(p) + h);
   } else if constexpr (VEC && J == 2) {
     *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
   } else {
@@ -85,18 +87,17 @@ __device__ __forceinline__ void store_f32(float* p, int n_valid, const float (&v
 
 }  // namespace
 
+// One token's inputs, read before any token of the wavefront is computed.
 template <bool BF16, int J, bool VEC>
-__global__ void __launch_bounds__(kBwdThreads) route_bwd_kernel(RouteBwdParams p) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * (kBwdThreads / 64) + (threadIdx.x >> 6);
-  if (t >= p.T) return;                                  // whole wavefront leaves together
-  const int E = p.E, k = p.k;
-  const int e0 = J * lane;
-  const int nv = min(J, max(0, E - e0));                 // this lane's experts
-  // every read of the token first
-  float x[J], h[J];
+__device__ __forceinline__ void load_token(const RouteBwdParams& p, int t, int lane, int e0, int nv,
+                                           float (&x)[J], float (&h)[J], int& my_id,
+                                           float& my_g) {
 #pragma unroll
   for (int j = 0; j < J; ++j) { x[j] = 0.0f; h[j] = 0.0f; }
+  my_id = -1;
+  my_g = 0.0f;
+  if (t >= p.T) return;
+  const int E = p.E, k = p.k;
   if (nv > 0) {                                          // lanes past E read nothing
     if constexpr (BF16)
       load_bf16<J, VEC>(static_cast<const uint16_t*>(p.logits) + (size_t)t * E + e0, nv, x);
@@ -104,12 +105,18 @@ __global__ void __launch_bounds__(kBwdThreads) route_bwd_kernel(RouteBwdParams p
       load_f32<J, VEC>(static_cast<const float*>(p.logits) + (size_t)t * E + e0, nv, x);
     if (p.grad_scores != nullptr) load_f32<J, VEC>(p.grad_scores + (size_t)t * E + e0, nv, h);
   }
-  int my_id = -1;
-  float my_g = 0.0f;
   if (p.grad_weights != nullptr && lane < k) {
     my_id = p.ids[(size_t)t * k + lane];
     my_g = p.grad_weights[(size_t)t * k + lane] * p.scale;
   }
+}
+
+// One token's gradient row, from its inputs; stored with streaming stores.
+template <int J, bool VEC>
+__device__ __forceinline__ void token_grad(const RouteBwdParams& p, int t, int lane, int e0, int nv,
+                                           float (&x)[J], const float (&h)[J], int my_id,
+                                           float my_g) {
+  const int E = p.E, k = p.k;
 #pragma unroll
   for (int j = 0; j < J; ++j)
     if (j >= nv) x[j] = kNegInf;                        // outside E: no softmax mass
@@ -247,9 +254,29 @@ __global__ void __launch_bounds__(kBwdThreads) route_bwd_kernel(RouteBwdParams p
   if (nv > 0) store_f32<J, VEC>(p.grad_logits + (size_t)t * E + e0, nv, dx);
 }
 
+// Wavefront w of block b: tokens [kBwdTokens (4 b + w), +kBwdTokens), all of
+// their inputs requested before the first is computed.
+template <bool BF16, int J, bool VEC>
+__global__ void __launch_bounds__(kBwdThreads) route_bwd_kernel(RouteBwdParams p) {
+  const int lane = threadIdx.x & 63;
+  const int t0 = (blockIdx.x * (kBwdThreads / 64) + (threadIdx.x >> 6)) * kBwdTokens;
+  if (t0 >= p.T) return;                                 // whole wavefront leaves together
+  const int e0 = J * lane;
+  const int nv = min(J, max(0, p.E - e0));               // this lane's experts
+  float x[kBwdTokens][J], h[kBwdTokens][J], g[kBwdTokens];
+  int id[kBwdTokens];
+#pragma unroll
+  for (int u = 0; u < kBwdTokens; ++u)
+    load_token<BF16, J, VEC>(p, t0 + u, lane, e0, nv, x[u], h[u], id[u], g[u]);
+#pragma unroll
+  for (int u = 0; u < kBwdTokens; ++u)
+    if (t0 + u < p.T) token_grad<J, VEC>(p, t0 + u, lane, e0, nv, x[u], h[u], id[u], g[u]);
+}
+
 template <bool BF16, int J>
 static hipError_t launch_bwd_j(const RouteBwdParams& p, bool vec, hipStream_t s) {
-  const dim3 grid((p.T + kBwdThreads / 64 - 1) / (kBwdThreads / 64));
+  const int per_block = kBwdThreads / 64 * kBwdTokens;
+  const dim3 grid((p.T + per_block - 1) / per_block);
   if (vec) MOE_LAUNCH((route_bwd_kernel<BF16, J, true>), grid, dim3(kBwdThreads), 0, s, p);
   else MOE_LAUNCH((route_bwd_kernel<BF16, J, false>), grid, dim3(kBwdThreads), 0, s, p);
   return hipGetLastError();
