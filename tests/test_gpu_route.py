@@ -101,6 +101,8 @@ SMALL = [
     (16, 3, "sigmoid", False, 4, 1, 1, False, 1.0, "bf16", 0.05),
     (32, 4, "softmax", True, 0, 0, 2, True, 1.0, "bf16", 0.1),      # pre-softmax with bias
     (32, 4, "softmax", False, 4, 2, 2, True, 1.0, "f32", 0.1),      # grouped softmax
+    (64, 4, "softmax", True, 8, 2, 2, True, 1.0, "bf16", None),     # softmax, group-masked, top-k
+    (128, 6, "softmax", True, 8, 3, 1, False, 1.0, "f32", None),    # same, group max, no renorm
     (64, 6, "sigmoid", False, 8, 3, 2, True, 1.5, "bf16", 0.01),
     (60, 4, "softmax", True, 0, 0, 2, True, 1.0, "bf16", None),     # ragged rows, no vec loads
     (100, 5, "sigmoid", False, 0, 0, 2, False, 1.0, "f32", 0.02),

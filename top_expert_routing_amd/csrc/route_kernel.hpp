@@ -383,9 +383,14 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>) route_kernel(RouteParams p) 
   }
 
   const bool refine = !p.grouped && k <= 4 * LPT && k > 2;
+  // softmax before top-k without a bias keys on the logits themselves (the
+  // same order as the probabilities), but a group score sums probabilities:
+  // grouped, it needs the token maximum m to form exp(x - m)
+  const bool group_exp = VAR == kVarSoftmax && pre && p.grouped && p.topn > 1;
   const bool need_ms =
       VAR == kVarSigmoid ? false
-                         : ((VAR == kVarSoftmax ? (pre && !p.renorm) : pre) || p.scores != nullptr);
+                         : ((VAR == kVarSoftmax ? (pre && !p.renorm) : pre) || p.scores != nullptr ||
+                            group_exp);
   const int mode = (VAR == kVarSigmoid || (VAR == kVarSoftmaxBias && pre))
                        ? kEmitPlain
                        : ((VAR == kVarSoftmax && pre && !p.renorm) ? kEmitExactPre : kEmitSoftSel);
@@ -487,7 +492,11 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>) route_kernel(RouteParams p) 
         g1 = fmaxf(g1, a1);
         g2 = n2;
       }
-      const float gs = p.topn == 1 ? g1 : g1 + g2;
+      // (softmax before top-k, keys = logits: the sum of the two largest
+      // probabilities orders like exp(g1 - m) + exp(g2 - m), the common
+      // normaliser dropped)
+      const float gs = p.topn == 1 ? g1
+                                   : (group_exp ? exp_f32(g1 - m) + exp_f32(g2 - m) : g1 + g2);
       const int myg = lane_c >> p.lg_shift;
       // group order as packed (score, group) words: slots n_group..LPT-1 hold 0
       const uint64_t gk = pack_key(gs, myg);
