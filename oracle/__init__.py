@@ -24,6 +24,7 @@ permutation  tile-padded per-expert offsets, expanded->permuted and
 aux_loss     load-balancing loss forward and backward
 front_end    RMSNorm -> router projection -> top-k on raw logits -> activation
 backward     gradient of the routing weights and aux-loss scores w.r.t. logits
+dispatch     token rows into permuted (expert) order and the weighted combine back
 
 Parity pins: every function here is pinned by ``tests/test_oracle_*.py`` against
 closed forms, invariants, brute force on tiny inputs or library routines; see
@@ -34,11 +35,12 @@ from .permutation import permute, PermuteResult, max_padded_tokens, max_tiles
 from .aux_loss import aux_loss_fwd, aux_loss_bwd
 from .front_end import rmsnorm, front_end_route, bf16_round_bits, FrontEndResult
 from .backward import route_backward
+from .dispatch import dispatch, combine
 
 __all__ = [
     "route", "RouteResult", "decode_input", "selection_keys32", "exact_keys64",
     "permute", "PermuteResult", "max_padded_tokens", "max_tiles",
     "aux_loss_fwd", "aux_loss_bwd",
     "rmsnorm", "front_end_route", "bf16_round_bits", "FrontEndResult",
-    "route_backward",
+    "route_backward", "dispatch", "combine",
 ]

@@ -10,6 +10,7 @@ import pytest
 import oracle
 import test_oracle_aux_front as T_AF
 import test_oracle_backward as T_B
+import test_oracle_dispatch as T_D
 import test_oracle_golden as T_G
 import test_oracle_permutation as T_P
 import test_oracle_routing as T_R
@@ -26,6 +27,8 @@ PINS = [
     T_G.pin_golden_routing, T_G.pin_golden_permutation, T_G.pin_golden_aux_loss,
     T_G.pin_golden_rmsnorm,
     T_B.pin_backward_finite_differences, T_B.pin_backward_invariants,
+    T_D.pin_dispatch_rows, T_D.pin_combine_inverts_dispatch, T_D.pin_combine_one_hot_and_linearity,
+    T_D.pin_combine_local_shard_and_example,
 ]
 
 # (module, text in the oracle, planted replacement, what the mistake is)
@@ -95,6 +98,14 @@ MUTATIONS = [
     ("backward", "            np.add.at(grad, (rows, ids), w * (g - c))",
      "            np.add.at(grad, (rows, ids[:, ::-1]), w * (g - c))",
      "backward: gradient scattered to the chosen experts in reverse order"),
+    ("dispatch", "    out[routed] = hidden[p2t[routed]]", "    out[:] = hidden[np.maximum(p2t, 0)]",
+     "dispatch: padding slots copy token 0 instead of zeros"),
+    ("dispatch", "        out[ok] += w[ok, j, None] * y[slot[ok]]", "        out[ok] += y[slot[ok]]",
+     "combine: routing weights ignored"),
+    ("dispatch", "        ok = slot >= 0", "        ok = slot >= -1",
+     "combine: a non-local choice reads the last row"),
+    ("dispatch", "        out[ok] += w[ok, j, None] * y[slot[ok]]", "        out[ok] += w[ok, k - 1 - j, None] * y[slot[ok]]",
+     "combine: weights paired with the wrong choice"),
 ]
 
 
