@@ -251,6 +251,39 @@ moe_status moe_route_backward(const moe_route_args* args, const void* logits,
                               const int32_t* topk_ids, const float* grad_weights,
                               const float* grad_scores, float* grad_logits, hipStream_t stream);
 
+/* Token dispatch and combine either side of the grouped expert GEMM ([LMD]
+ * Description: dispatch sends tokens to expert buffers by the routing
+ * decision, combine returns expert outputs to token order with the routing
+ * scales).  The pages give names and signatures only; the plainest reading in
+ * moe_route_permute's own maps ([FI] Returns):
+ *
+ *   moe_dispatch:  permuted_hidden[p, :] = hidden[permuted_idx_to_token_idx[p], :]
+ *                  for p < *total_num_padded_tokens (a bit copy), a zero row
+ *                  where the slot is padding (-1); rows past the total are not
+ *                  written.
+ *   moe_combine:   out[t, :] = sum_j topk_weights[t, j]
+ *                              * expert_out[expanded_idx_to_permuted_idx[t*k + j], :]
+ *                  summed in choice order in float32 and rounded once to dtype
+ *                  (bfloat16: nearest even); a choice whose index is -1 (an
+ *                  expert outside the local range) adds nothing.
+ *
+ * dtype            MOE_F32 or MOE_BF16 for hidden / permuted_hidden /
+ *                  expert_out / out; topk_weights are weights_dtype (MOE_F32 or
+ *                  MOE_BF16), as moe_route_permute wrote them.
+ * T, H             tokens and hidden size (H >= 1); top_k in [1, 64].
+ * permuted_idx_to_token_idx, total_num_padded_tokens: device outputs of
+ *                  moe_route_permute; max_padded_tokens = the rows of
+ *                  permuted_hidden (moe_max_padded_tokens()).
+ * No workspace.  Rows move with 16-byte accesses when rows and pointers are
+ * 16-byte aligned, element by element otherwise. */
+moe_status moe_dispatch(const void* hidden, int32_t dtype, int32_t T, int32_t H,
+                        const int32_t* permuted_idx_to_token_idx,
+                        const int32_t* total_num_padded_tokens, int64_t max_padded_tokens,
+                        void* permuted_hidden, hipStream_t stream);
+moe_status moe_combine(const void* expert_out, int32_t dtype, int32_t T, int32_t H, int32_t top_k,
+                       const int32_t* expanded_idx_to_permuted_idx, const void* topk_weights,
+                       int32_t weights_dtype, void* out, hipStream_t stream);
+
 /* Fused decode front end ([NKI] rmsnorm_router_topk_a2av: Background,
  * Parameters, Returns, Notes):
  *
@@ -319,7 +352,9 @@ typedef enum moe_kernel_kind {
   MOE_KERNEL_AUX_BWD = 4,
   MOE_KERNEL_FRONT_END = 5,
   MOE_KERNEL_ROUTE_BWD = 6,
-  MOE_KERNEL_KINDS = 7
+  MOE_KERNEL_DISPATCH = 7,
+  MOE_KERNEL_COMBINE = 8,
+  MOE_KERNEL_KINDS = 9
 } moe_kernel_kind;
 moe_status moe_profile_begin(void);
 moe_status moe_profile_end(void);

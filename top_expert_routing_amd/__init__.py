@@ -22,10 +22,12 @@ from ._lib import (MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHI
                    MOE_F32, MOE_BF16, MOE_F16, MOE_SOFTMAX, MOE_SIGMOID, MoeError,
                    moe_route_args, LIB_PATH, MOE_KERNEL_ROUTE, MOE_KERNEL_COUNTS,
                    MOE_KERNEL_SCATTER, MOE_KERNEL_AUX_FWD, MOE_KERNEL_AUX_BWD,
-                   MOE_KERNEL_FRONT_END, MOE_KERNEL_ROUTE_BWD)
+                   MOE_KERNEL_FRONT_END, MOE_KERNEL_ROUTE_BWD,
+                   MOE_KERNEL_DISPATCH, MOE_KERNEL_COMBINE)
 
 __all__ = [
     "moe_route", "moe_route_permute", "moe_aux_loss", "rmsnorm_gate_route", "moe_route_backward",
+    "moe_dispatch", "moe_combine",
     "moe_route_workspace_size", "moe_route_count_region_bytes", "moe_aux_loss_workspace_size",
     "moe_profile_begin", "moe_profile_end", "moe_profile_read",
     "rmsnorm_gate_route_workspace_size", "rmsnorm_gate_route_sync_region_bytes",
@@ -116,6 +118,21 @@ def moe_route_backward(args: moe_route_args, logits, topk_ids, grad_weights, gra
     _check(_lib.lib.moe_route_backward(ctypes.byref(args), _ptr(logits), _ptr(topk_ids),
                                        _ptr(grad_weights), _ptr(grad_scores), _ptr(grad_logits),
                                        _stream(stream)))
+
+
+def moe_dispatch(hidden, dtype: int, T: int, H: int, permuted_idx_to_token_idx,
+                 total_num_padded_tokens, max_padded_tokens: int, permuted_hidden,
+                 stream=None) -> None:
+    _check(_lib.lib.moe_dispatch(_ptr(hidden), dtype, T, H, _ptr(permuted_idx_to_token_idx),
+                                 _ptr(total_num_padded_tokens), ctypes.c_int64(max_padded_tokens),
+                                 _ptr(permuted_hidden), _stream(stream)))
+
+
+def moe_combine(expert_out, dtype: int, T: int, H: int, top_k: int, expanded_idx_to_permuted_idx,
+                topk_weights, weights_dtype: int, out, stream=None) -> None:
+    _check(_lib.lib.moe_combine(_ptr(expert_out), dtype, T, H, top_k,
+                                _ptr(expanded_idx_to_permuted_idx), _ptr(topk_weights),
+                                weights_dtype, _ptr(out), _stream(stream)))
 
 
 def rmsnorm_gate_route(hidden, gamma, router_weights, router_bias, dtype: int, T: int, H: int,

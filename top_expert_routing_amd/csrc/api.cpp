@@ -583,6 +583,50 @@ moe_status moe_route_backward(const moe_route_args* args, const void* logits,
   return MOE_OK;
 }
 
+moe_status moe_dispatch(const void* hidden, int32_t dtype, int32_t T, int32_t H,
+                        const int32_t* p2t, const int32_t* total, int64_t max_padded, void* out,
+                        hipStream_t stream) {
+  clear_error();
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return fail(MOE_EINVAL, "dtype must be MOE_F32 or MOE_BF16");
+  if (T < 0 || H < 1 || max_padded < 0) return fail(MOE_EINVAL, "T >= 0, H >= 1, max_padded_tokens >= 0");
+  if (T == 0 || max_padded == 0) return MOE_OK;
+  if (hidden == nullptr || p2t == nullptr || total == nullptr || out == nullptr)
+    return fail(MOE_EINVAL, "a required pointer is NULL");
+  const int esz = dtype == MOE_BF16 ? 2 : 4;
+  if (!aligned(hidden, esz) || !aligned(out, esz) || !aligned(p2t, 4) || !aligned(total, 4))
+    return fail(MOE_EINVAL, "misaligned pointer");
+  hipError_t e = launch_with_profile(MOE_KERNEL_DISPATCH, stream, [&] {
+    return moe::launch_dispatch(hidden, (int64_t)H * esz, p2t, total, max_padded, out, stream);
+  });
+  if (e != hipSuccess) return hip_fail(e, "dispatch_kernel launch");
+  return MOE_OK;
+}
+
+moe_status moe_combine(const void* expert_out, int32_t dtype, int32_t T, int32_t H, int32_t top_k,
+                       const int32_t* e2p, const void* weights, int32_t weights_dtype, void* out,
+                       hipStream_t stream) {
+  clear_error();
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return fail(MOE_EINVAL, "dtype must be MOE_F32 or MOE_BF16");
+  if (weights_dtype != MOE_F32 && weights_dtype != MOE_BF16)
+    return fail(MOE_EINVAL, "weights_dtype must be MOE_F32 or MOE_BF16");
+  if (T < 0 || H < 1) return fail(MOE_EINVAL, "T >= 0 and H >= 1");
+  if (top_k < 1) return fail(MOE_EINVAL, "top_k >= 1");
+  if (top_k > kMaxTopK) return fail(MOE_EUNSUPPORTED, "top_k > %d", kMaxTopK);
+  if (T == 0) return MOE_OK;
+  if (expert_out == nullptr || e2p == nullptr || weights == nullptr || out == nullptr)
+    return fail(MOE_EINVAL, "a required pointer is NULL");
+  const int esz = dtype == MOE_BF16 ? 2 : 4;
+  if (!aligned(expert_out, esz) || !aligned(out, esz) || !aligned(e2p, 4) ||
+      !aligned(weights, weights_dtype == MOE_BF16 ? 2 : 4))
+    return fail(MOE_EINVAL, "misaligned pointer");
+  hipError_t e = launch_with_profile(MOE_KERNEL_COMBINE, stream, [&] {
+    return moe::launch_combine(expert_out, dtype == MOE_BF16, T, H, top_k, e2p, weights,
+                               weights_dtype == MOE_BF16, out, stream);
+  });
+  if (e != hipSuccess) return hip_fail(e, "combine_kernel launch");
+  return MOE_OK;
+}
+
 size_t rmsnorm_gate_route_workspace_size(int32_t T, int32_t H, int32_t E) {
   if (T < 1 || H < 128 || H % 128 || E < 1) return 0;
   return align256(moe::front_end_workspace_bytes(T, H, E));

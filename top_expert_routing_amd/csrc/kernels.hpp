@@ -141,6 +141,12 @@ struct RouteBwdParams {
 };
 hipError_t launch_route_backward(const RouteBwdParams& p, bool bf16, hipStream_t s);
 
+// Token dispatch / combine (see dispatch.hip).
+hipError_t launch_dispatch(const void* hidden, int64_t row_bytes, const int32_t* p2t,
+                           const int32_t* total, int64_t max_rows, void* out, hipStream_t s);
+hipError_t launch_combine(const void* expert_out, bool bf16, int T, int H, int k, const int32_t* e2p,
+                          const void* weights, bool w_bf16, void* out, hipStream_t s);
+
 struct FrontEndParams {
   const void* hidden;
   const void* gamma;
