@@ -207,6 +207,45 @@ def other_configs(mr, torch, np, dev, rotate_mb, K):
             "gbs": set_b / (ms * 1e-3) / 1e9, "buffer_sets": R}
         del bsets
 
+    # token dispatch and combine around the expert GEMM, DeepSeek-V3-like route
+    # at the front end's hidden size (7168, bf16), rows of synthetic N(0,1)
+    w = WORKLOADS["deepseek_v3_like"]
+    logits, bias = route_inputs(w)
+    x0 = dev_logits(w, logits)
+    b0 = torch.from_numpy(bias).to(dev)
+    args = mr.make_route_args(w.T, w.E, w.k, score_fn=w.score_fn, n_group=w.n_group,
+                              topk_group=w.topk_group, group_topn=w.group_topn, renorm=w.renorm,
+                              scale=w.scale, logits_dtype=w.logits_dtype, bias_dtype=w.bias_dtype)
+    o = mr.alloc_route_outputs(args, dev, permute=True, tile=w.tile)
+    mr.route_permute(args, x0, b0, tile=w.tile, out=o)
+    torch.cuda.synchronize()
+    H = FRONT_END.H
+    total = int(o.total_num_padded_tokens.item())
+    max_rows = o.permuted_idx_to_token_idx.numel()
+    gen = torch.Generator(device="cpu").manual_seed(w.seed + 2)
+    hid0 = torch.randn((w.T, H), generator=gen).to(torch.bfloat16).to(dev)
+    d_bytes = total * H * 2 + w.T * w.k * H * 2 + total * 4          # rows written + read, p2t
+    c_bytes = w.T * w.k * H * 2 + w.T * H * 2 + w.T * w.k * 8        # rows read + written, maps
+    R = n_sets(max_rows * H * 2 + w.T * H * 2, rotate_mb)
+    dsets = [(hid0 if r == 0 else hid0.clone(),
+              torch.empty((max_rows, H), dtype=torch.bfloat16, device=dev)) for r in range(R)]
+    ms_d = graph_ms(torch, lambda i: mr.moe_dispatch(
+        dsets[i % R][0], mr.MOE_BF16, w.T, H, o.permuted_idx_to_token_idx,
+        o.total_num_padded_tokens, max_rows, dsets[i % R][1]), K)
+    csets = [(ds[1], torch.empty((w.T, H), dtype=torch.bfloat16, device=dev)) for ds in dsets]
+    ms_c = graph_ms(torch, lambda i: mr.moe_combine(
+        csets[i % R][0], mr.MOE_BF16, w.T, H, w.k, o.expanded_idx_to_permuted_idx, o.topk_weights,
+        mr.MOE_F32, csets[i % R][1]), K)
+    res["deepseek_v3_like_dispatch"] = {
+        "workload": f"{w.description}; hidden [{w.T},{H}] bf16 rows into {total} permuted rows",
+        "us_per_call": ms_d * 1e3, "algorithmic_bytes": d_bytes, "gbs": d_bytes / (ms_d * 1e-3) / 1e9,
+        "buffer_sets": R}
+    res["deepseek_v3_like_combine"] = {
+        "workload": f"{w.description}; {w.k} weighted expert rows per token back to [{w.T},{H}] bf16",
+        "us_per_call": ms_c * 1e3, "algorithmic_bytes": c_bytes, "gbs": c_bytes / (ms_c * 1e-3) / 1e9,
+        "buffer_sets": R}
+    del dsets, csets, o
+
     f = FRONT_END
     hidden, gamma, W, _ = front_end_inputs(f)
     def bf(a):

@@ -202,3 +202,21 @@ def test_route_backward_validation():
     # T = 0 is valid and launches nothing, even with placeholder pointers
     empty = mr.make_route_args(0, 16, 2)
     assert B(ctypes.byref(empty), None, None, None, FAKE, None, None) == mr.MOE_OK
+
+
+def test_dispatch_combine_validation():
+    D, C = _lib.lib.moe_dispatch, _lib.lib.moe_combine
+    i64 = ctypes.c_int64
+    # every call below fails on the host, before anything is launched
+    assert D(FAKE, mr.MOE_F16, 10, 64, FAKE, FAKE, i64(100), FAKE, None) == mr.MOE_EINVAL
+    assert D(FAKE, mr.MOE_BF16, 10, 0, FAKE, FAKE, i64(100), FAKE, None) == mr.MOE_EINVAL
+    assert D(None, mr.MOE_BF16, 10, 64, FAKE, FAKE, i64(100), FAKE, None) == mr.MOE_EINVAL
+    assert D(FAKE, mr.MOE_BF16, 10, 64, FAKE, None, i64(100), FAKE, None) == mr.MOE_EINVAL
+    assert D(ctypes.c_void_p(0x1001), mr.MOE_BF16, 10, 64, FAKE, FAKE, i64(100), FAKE, None) == mr.MOE_EINVAL
+    assert D(FAKE, mr.MOE_BF16, 0, 64, None, None, i64(0), None, None) == mr.MOE_OK   # nothing to do
+    assert C(FAKE, mr.MOE_BF16, 10, 64, 0, FAKE, FAKE, mr.MOE_F32, FAKE, None) == mr.MOE_EINVAL
+    assert C(FAKE, mr.MOE_BF16, 10, 64, 65, FAKE, FAKE, mr.MOE_F32, FAKE, None) == mr.MOE_EUNSUPPORTED
+    assert C(FAKE, mr.MOE_BF16, 10, 64, 8, FAKE, FAKE, mr.MOE_F16, FAKE, None) == mr.MOE_EINVAL
+    assert C(FAKE, mr.MOE_BF16, 10, 64, 8, None, FAKE, mr.MOE_F32, FAKE, None) == mr.MOE_EINVAL
+    assert C(FAKE, mr.MOE_F32, 10, 64, 8, FAKE, ctypes.c_void_p(0x1002), mr.MOE_F32, FAKE, None) == mr.MOE_EINVAL
+    assert C(None, mr.MOE_BF16, 0, 64, 8, None, None, mr.MOE_F32, None, None) == mr.MOE_OK
