@@ -88,52 +88,65 @@ __global__ void __launch_bounds__(kMoveThreads)
   constexpr int EPL = BF16 ? 8 : 4;                     // elements per lane per slab
   constexpr int kMaxK = 64;
   if constexpr (VEC) {
-    for (int c0 = 0; c0 < H; c0 += 64 * EPL) {
-      const int c = c0 + lane * EPL;
-      float acc[EPL];
+    constexpr int kSlabs = 2;                           // slabs whose rows are requested together
+    for (int c0 = 0; c0 < H; c0 += kSlabs * 64 * EPL) {
+      float acc[kSlabs][EPL];
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) acc[i] = 0.0f;
-      // the k rows of this slab, eight requested at a time, summed in choice order
+      for (int sl = 0; sl < kSlabs; ++sl)
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) acc[sl][i] = 0.0f;
+      // the k rows of these slabs, eight choices requested at a time, summed
+      // in choice order
       for (int j0 = 0; j0 < k; j0 += 8) {
-        u32x4 r[8];
+        u32x4 r[kSlabs][8];
         float wj[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int j = j0 + u < kMaxK ? j0 + u : 0;
           const int slot = __builtin_amdgcn_readlane(my_slot, j);
-          wj[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), j));
-          const bool use = j0 + u < k && slot >= 0 && c < H;
-          const size_t off = (size_t)slot * H + c;
-          r[u] = use ? (BF16 ? *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(expert_out) + off)
-                             : *reinterpret_cast<const u32x4*>(static_cast<const float*>(expert_out) + off))
-                     : u32x4{0, 0, 0, 0};
-          if (!(j0 + u < k && slot >= 0)) wj[u] = 0.0f;
-        }
+          const bool live = j0 + u < k && slot >= 0;
+          wj[u] = live ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), j)) : 0.0f;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          if constexpr (BF16) {
-            const uint32_t wv[4] = {r[u].x, r[u].y, r[u].z, r[u].w};
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-              acc[2 * h] += wj[u] * bf16_lo(wv[h]);
-              acc[2 * h + 1] += wj[u] * bf16_hi(wv[h]);
-            }
-          } else {
-            acc[0] += wj[u] * __uint_as_float(r[u].x);
-            acc[1] += wj[u] * __uint_as_float(r[u].y);
-            acc[2] += wj[u] * __uint_as_float(r[u].z);
-            acc[3] += wj[u] * __uint_as_float(r[u].w);
+          for (int sl = 0; sl < kSlabs; ++sl) {
+            const int c = c0 + sl * 64 * EPL + lane * EPL;
+            const size_t off = (size_t)slot * H + c;
+            r[sl][u] = (live && c < H)
+                           ? __builtin_nontemporal_load(
+                                 BF16 ? reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(expert_out) + off)
+                                      : reinterpret_cast<const u32x4*>(static_cast<const float*>(expert_out) + off))
+                           : u32x4{0, 0, 0, 0};
           }
         }
+#pragma unroll
+        for (int sl = 0; sl < kSlabs; ++sl)
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            if constexpr (BF16) {
+              const uint32_t wv[4] = {r[sl][u].x, r[sl][u].y, r[sl][u].z, r[sl][u].w};
+#pragma unroll
+              for (int h = 0; h < 4; ++h) {
+                acc[sl][2 * h] += wj[u] * bf16_lo(wv[h]);
+                acc[sl][2 * h + 1] += wj[u] * bf16_hi(wv[h]);
+              }
+            } else {
+              acc[sl][0] += wj[u] * __uint_as_float(r[sl][u].x);
+              acc[sl][1] += wj[u] * __uint_as_float(r[sl][u].y);
+              acc[sl][2] += wj[u] * __uint_as_float(r[sl][u].z);
+              acc[sl][3] += wj[u] * __uint_as_float(r[sl][u].w);
+            }
+          }
       }
-      if (c < H) {
+#pragma unroll
+      for (int sl = 0; sl < kSlabs; ++sl) {
+        const int c = c0 + sl * 64 * EPL + lane * EPL;
+        if (c >= H) continue;
         if constexpr (BF16) {
-          const u32x4 o{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]),
-                        pack_bf16(acc[4], acc[5]), pack_bf16(acc[6], acc[7])};
+          const u32x4 o{pack_bf16(acc[sl][0], acc[sl][1]), pack_bf16(acc[sl][2], acc[sl][3]),
+                        pack_bf16(acc[sl][4], acc[sl][5]), pack_bf16(acc[sl][6], acc[sl][7])};
           *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + (size_t)t * H + c) = o;
         } else {
           *reinterpret_cast<f32x4*>(static_cast<float*>(out) + (size_t)t * H + c) =
-              f32x4{acc[0], acc[1], acc[2], acc[3]};
+              f32x4{acc[sl][0], acc[sl][1], acc[sl][2], acc[sl][3]};
         }
       }
     }
