@@ -25,6 +25,7 @@ aux_loss     load-balancing loss forward and backward
 front_end    RMSNorm -> router projection -> top-k on raw logits -> activation
 backward     gradient of the routing weights and aux-loss scores w.r.t. logits
 dispatch     token rows into permuted (expert) order and the weighted combine back
+dense        dense [T, E] probs and routing map from the top-k outputs
 
 Parity pins: every function here is pinned by ``tests/test_oracle_*.py`` against
 closed forms, invariants, brute force on tiny inputs or library routines; see
@@ -36,11 +37,12 @@ from .aux_loss import aux_loss_fwd, aux_loss_bwd
 from .front_end import rmsnorm, front_end_route, bf16_round_bits, FrontEndResult
 from .backward import route_backward
 from .dispatch import dispatch, combine
+from .dense import dense_outputs
 
 __all__ = [
     "route", "RouteResult", "decode_input", "selection_keys32", "exact_keys64",
     "permute", "PermuteResult", "max_padded_tokens", "max_tiles",
     "aux_loss_fwd", "aux_loss_bwd",
     "rmsnorm", "front_end_route", "bf16_round_bits", "FrontEndResult",
-    "route_backward", "dispatch", "combine",
+    "route_backward", "dispatch", "combine", "dense_outputs",
 ]

@@ -11,6 +11,7 @@ import oracle
 import test_oracle_aux_front as T_AF
 import test_oracle_backward as T_B
 import test_oracle_dispatch as T_D
+import test_oracle_dense as T_X
 import test_oracle_golden as T_G
 import test_oracle_permutation as T_P
 import test_oracle_routing as T_R
@@ -29,6 +30,7 @@ PINS = [
     T_B.pin_backward_finite_differences, T_B.pin_backward_invariants,
     T_D.pin_dispatch_rows, T_D.pin_combine_inverts_dispatch, T_D.pin_combine_one_hot_and_linearity,
     T_D.pin_combine_local_shard_and_example,
+    T_X.pin_dense_structure, T_X.pin_dense_example,
 ]
 
 # (module, text in the oracle, planted replacement, what the mistake is)
@@ -106,6 +108,10 @@ MUTATIONS = [
      "combine: a non-local choice reads the last row"),
     ("dispatch", "        out[ok] += w[ok, j, None] * y[slot[ok]]", "        out[ok] += w[ok, k - 1 - j, None] * y[slot[ok]]",
      "combine: weights paired with the wrong choice"),
+    ("dense", "                probs[t, e] = w[t, j]", "                probs[t, e] = w[t, k - 1 - j]",
+     "dense: weights placed at the wrong choice's expert"),
+    ("dense", "            if 0 <= e < E:", "            if e < E:",
+     "dense: negative ids wrap to the last experts"),
 ]
 
 
