@@ -207,6 +207,23 @@ def other_configs(mr, torch, np, dev, rotate_mb, K):
             "gbs": set_b / (ms * 1e-3) / 1e9, "buffer_sets": R}
         del bsets
 
+    # dense [T, E] probs + routing map from the DeepSeek-V3-like top-k outputs
+    w = WORKLOADS["deepseek_v3_like"]
+    gen = torch.Generator(device="cpu").manual_seed(w.seed + 3)
+    ids0 = torch.argsort(torch.rand((w.T, w.E), generator=gen), dim=1)[:, :w.k].to(torch.int32).to(dev)
+    wts0 = torch.rand((w.T, w.k), generator=gen).to(dev)
+    x_bytes = w.T * w.k * 8 + w.T * w.E * 5
+    R = n_sets(x_bytes, rotate_mb)
+    xsets = [(ids0.clone(), wts0.clone(), torch.empty((w.T, w.E), dtype=torch.float32, device=dev),
+              torch.empty((w.T, w.E), dtype=torch.uint8, device=dev)) for _ in range(R)]
+    ms_x = graph_ms(torch, lambda i: mr.moe_topk_to_dense(w.T, w.E, w.k, xsets[i % R][0], xsets[i % R][1],
+                                                          mr.MOE_F32, xsets[i % R][2], xsets[i % R][3]), K)
+    res["deepseek_v3_like_dense_outputs"] = {
+        "workload": f"{w.description}; top-k ids/weights -> dense probs [T,E] f32 + routing map [T,E] u8",
+        "us_per_call": ms_x * 1e3, "algorithmic_bytes": x_bytes, "gbs": x_bytes / (ms_x * 1e-3) / 1e9,
+        "buffer_sets": R}
+    del xsets
+
     # token dispatch and combine around the expert GEMM, DeepSeek-V3-like route
     # at the front end's hidden size (7168, bf16), rows of synthetic N(0,1)
     w = WORKLOADS["deepseek_v3_like"]

@@ -276,6 +276,21 @@ moe_status moe_route_backward(const moe_route_args* args, const void* logits,
  *                  permuted_hidden (moe_max_padded_tokens()).
  * No workspace.  Rows move with 16-byte accesses when rows and pointers are
  * 16-byte aligned, element by element otherwise. */
+/* Dense form of moe_route's top-k outputs ([TE] I/O Contract: the probs and
+ * routing_map outputs of fused_topk_with_score_function, each [T, E]):
+ *
+ *   probs[t, e]       = topk_weights[t, j] where topk_ids[t, j] == e, else 0
+ *   routing_map[t, e] = 1 where token t chose expert e, else 0
+ *
+ * Values are copied, not recomputed (bf16 weights are widened exactly).
+ * topk_ids [T, k] int32 (ids outside [0, E) are ignored), topk_weights [T, k]
+ * in weights_dtype (MOE_F32 or MOE_BF16); probs: nullable out [T, E] float32;
+ * routing_map: nullable out [T, E] uint8 (bool); at least one is given.
+ * E <= 512, k in [1, 64].  No workspace. */
+moe_status moe_topk_to_dense(int32_t T, int32_t E, int32_t top_k, const int32_t* topk_ids,
+                             const void* topk_weights, int32_t weights_dtype, float* probs,
+                             uint8_t* routing_map, hipStream_t stream);
+
 moe_status moe_dispatch(const void* hidden, int32_t dtype, int32_t T, int32_t H,
                         const int32_t* permuted_idx_to_token_idx,
                         const int32_t* total_num_padded_tokens, int64_t max_padded_tokens,
@@ -354,7 +369,8 @@ typedef enum moe_kernel_kind {
   MOE_KERNEL_ROUTE_BWD = 6,
   MOE_KERNEL_DISPATCH = 7,
   MOE_KERNEL_COMBINE = 8,
-  MOE_KERNEL_KINDS = 9
+  MOE_KERNEL_DENSE = 9,
+  MOE_KERNEL_KINDS = 10
 } moe_kernel_kind;
 moe_status moe_profile_begin(void);
 moe_status moe_profile_end(void);

@@ -220,3 +220,15 @@ def test_dispatch_combine_validation():
     assert C(FAKE, mr.MOE_BF16, 10, 64, 8, None, FAKE, mr.MOE_F32, FAKE, None) == mr.MOE_EINVAL
     assert C(FAKE, mr.MOE_F32, 10, 64, 8, FAKE, ctypes.c_void_p(0x1002), mr.MOE_F32, FAKE, None) == mr.MOE_EINVAL
     assert C(None, mr.MOE_BF16, 0, 64, 8, None, None, mr.MOE_F32, None, None) == mr.MOE_OK
+
+
+def test_topk_to_dense_validation():
+    X = _lib.lib.moe_topk_to_dense
+    # every call below fails on the host, before anything is launched
+    assert X(10, 8, 2, FAKE, FAKE, mr.MOE_F32, None, None, None) == mr.MOE_EINVAL    # no output
+    assert X(10, 8, 9, FAKE, FAKE, mr.MOE_F32, FAKE, None, None) == mr.MOE_EINVAL    # k > E
+    assert X(10, 600, 8, FAKE, FAKE, mr.MOE_F32, FAKE, None, None) == mr.MOE_EUNSUPPORTED
+    assert X(10, 8, 2, None, FAKE, mr.MOE_F32, FAKE, None, None) == mr.MOE_EINVAL
+    assert X(10, 8, 2, FAKE, FAKE, mr.MOE_F16, FAKE, None, None) == mr.MOE_EINVAL
+    assert X(10, 8, 2, FAKE, ctypes.c_void_p(0x1002), mr.MOE_F32, FAKE, None, None) == mr.MOE_EINVAL
+    assert X(0, 8, 2, None, None, mr.MOE_F32, FAKE, None, None) == mr.MOE_OK         # nothing to do

@@ -23,11 +23,11 @@ from ._lib import (MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHI
                    moe_route_args, LIB_PATH, MOE_KERNEL_ROUTE, MOE_KERNEL_COUNTS,
                    MOE_KERNEL_SCATTER, MOE_KERNEL_AUX_FWD, MOE_KERNEL_AUX_BWD,
                    MOE_KERNEL_FRONT_END, MOE_KERNEL_ROUTE_BWD,
-                   MOE_KERNEL_DISPATCH, MOE_KERNEL_COMBINE)
+                   MOE_KERNEL_DISPATCH, MOE_KERNEL_COMBINE, MOE_KERNEL_DENSE)
 
 __all__ = [
     "moe_route", "moe_route_permute", "moe_aux_loss", "rmsnorm_gate_route", "moe_route_backward",
-    "moe_dispatch", "moe_combine",
+    "moe_dispatch", "moe_combine", "moe_topk_to_dense",
     "moe_route_workspace_size", "moe_route_count_region_bytes", "moe_aux_loss_workspace_size",
     "moe_profile_begin", "moe_profile_end", "moe_profile_read",
     "rmsnorm_gate_route_workspace_size", "rmsnorm_gate_route_sync_region_bytes",
@@ -118,6 +118,13 @@ def moe_route_backward(args: moe_route_args, logits, topk_ids, grad_weights, gra
     _check(_lib.lib.moe_route_backward(ctypes.byref(args), _ptr(logits), _ptr(topk_ids),
                                        _ptr(grad_weights), _ptr(grad_scores), _ptr(grad_logits),
                                        _stream(stream)))
+
+
+def moe_topk_to_dense(T: int, E: int, top_k: int, topk_ids, topk_weights, weights_dtype: int,
+                      probs=None, routing_map=None, stream=None) -> None:
+    _check(_lib.lib.moe_topk_to_dense(T, E, top_k, _ptr(topk_ids), _ptr(topk_weights),
+                                      weights_dtype, _ptr(probs), _ptr(routing_map),
+                                      _stream(stream)))
 
 
 def moe_dispatch(hidden, dtype: int, T: int, H: int, permuted_idx_to_token_idx,

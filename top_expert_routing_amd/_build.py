@@ -22,7 +22,7 @@ LIB_DIR = os.path.join(HERE, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libmoe_route.so")
 
 SOURCES = ["route_sigmoid.hip", "route_softmax.hip", "route_softmax_bias.hip",
-           "route_kernels.hip", "route_backward.hip", "dispatch.hip", "aux_loss.hip", "front_end.hip", "api.cpp"]
+           "route_kernels.hip", "route_backward.hip", "dispatch.hip", "dense.hip", "aux_loss.hip", "front_end.hip", "api.cpp"]
 ARCH = os.environ.get("MOE_ROUTE_ARCH", "gfx950")
 
 COMMON_FLAGS = [

@@ -21,7 +21,7 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EUNSUPPORTED", 3: "MOE_EWO
 # Every symbol the header declares.
 EXPORTED = [
     "moe_route", "moe_route_permute", "moe_aux_loss", "rmsnorm_gate_route", "moe_route_backward",
-    "moe_dispatch", "moe_combine",
+    "moe_dispatch", "moe_combine", "moe_topk_to_dense",
     "moe_route_workspace_size", "moe_route_count_region_bytes", "moe_aux_loss_workspace_size",
     "rmsnorm_gate_route_workspace_size", "rmsnorm_gate_route_sync_region_bytes",
     "moe_max_padded_tokens", "moe_max_tiles",
@@ -31,7 +31,7 @@ EXPORTED = [
 
 MOE_KERNEL_ROUTE, MOE_KERNEL_COUNTS, MOE_KERNEL_SCATTER = 0, 1, 2
 MOE_KERNEL_AUX_FWD, MOE_KERNEL_AUX_BWD, MOE_KERNEL_FRONT_END = 3, 4, 5
-MOE_KERNEL_ROUTE_BWD, MOE_KERNEL_DISPATCH, MOE_KERNEL_COMBINE = 6, 7, 8
+MOE_KERNEL_ROUTE_BWD, MOE_KERNEL_DISPATCH, MOE_KERNEL_COMBINE, MOE_KERNEL_DENSE = 6, 7, 8, 9
 
 
 class MoeError(RuntimeError):
@@ -97,6 +97,8 @@ def _load():
     lib.moe_dispatch.restype = i32
     lib.moe_combine.argtypes = [vp, i32, i32, i32, i32, vp, vp, i32, vp, vp]
     lib.moe_combine.restype = i32
+    lib.moe_topk_to_dense.argtypes = [i32, i32, i32, vp, vp, i32, vp, vp, vp]
+    lib.moe_topk_to_dense.restype = i32
     lib.rmsnorm_gate_route.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, i32, vp, vp,
                                        vp, vp, sz, vp]
     lib.rmsnorm_gate_route.restype = i32

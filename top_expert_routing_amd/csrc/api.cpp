@@ -583,6 +583,27 @@ moe_status moe_route_backward(const moe_route_args* args, const void* logits,
   return MOE_OK;
 }
 
+moe_status moe_topk_to_dense(int32_t T, int32_t E, int32_t k, const int32_t* ids, const void* weights,
+                             int32_t weights_dtype, float* probs, uint8_t* rmap, hipStream_t stream) {
+  clear_error();
+  if (T < 0 || E < 1) return fail(MOE_EINVAL, "T >= 0 and E >= 1");
+  if (E > 512) return fail(MOE_EUNSUPPORTED, "E > 512");
+  if (k < 1 || k > E) return fail(MOE_EINVAL, "top_k must be in [1, E]");
+  if (k > kMaxTopK) return fail(MOE_EUNSUPPORTED, "top_k > %d", kMaxTopK);
+  if (weights_dtype != MOE_F32 && weights_dtype != MOE_BF16)
+    return fail(MOE_EINVAL, "weights_dtype must be MOE_F32 or MOE_BF16");
+  if (probs == nullptr && rmap == nullptr) return fail(MOE_EINVAL, "one of probs / routing_map is required");
+  if (T == 0) return MOE_OK;
+  if (ids == nullptr || weights == nullptr) return fail(MOE_EINVAL, "topk_ids and topk_weights are required");
+  if (!aligned(ids, 4) || !aligned(probs, 4) || !aligned(weights, weights_dtype == MOE_BF16 ? 2 : 4))
+    return fail(MOE_EINVAL, "misaligned pointer");
+  hipError_t e = launch_with_profile(MOE_KERNEL_DENSE, stream, [&] {
+    return moe::launch_dense(T, E, k, ids, weights, weights_dtype == MOE_BF16, probs, rmap, stream);
+  });
+  if (e != hipSuccess) return hip_fail(e, "dense_kernel launch");
+  return MOE_OK;
+}
+
 moe_status moe_dispatch(const void* hidden, int32_t dtype, int32_t T, int32_t H,
                         const int32_t* p2t, const int32_t* total, int64_t max_padded, void* out,
                         hipStream_t stream) {

@@ -1,0 +1,92 @@
+// gfx950 kernel for the dense [T, E] form of the top-k outputs
+// (TransformerEngine Fused Router, I/O Contract: probs and routing_map of
+// fused_topk_with_score_function): probs[t, e] = the weight of expert e if
+// token t chose it, else 0; routing_map[t, e] = whether it did.
+//
+// One wavefront per token; lane l writes experts [J l, J l + J) with one
+// vector store per output (J = ceil(E / 64) rounded to 1/2/4/8); lanes j < k
+// read the token's j-th id and weight, and k readlanes bring each to the lane
+// owning the expert.  Write-bound: T E (4 + 1) bytes.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+constexpr int kDenseThreads = 256;
+}
+
+template <int J, bool VEC>
+__global__ void __launch_bounds__(kDenseThreads)
+    dense_kernel(int T, int E, int k, const int32_t* __restrict__ ids, const void* __restrict__ weights,
+                 int w_bf16, float* __restrict__ probs, uint8_t* __restrict__ rmap) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kDenseThreads / 64) + (threadIdx.x >> 6);
+  if (t >= T) return;                                   // whole wavefront leaves together
+  int my_id = -1;
+  float my_w = 0.0f;
+  if (lane < k) {
+    my_id = ids[(size_t)t * k + lane];
+    my_w = w_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(weights)[(size_t)t * k + lane])
+                  : static_cast<const float*>(weights)[(size_t)t * k + lane];
+  }
+  const int e0 = J * lane;
+  float v[J];
+  uint32_t sel = 0;
+#pragma unroll
+  for (int j = 0; j < J; ++j) v[j] = 0.0f;
+  for (int i = 0; i < k; ++i) {
+    const int e = __builtin_amdgcn_readlane(my_id, i);
+    const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), i));
+    if (e >= 0 && e < E && e / J == lane) {
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+        if (e % J == j) { v[j] = w; sel |= 1u << j; }
+    }
+  }
+  if (e0 >= E) return;
+  const size_t base = (size_t)t * E + e0;
+  if constexpr (VEC && J >= 4) {
+    if (probs != nullptr) {
+#pragma unroll
+      for (int h = 0; h < J / 4; ++h)
+        __builtin_nontemporal_store(f32x4{v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]},
+                                    reinterpret_cast<f32x4*>(probs + base) + h);
+    }
+    if (rmap != nullptr) {
+      uint32_t b[J / 4];
+#pragma unroll
+      for (int h = 0; h < J / 4; ++h) b[h] = (sel >> (4 * h)) & 1u | ((sel >> (4 * h + 1)) & 1u) << 8 |
+                                              ((sel >> (4 * h + 2)) & 1u) << 16 | ((sel >> (4 * h + 3)) & 1u) << 24;
+      if constexpr (J == 4) *reinterpret_cast<uint32_t*>(rmap + base) = b[0];
+      else *reinterpret_cast<uint2*>(rmap + base) = make_uint2(b[0], b[1]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      if (e0 + j >= E) break;
+      if (probs != nullptr) probs[base + j] = v[j];
+      if (rmap != nullptr) rmap[base + j] = (uint8_t)((sel >> j) & 1u);
+    }
+  }
+}
+
+hipError_t launch_dense(int T, int E, int k, const int32_t* ids, const void* weights, bool w_bf16,
+                        float* probs, uint8_t* rmap, hipStream_t s) {
+  const int J = E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : 8;   // E <= 512
+  const bool vec = J >= 4 && E % J == 0 && (uintptr_t)probs % 16 == 0 && (uintptr_t)rmap % 8 == 0;
+  const dim3 grid((T + kDenseThreads / 64 - 1) / (kDenseThreads / 64));
+#define MOE_DENSE(JJ, V)                                                                     \
+  MOE_LAUNCH((dense_kernel<JJ, V>), grid, dim3(kDenseThreads), 0, s, T, E, k, ids, weights, \
+             (int)w_bf16, probs, rmap)
+  switch (J) {
+    case 1: MOE_DENSE(1, false); break;
+    case 2: MOE_DENSE(2, false); break;
+    case 4: if (vec) MOE_DENSE(4, true); else MOE_DENSE(4, false); break;
+    default: if (vec) MOE_DENSE(8, true); else MOE_DENSE(8, false); break;
+  }
+#undef MOE_DENSE
+  return hipGetLastError();
+}
+
+}  // namespace moe

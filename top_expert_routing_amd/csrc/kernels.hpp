@@ -147,6 +147,10 @@ hipError_t launch_dispatch(const void* hidden, int64_t row_bytes, const int32_t*
 hipError_t launch_combine(const void* expert_out, bool bf16, int T, int H, int k, const int32_t* e2p,
                           const void* weights, bool w_bf16, void* out, hipStream_t s);
 
+// Dense [T, E] probs / routing map from the top-k outputs (see dense.hip).
+hipError_t launch_dense(int T, int E, int k, const int32_t* ids, const void* weights, bool w_bf16,
+                        float* probs, uint8_t* rmap, hipStream_t s);
+
 struct FrontEndParams {
   const void* hidden;
   const void* gamma;
