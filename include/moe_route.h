@@ -1,7 +1,7 @@
 /*
  * moe_route.h -- C ABI of the MI355X (gfx950) fused MoE top-k routing library.
  *
- * Four operations, each one asynchronous launch sequence on the caller's HIP
+ * Operations, each one asynchronous launch sequence on the caller's HIP
  * stream:
  *
  *   moe_route            router logits [T, E] -> top-k ids and weights
@@ -10,6 +10,10 @@
  *   moe_aux_loss         load-balancing loss, forward and/or backward
  *   rmsnorm_gate_route   RMSNorm -> router projection (MFMA) -> top-k on the
  *                        raw logits -> activation of the chosen experts
+ *   moe_route_backward   gradient of the weights / scores w.r.t. the logits
+ *   moe_topk_to_dense    dense [T, E] probs and routing map from the top-k
+ *   moe_dispatch         token rows into permuted (expert) order
+ *   moe_combine          weighted expert rows back into token order
  *
  * Conventions shared by every entry point
  * ----------------------------------------
