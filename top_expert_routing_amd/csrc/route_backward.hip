@@ -12,12 +12,14 @@
 //
 //   grad_logits = d/dx ( sum_j g_j w'_j + sum_e h_e scores_e )
 //
-// Four tokens per wavefront, their inputs requested together; lane l holds
-// experts [J l, J l + J): the logits row, the score gradient row and the
-// output row move with one vector access per lane; the chosen experts' weight gradients
-// reach their owner lanes by readlane; per-token sums are wavefront
-// reductions.  HBM-bound: per token it reads the logits row (+ the score
-// gradient row) and k ids and weight gradients, and writes one float32 row.
+// A token per cluster of L lanes (L = 8/16/32 with four experts per lane for
+// E <= 32/64/128, else the whole wavefront with J = ceil(E / 64) per lane);
+// lane l of a cluster holds experts [J l, J l + J): the logits row, the score
+// gradient row and the output row move with one vector access per lane; the
+// chosen experts' weight gradients reach their owner lanes by readlane (or a
+// cluster shuffle); per-token sums are cluster reductions.  HBM-bound: per
+// token it reads the logits row (+ the score gradient row) and k ids and
+// weight gradients, and writes one float32 row.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -26,11 +28,13 @@ namespace moe {
 namespace {
 
 constexpr int kBwdThreads = 256;
-constexpr int kBwdTokens = 1;       // tokens per wavefront
 constexpr float kNegInf = -__builtin_huge_valf();
 
-__device__ __forceinline__ float wsum(float v) { return cl_sum<64>(v); }
-__device__ __forceinline__ float wmax(float v) { return cl_max<64>(v); }
+// reductions over the L lanes of one token
+template <int L>
+__device__ __forceinline__ float wsum(float v) { return cl_sum<L>(v); }
+template <int L>
+__device__ __forceinline__ float wmax(float v) { return cl_max<L>(v); }
 
 // J consecutive elements at p (VEC: one vector access, p aligned to its size)
 template <int J, bool VEC>
@@ -89,7 +93,7 @@ __device__ __forceinline__ void store_f32(float* p, int n_valid, const float (&v
 
 // One token's inputs, read before any token of the wavefront is computed.
 template <bool BF16, int J, bool VEC>
-__device__ __forceinline__ void load_token(const RouteBwdParams& p, int t, int lane, int e0, int nv,
+__device__ __forceinline__ void load_token(const RouteBwdParams& p, int t, int lane_c, int e0, int nv,
                                            float (&x)[J], float (&h)[J], int& my_id,
                                            float& my_g) {
 #pragma unroll
@@ -105,17 +109,18 @@ __device__ __forceinline__ void load_token(const RouteBwdParams& p, int t, int l
       load_f32<J, VEC>(static_cast<const float*>(p.logits) + (size_t)t * E + e0, nv, x);
     if (p.grad_scores != nullptr) load_f32<J, VEC>(p.grad_scores + (size_t)t * E + e0, nv, h);
   }
-  if (p.grad_weights != nullptr && lane < k) {
-    my_id = p.ids[(size_t)t * k + lane];
-    my_g = p.grad_weights[(size_t)t * k + lane] * p.scale;
+  if (p.grad_weights != nullptr && lane_c < k) {
+    my_id = p.ids[(size_t)t * k + lane_c];
+    my_g = p.grad_weights[(size_t)t * k + lane_c] * p.scale;
   }
 }
 
 // One token's gradient row, from its inputs; stored with streaming stores.
-template <int J, bool VEC>
-__device__ __forceinline__ void token_grad(const RouteBwdParams& p, int t, int lane, int e0, int nv,
-                                           float (&x)[J], const float (&h)[J], int my_id,
+template <int J, int L, bool VEC>
+__device__ __forceinline__ void token_grad(const RouteBwdParams& p, int t, bool tv, int lane, int e0,
+                                           int nv, float (&x)[J], const float (&h)[J], int my_id,
                                            float my_g) {
+  const int lane_c = lane & (L - 1), cbase = lane & ~(L - 1);
   const int E = p.E, k = p.k;
 #pragma unroll
   for (int j = 0; j < J; ++j)
@@ -141,11 +146,11 @@ __device__ __forceinline__ void token_grad(const RouteBwdParams& p, int t, int l
     float m = kNegInf;
 #pragma unroll
     for (int j = 0; j < J; ++j) m = fmaxf(m, x[j]);
-    m = wmax(m);
+    m = wmax<L>(m);
     float z = 0.0f;
 #pragma unroll
     for (int j = 0; j < J; ++j) { pz[j] = exp_f32(x[j] - m); z += pz[j]; }
-    const float inv = 1.0f / wsum(z);
+    const float inv = 1.0f / wsum<L>(z);
 #pragma unroll
     for (int j = 0; j < J; ++j) pz[j] *= inv;
   }
@@ -157,9 +162,16 @@ __device__ __forceinline__ void token_grad(const RouteBwdParams& p, int t, int l
 #pragma unroll
     for (int j = 0; j < J; ++j) g[j] = 0.0f;
     for (int i = 0; i < k; ++i) {
-      const int e = __builtin_amdgcn_readlane(my_id, i);
-      const float gi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_g), i));
-      if (e >= 0 && e < E && e / J == lane) {
+      int e;
+      float gi;
+      if constexpr (L == 64) {                           // one token per wavefront: uniform
+        e = __builtin_amdgcn_readlane(my_id, i);
+        gi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_g), i));
+      } else {                                           // the cluster's lane i
+        e = __shfl(my_id, cbase + i, 64);
+        gi = __shfl(my_g, cbase + i, 64);
+      }
+      if (e >= 0 && e < E && e / J == lane_c) {
 #pragma unroll
         for (int j = 0; j < J; ++j)
           if (e % J == j) { g[j] = gi; sel |= 1u << j; }
@@ -172,8 +184,8 @@ __device__ __forceinline__ void token_grad(const RouteBwdParams& p, int t, int l
 #pragma unroll
         for (int j = 0; j < J; ++j)
           if ((sel >> j) & 1u) { S += s[j]; gs += g[j] * s[j]; }
-        S = wsum(S);
-        gs = wsum(gs);
+        S = wsum<L>(S);
+        gs = wsum<L>(gs);
         const float invS = 1.0f / S, c = gs * invS;      // c = sum_j g_j w_j
 #pragma unroll
         for (int j = 0; j < J; ++j) gs_[j] = (g[j] - c) * invS;
@@ -191,8 +203,8 @@ __device__ __forceinline__ void token_grad(const RouteBwdParams& p, int t, int l
 #pragma unroll
         for (int j = 0; j < J; ++j)
           if ((sel >> j) & 1u) { S += pz[j]; gp += g[j] * pz[j]; }
-        S = wsum(S);
-        gp = wsum(gp);
+        S = wsum<L>(S);
+        gp = wsum<L>(gp);
         const float invS = 1.0f / S, c = gp * invS;
 #pragma unroll
         for (int j = 0; j < J; ++j) dp[j] = ((sel >> j) & 1u) ? (g[j] - c) * invS : 0.0f;
@@ -203,7 +215,7 @@ __device__ __forceinline__ void token_grad(const RouteBwdParams& p, int t, int l
       float c2 = 0.0f;                                   // softmax Jacobian, transposed
 #pragma unroll
       for (int j = 0; j < J; ++j) c2 += pz[j] * dp[j];
-      c2 = wsum(c2);
+      c2 = wsum<L>(c2);
 #pragma unroll
       for (int j = 0; j < J; ++j) dx[j] += pz[j] * (dp[j] - c2);
     } else {                                             // softmax of the chosen logits
@@ -211,18 +223,18 @@ __device__ __forceinline__ void token_grad(const RouteBwdParams& p, int t, int l
 #pragma unroll
       for (int j = 0; j < J; ++j)
         if ((sel >> j) & 1u) ms = fmaxf(ms, x[j]);
-      ms = wmax(ms);
+      ms = wmax<L>(ms);
       float w[J], zs = 0.0f;
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         w[j] = ((sel >> j) & 1u) ? exp_f32(x[j] - ms) : 0.0f;
         zs += w[j];
       }
-      const float invz = 1.0f / wsum(zs);
+      const float invz = 1.0f / wsum<L>(zs);
       float c = 0.0f;
 #pragma unroll
       for (int j = 0; j < J; ++j) { w[j] *= invz; c += w[j] * g[j]; }
-      c = wsum(c);
+      c = wsum<L>(c);
 #pragma unroll
       for (int j = 0; j < J; ++j)
         if ((sel >> j) & 1u) dx[j] += w[j] * (g[j] - c);
@@ -234,66 +246,75 @@ __device__ __forceinline__ void token_grad(const RouteBwdParams& p, int t, int l
       float Z = 0.0f;
 #pragma unroll
       for (int j = 0; j < J; ++j) Z += s[j];
-      Z = wsum(Z);
+      Z = wsum<L>(Z);
       const float invZ = 1.0f / Z;
       float c = 0.0f;
 #pragma unroll
       for (int j = 0; j < J; ++j) c += h[j] * s[j];
-      c = wsum(c) * invZ;                                // sum_e h_e q_e
+      c = wsum<L>(c) * invZ;                                // sum_e h_e q_e
 #pragma unroll
       for (int j = 0; j < J; ++j) dx[j] += ds[j] * (h[j] - c) * invZ;
     } else {                                             // q = softmax over E
       float c = 0.0f;
 #pragma unroll
       for (int j = 0; j < J; ++j) c += h[j] * pz[j];
-      c = wsum(c);
+      c = wsum<L>(c);
 #pragma unroll
       for (int j = 0; j < J; ++j) dx[j] += pz[j] * (h[j] - c);
     }
   }
-  if (nv > 0) store_f32<J, VEC>(p.grad_logits + (size_t)t * E + e0, nv, dx);
+  if (tv && nv > 0) store_f32<J, VEC>(p.grad_logits + (size_t)t * E + e0, nv, dx);
 }
 
-// Wavefront w of block b: tokens [kBwdTokens (4 b + w), +kBwdTokens), all of
-// their inputs requested before the first is computed.
-template <bool BF16, int J, bool VEC>
+// A token per cluster of L lanes (64 / L tokens per wavefront): token
+// (4 b + w) (64 / L) + lane / L.  Clusters past T compute but store nothing.
+template <bool BF16, int J, int L, bool VEC>
 __global__ void __launch_bounds__(kBwdThreads) route_bwd_kernel(RouteBwdParams p) {
+  constexpr int kTpw = 64 / L;
   const int lane = threadIdx.x & 63;
-  const int t0 = (blockIdx.x * (kBwdThreads / 64) + (threadIdx.x >> 6)) * kBwdTokens;
+  const int t0 = (blockIdx.x * (kBwdThreads / 64) + (threadIdx.x >> 6)) * kTpw;
   if (t0 >= p.T) return;                                 // whole wavefront leaves together
-  const int e0 = J * lane;
+  const int t = t0 + lane / L;
+  const bool tv = t < p.T;
+  const int e0 = J * (lane & (L - 1));
   const int nv = min(J, max(0, p.E - e0));               // this lane's experts
-  float x[kBwdTokens][J], h[kBwdTokens][J], g[kBwdTokens];
-  int id[kBwdTokens];
-#pragma unroll
-  for (int u = 0; u < kBwdTokens; ++u)
-    load_token<BF16, J, VEC>(p, t0 + u, lane, e0, nv, x[u], h[u], id[u], g[u]);
-#pragma unroll
-  for (int u = 0; u < kBwdTokens; ++u)
-    if (t0 + u < p.T) token_grad<J, VEC>(p, t0 + u, lane, e0, nv, x[u], h[u], id[u], g[u]);
+  float x[J], h[J], g;
+  int id;
+  load_token<BF16, J, VEC>(p, tv ? t : p.T, lane & (L - 1), e0, nv, x, h, id, g);
+  token_grad<J, L, VEC>(p, t, tv, lane, e0, nv, x, h, id, g);
 }
 
-template <bool BF16, int J>
+template <bool BF16, int J, int L>
 static hipError_t launch_bwd_j(const RouteBwdParams& p, bool vec, hipStream_t s) {
-  const int per_block = kBwdThreads / 64 * kBwdTokens;
+  const int per_block = kBwdThreads / 64 * (64 / L);
   const dim3 grid((p.T + per_block - 1) / per_block);
-  if (vec) MOE_LAUNCH((route_bwd_kernel<BF16, J, true>), grid, dim3(kBwdThreads), 0, s, p);
-  else MOE_LAUNCH((route_bwd_kernel<BF16, J, false>), grid, dim3(kBwdThreads), 0, s, p);
+  if (vec) MOE_LAUNCH((route_bwd_kernel<BF16, J, L, true>), grid, dim3(kBwdThreads), 0, s, p);
+  else MOE_LAUNCH((route_bwd_kernel<BF16, J, L, false>), grid, dim3(kBwdThreads), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_route_backward(const RouteBwdParams& p, bool bf16, hipStream_t s) {
-  const int J = p.E <= 64 ? 1 : p.E <= 128 ? 2 : p.E <= 256 ? 4 : 8;   // E <= 512
+  // lanes per token: four experts per lane (16-byte float32 accesses) while a
+  // token's k choices still fit its lanes; else the whole wavefront
+  const int L = (p.E <= 32 && p.k <= 8) ? 8 : (p.E <= 64 && p.k <= 16) ? 16
+              : (p.E <= 256 && p.k <= 32) ? 32 : 64;
+  const int J = L < 32 ? 4 : L == 32 ? (p.E <= 128 ? 4 : 8)
+              : p.E <= 64 ? 1 : p.E <= 128 ? 2 : p.E <= 256 ? 4 : 8;   // E <= 512
   // vector accesses when every lane's J elements are whole and aligned
   const int esz = bf16 ? 2 : 4;
   const bool vec = J > 1 && p.E % J == 0 &&
                    (uintptr_t)p.logits % (J * esz) == 0 && (uintptr_t)p.grad_logits % (J * 4) == 0 &&
                    (p.grad_scores == nullptr || (uintptr_t)p.grad_scores % (J * 4) == 0);
+  if (L == 8) return bf16 ? launch_bwd_j<true, 4, 8>(p, vec, s) : launch_bwd_j<false, 4, 8>(p, vec, s);
+  if (L == 16) return bf16 ? launch_bwd_j<true, 4, 16>(p, vec, s) : launch_bwd_j<false, 4, 16>(p, vec, s);
+  if (L == 32 && J == 4)
+    return bf16 ? launch_bwd_j<true, 4, 32>(p, vec, s) : launch_bwd_j<false, 4, 32>(p, vec, s);
+  if (L == 32) return bf16 ? launch_bwd_j<true, 8, 32>(p, vec, s) : launch_bwd_j<false, 8, 32>(p, vec, s);
   switch (J) {
-    case 1: return bf16 ? launch_bwd_j<true, 1>(p, false, s) : launch_bwd_j<false, 1>(p, false, s);
-    case 2: return bf16 ? launch_bwd_j<true, 2>(p, vec, s) : launch_bwd_j<false, 2>(p, vec, s);
-    case 4: return bf16 ? launch_bwd_j<true, 4>(p, vec, s) : launch_bwd_j<false, 4>(p, vec, s);
-    default: return bf16 ? launch_bwd_j<true, 8>(p, vec, s) : launch_bwd_j<false, 8>(p, vec, s);
+    case 1: return bf16 ? launch_bwd_j<true, 1, 64>(p, false, s) : launch_bwd_j<false, 1, 64>(p, false, s);
+    case 2: return bf16 ? launch_bwd_j<true, 2, 64>(p, vec, s) : launch_bwd_j<false, 2, 64>(p, vec, s);
+    case 4: return bf16 ? launch_bwd_j<true, 4, 64>(p, vec, s) : launch_bwd_j<false, 4, 64>(p, vec, s);
+    default: return bf16 ? launch_bwd_j<true, 8, 64>(p, vec, s) : launch_bwd_j<false, 8, 64>(p, vec, s);
   }
 }
 
