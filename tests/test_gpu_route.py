@@ -264,3 +264,16 @@ def test_workspace_reuse_across_sizes():
         if permute:
             compare_permutation(fetch_permutation(out), ids, w.tile, 0, w.E, label)
         assert int(ws[:region].count_nonzero().item()) == 0, f"{label}: counting region not cleared"
+
+
+@pytest.mark.parametrize("name,T,tile,off,n_loc", [
+    ("tiny_softmax_post", 1, 1, 0, None), ("tiny_softmax_post", 64, 16, 0, None),
+    ("tiny_softmax_post", 40, 4, 2, 4), ("deepseek_v3_like", 64, 8, 64, 64),
+    ("deepseek_v3_like", 17, 256, 0, None), ("qwen_moe_like", 33, 2, 100, 28),
+    ("mixtral_like", 64, 1, 7, 1),
+])
+def test_single_block_permutation(name, T, tile, off, n_loc):
+    # T <= 64: the route kernel builds the permutation from its own bitmask
+    w = with_overrides(WORKLOADS[name], T=T)
+    logits, bias = route_inputs(w, T=T, seed=2000 + T + tile + off)
+    run_and_check(w, logits, bias, f"single block {name} T={T}", tile=tile, off=off, n_loc=n_loc)

@@ -278,7 +278,8 @@ moe_status launch_route_checked(const moe::RouteParams& p, const Shape& sh, bool
                                 hipStream_t stream) {
   const int rwpl = (p.variant == moe::kVarSoftmax && bf16) ? sh.epl / 2 : sh.epl;
   const size_t lds = moe::route_lds_bytes(sh.lpt, rwpl, sh.epl, p.hmask_len, p.cap, p.k,
-                                          p.grouped ? p.n_group : 0);
+                                          p.grouped ? p.n_group : 0) +
+                     (p.fused ? (((size_t)p.loc_n + 1) * 4 + 15) & ~(size_t)15 : 0);
   if (lds > 160 * 1024)
     return fail(MOE_EUNSUPPORTED, "route kernel needs %zu bytes of LDS", lds);
   hipError_t e = launch_with_profile(MOE_KERNEL_ROUTE, stream, [&] {
@@ -455,6 +456,25 @@ moe_status moe_route_permute(const moe_route_args* args, int32_t tile, int32_t l
   int32_t* rows = ws_count_rows(workspace);
   int32_t* hist = ws_hist(workspace);
 
+  if (cp.nb == 1) {
+    // every token in one route block: the route kernel finishes the
+    // permutation from its own bitmask (no counting rows, no second launch)
+    moe::RouteParams p = make_params(a, sh, logits, bias, topk_ids, topk_weights, scores, nullptr,
+                                     nullptr, cp.group_blocks, loc_off, loc_n);
+    p.fused = 1;
+    p.hmask_len = (loc_n + 1) & ~1;                     // the bitmask, without counting rows
+    p.tile = tile;
+    p.tile_shift = log2_exact(tile);
+    p.e2p = e2p;
+    p.p2t = p2t;
+    p.counts = expert_counts;
+    p.padded_offsets = padded_offsets;
+    p.total_out = total_num_padded_tokens;
+    p.nctas_out = num_non_exiting_ctas;
+    p.batch_idx = batch_idx;
+    p.mn_limit = mn_limit;
+    return launch_route_checked(p, sh, a.logits_dtype == MOE_BF16, stream);
+  }
   const moe::RouteParams p = make_params(a, sh, logits, bias, topk_ids, topk_weights, scores,
                                          rows, hist, cp.group_blocks, loc_off, loc_n);
   st = launch_route_checked(p, sh, a.logits_dtype == MOE_BF16, stream);

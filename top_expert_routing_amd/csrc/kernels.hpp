@@ -65,6 +65,19 @@ struct RouteParams {
   int loc_off, loc_n;
   int hmask_len;          // LDS u64 words for the block bitmask (even)
   int cap;                // candidate list capacity per token (>= k)
+  // A call whose tokens fit one block (T <= 64) finishes the permutation in
+  // the route kernel itself, from the block's LDS bitmask (no counting rows,
+  // no scatter launch): set `fused` and these outputs.
+  int fused;
+  int tile, tile_shift;
+  int32_t* e2p;           // [T k]
+  int32_t* p2t;           // [max padded]
+  int32_t* counts;        // [loc_n]
+  int32_t* padded_offsets;   // [loc_n + 1]
+  int32_t* total_out;
+  int32_t* nctas_out;
+  int32_t* batch_idx;     // [max tiles]
+  int32_t* mn_limit;      // [max tiles]
 };
 
 struct ScatterParams {

@@ -309,6 +309,69 @@ __device__ __forceinline__ void emit_selected(const EmitCtx& c, const int* mysel
 
 // Padded experts (e >= E) carry logit -inf and bias -inf, so their keys are
 // -inf and no per-element validity masks are needed anywhere.
+// The permutation of a call whose tokens all lie in this block (T <= 64), from
+// the block's bitmask of which tokens chose each local expert (FlashInfer
+// trtllm_gen_routing, Returns: the padded offsets, both index maps and the
+// per-tile expert and row limit): counts are popcounts, the padded offsets a
+// scan, and token t's slot for expert e is offset(e) + the number of lower
+// tokens that chose e (stable by token).  po: LDS for loc_n + 1 ints.
+template <int BLOCK>
+__device__ void permute_in_block(const RouteParams& p, const uint64_t* hmask, int* po) {
+  const int tid = threadIdx.x;
+  const int El = p.loc_n, k = p.k, tile = p.tile;
+  __syncthreads();                                      // the bitmask and the ids are complete
+  if (tid < 64) {                                       // exclusive scan of the padded sizes
+    const int n = El + 1;
+    const int per = (n + 63) / 64;
+    const int lo = min(n, tid * per), hi = min(n, lo + per);
+    int sum = 0;
+    for (int e = lo; e < hi; ++e)
+      sum += e < El ? ((__popcll(hmask[e]) + tile - 1) & ~(tile - 1)) : 0;
+    int incl = sum;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o, 64);
+      if (tid >= o) incl += u;
+    }
+    int run = incl - sum;
+    for (int e = lo; e < hi; ++e) {
+      po[e] = run;
+      run += e < El ? ((__popcll(hmask[e]) + tile - 1) & ~(tile - 1)) : 0;
+    }
+  }
+  __syncthreads();
+  // both index maps; every (token, choice) of the call is in this block
+  for (int q = tid; q < p.T * k; q += BLOCK) {
+    const int t = q / k;
+    const int el = p.ids[q] - p.loc_off;
+    int slot = -1;
+    if (el >= 0 && el < El) {
+      slot = po[el] + __popcll(hmask[el] & ((1ull << t) - 1ull));
+      p.p2t[slot] = t;
+    }
+    p.e2p[q] = slot;
+  }
+  // per expert: count, padded offset, its tiles, the -1 padding of its last tile
+  for (int e = tid; e < El; e += BLOCK) {
+    const int seg = po[e], cnt = __popcll(hmask[e]);
+    const int seg_end = seg + cnt;
+    const int ntile = (po[e + 1] - seg) >> p.tile_shift;
+    for (int j = 0; j < ntile; ++j) {
+      const int c = (seg >> p.tile_shift) + j;
+      p.batch_idx[c] = e;
+      p.mn_limit[c] = min(seg + (j + 1) * tile, seg_end);
+    }
+    for (int s2 = seg_end; s2 < po[e + 1]; ++s2) p.p2t[s2] = -1;
+    if (p.counts != nullptr) p.counts[e] = cnt;
+    p.padded_offsets[e] = seg;
+  }
+  if (tid == 0) {
+    const int total = po[El];
+    p.padded_offsets[El] = total;
+    *p.total_out = total;
+    *p.nctas_out = total >> p.tile_shift;
+  }
+}
+
 template <int LPT, int EPL, bool BF16, int VAR>
 __global__ void __launch_bounds__(kRouteBlock<LPT>) route_kernel(RouteParams p) {
   constexpr int BLOCK = kRouteBlock<LPT>;
@@ -369,7 +432,7 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>) route_kernel(RouteParams p) 
       bias_s[e] = b;
     }
   }
-  const bool counting = p.super_rows != nullptr;
+  const bool counting = p.super_rows != nullptr || p.fused;
   if (counting)
     for (int e = tid; e < p.loc_n; e += BLOCK) hmask[e] = 0;
   __syncthreads();
@@ -671,7 +734,7 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>) route_kernel(RouteParams p) 
     wave_lds_sync();
   }
 
-  if (counting) {
+  if (counting && p.super_rows != nullptr) {
     __syncthreads();
     int32_t* srow = p.super_rows + (size_t)(blk / p.group_blocks) * p.loc_n;
     for (int e = tid; e < p.loc_n; e += BLOCK) {
@@ -680,13 +743,15 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>) route_kernel(RouteParams p) 
       if (c != 0) atomicAdd(srow + e, c);
     }
   }
+  if (p.fused) permute_in_block<BLOCK>(p, hmask, reinterpret_cast<int*>(smem + L.total));
 }
 
 template <int LPT, int EPL, bool BF16, int VAR>
 hipError_t launch_route_inst(const RouteParams& p, int nb, hipStream_t s) {
   constexpr int BLOCK = kRouteBlock<LPT>;
   const size_t lds = route_lds_bytes(LPT, kRawRow<VAR, BF16> ? RawRow<EPL, BF16>::kWords : EPL,
-                                     EPL, p.hmask_len, p.cap, p.k, p.grouped ? p.n_group : 0);
+                                     EPL, p.hmask_len, p.cap, p.k, p.grouped ? p.n_group : 0) +
+                     (p.fused ? (((size_t)p.loc_n + 1) * 4 + 15) & ~(size_t)15 : 0);
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&route_kernel<LPT, EPL, BF16, VAR>),
