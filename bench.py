@@ -42,7 +42,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="deepseek_v3_like")
+    ap.add_argument("--workload", default="deepseek_v3_like",
+                    help="a routing workload, or decode_front_end for the front end alone")
     ap.add_argument("--rotate-mb", type=int, default=2 * 256 + 64,
                     help="bytes spanned by the rotating buffer sets (MiB)")
     ap.add_argument("--no-warm", action="store_true",
@@ -263,6 +264,14 @@ def other_configs(mr, torch, np, dev, rotate_mb, K):
         "buffer_sets": R}
     del dsets, csets, o
 
+    res["decode_front_end"] = front_end_bench(mr, torch, np, dev, rotate_mb, K)
+    return res
+
+
+def front_end_bench(mr, torch, np, dev, rotate_mb, K):
+    """The decode front end (RMSNorm -> projection -> top-k), cold (rotating sets):
+    microseconds per call, algorithmic GB/s and projection TFLOP/s."""
+    from workloads import FRONT_END, front_end_inputs
     f = FRONT_END
     hidden, gamma, W, _ = front_end_inputs(f)
     def bf(a):
@@ -284,13 +293,35 @@ def other_configs(mr, torch, np, dev, rotate_mb, K):
                               mr.MOE_SIGMOID, nm, ids, aff, workspace=wsf)
 
     ms = graph_ms(torch, fstep, K)
+    # both launches of a call under the library's event brackets, queue backlogged
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2.4e9 * 0.02))
+    mr.moe_profile_begin()
+    for i in range(min(K, 100)):
+        fstep(i)
+    mr.moe_profile_end()
+    torch.cuda.synchronize()
+    pms, pn = mr.moe_profile_read(mr.MOE_KERNEL_FRONT_END)
+    kernel_us = pms / pn * 1e3 if pn else None
     fb = 2 * f.T * f.H * 2 + f.H * 2 + f.H * f.E * 2 + f.T * f.k * 4 + f.T * f.E * 2
     flops = 2 * f.T * f.H * f.E
-    res["decode_front_end"] = {"workload": f.description, "us_per_call": ms * 1e3,
-                               "tokens_per_s": f.T / (ms * 1e-3), "algorithmic_bytes": fb,
-                               "gbs": fb / (ms * 1e-3) / 1e9, "mfma_tflops": flops / (ms * 1e-3) / 1e12,
-                               "buffer_sets": R}
-    return res
+    return {"workload": f.description, "us_per_call": ms * 1e3,
+            "tokens_per_s": f.T / (ms * 1e-3), "algorithmic_bytes": fb,
+            "gbs": fb / (ms * 1e-3) / 1e9, "mfma_tflops": flops / (ms * 1e-3) / 1e12,
+            "kernel_us_per_call": kernel_us, "buffer_sets": R}
+
+
+def copy_calibration(torch, dev, mb):
+    """Three plain device copies of mb MiB: the kernel of known size whose
+    rocprofv3 FETCH_SIZE / WRITE_SIZE readings scale other kernels' readings."""
+    n = mb * 2 ** 20 // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"bytes_read": n * 4, "bytes_written": n * 4, "launches": 3,
+            "op": "torch copy_ of a float32 tensor"}
 
 
 def cpu_baseline(w, sample_T: int, seconds: float):
@@ -325,9 +356,17 @@ def main():
     import top_expert_routing_amd as mr
     from workloads import WORKLOADS, route_inputs
 
-    w = WORKLOADS[a.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if a.workload == "decode_front_end":
+        # the decode front end alone (for counter passes over its two kernels)
+        fe = {"workload": "decode_front_end", "steps": a.steps,
+              **front_end_bench(mr, torch, np, dev, a.rotate_mb, a.steps)}
+        if a.copy_calibration_mb:
+            fe["copy_calibration"] = copy_calibration(torch, dev, a.copy_calibration_mb)
+        print(json.dumps(fe), flush=True)
+        return
+    w = WORKLOADS[a.workload]
     T, E, k, tile = w.T, w.E, w.k, w.tile
 
     logits_np, bias_np = route_inputs(w)
@@ -480,14 +519,7 @@ def main():
     if others is not None:
         line["other_configs"] = others
     if a.copy_calibration_mb:
-        n = a.copy_calibration_mb * 2 ** 20 // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        line["copy_calibration"] = {"bytes_read": n * 4, "bytes_written": n * 4, "launches": 3,
-                                    "op": "torch copy_ of a float32 tensor"}
+        line["copy_calibration"] = copy_calibration(torch, dev, a.copy_calibration_mb)
     s = json.dumps(line)
     print(s, flush=True)
     if a.json_out:

@@ -29,7 +29,7 @@ __global__ void __launch_bounds__(kAuxBlock)
     aux_fwd_partial_kernel(const float* __restrict__ probs, const int32_t* __restrict__ counts,
                            int64_t rows, int E, int64_t rows_per_block, int vec,
                            double* __restrict__ partial) {
-  __shared__ float cs[kAuxMaxE];
+  __shared__ __align__(16) float cs[kAuxMaxE];
   __shared__ float red[kAuxBlock / 64];
   for (int e = threadIdx.x; e < E; e += kAuxBlock) cs[e] = (float)counts[e];
   __syncthreads();
@@ -53,7 +53,8 @@ __global__ void __launch_bounds__(kAuxBlock)
                                     : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int u = 0; u < kAuxUnroll; ++u) {
-        acc += v[u].x * cs[col] + v[u].y * cs[col + 1] + v[u].z * cs[col + 2] + v[u].w * cs[col + 3];
+        const f32x4 c = *reinterpret_cast<const f32x4*>(cs + col);   // col % 4 == 0
+        acc += v[u].x * c.x + v[u].y * c.y + v[u].z * c.z + v[u].w * c.w;
         col += step;
         if (col >= E) col -= E;
       }
@@ -75,19 +76,17 @@ __global__ void __launch_bounds__(kAuxBlock)
 __global__ void __launch_bounds__(256)
     aux_fwd_final_kernel(const double* __restrict__ partial, int nparts, double scale,
                          float* __restrict__ loss) {
-  __shared__ double s[256];
-  double a = 0.0;
-  // each thread sums a contiguous run; runs are added in order below
+  __shared__ double s[4];
+  // each thread sums a contiguous run, then a fixed butterfly per wavefront and
+  // the four wavefront sums in order: the same order on every run
   const int per = (nparts + 255) / 256;
   const int lo = threadIdx.x * per;
+  double a = 0.0;
   for (int i = lo; i < lo + per && i < nparts; ++i) a += partial[i];
-  s[threadIdx.x] = a;
+  for (int o = 32; o > 0; o >>= 1) a += __shfl_xor(a, o, 64);
+  if ((threadIdx.x & 63) == 0) s[threadIdx.x >> 6] = a;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    double tot = 0.0;
-    for (int i = 0; i < 256; ++i) tot += s[i];
-    *loss = (float)(tot * scale);
-  }
+  if (threadIdx.x == 0) *loss = (float)((((s[0] + s[1]) + s[2]) + s[3]) * scale);
 }
 
 __global__ void __launch_bounds__(kAuxBlock)
