@@ -39,9 +39,19 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found; the HIP library cannot be built")
 
 
+# Per-source flags.  route_kernels.hip: the scatter kernel's block counter is a
+# single-lane returning atomic whose result is needed only at the kernel's end;
+# the atomic optimizer would turn it into a wave-wide atomic plus readfirstlane
+# at the branch join, which waits for the return at once.
+SOURCE_FLAGS = {
+    "route_kernels.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
+}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
+           "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     if verbose:

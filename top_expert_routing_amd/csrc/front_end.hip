@@ -230,19 +230,21 @@ __device__ void gemm_role(const FeArgs& a, int b, uint16_t* wt, uint16_t* gl) {
   const int lane = tid & 63, wv = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;           // k-group of 8
   const int row0 = tb * kTileRows + wv * 16 * kS;
+  // Every global read is issued before any is awaited (a load under a branch,
+  // or one whose value goes straight to LDS, is awaited at once, and with it
+  // every older load): the hidden rows (rows past T read row T - 1; their
+  // products are never stored: an MFMA output row depends on its own input
+  // row only), gamma into registers, then the W tile.
   u32x4 av[STEPS][kS];
 #pragma unroll
   for (int u = 0; u < STEPS; ++u)
 #pragma unroll
     for (int s = 0; s < kS; ++s) {
-      const int row = row0 + 16 * s + col;
-      av[u][s] = row < T
-                     ? *reinterpret_cast<const u32x4*>(a.hidden + (size_t)row * H + k0 + 32 * u +
-                                                       grp * 8)
-                     : u32x4{0, 0, 0, 0};
+      const int row = min(row0 + 16 * s + col, T - 1);
+      av[u][s] = *reinterpret_cast<const u32x4*>(a.hidden + (size_t)row * H + k0 + 32 * u + grp * 8);
     }
-  for (int v = tid; v < kc / 8; v += kThreads)
-    reinterpret_cast<u32x4*>(gl)[v] = reinterpret_cast<const u32x4*>(a.gamma + k0)[v];
+  static_assert(kc / 8 <= kThreads, "gamma: one 16-byte piece per thread");
+  const u32x4 gv = reinterpret_cast<const u32x4*>(a.gamma + k0)[tid < kc / 8 ? tid : 0];
   // W[k0 : k0+kc, n0 : n0+nw] -> wt[n][k]: 8 x 8 blocks, one per thread per round
   const int nb8 = (kc / 8) * (nw / 8);
   for (int q = tid; q < nb8; q += kThreads) {
@@ -262,6 +264,7 @@ __device__ void gemm_role(const FeArgs& a, int b, uint16_t* wt, uint16_t* gl) {
       *reinterpret_cast<u32x4*>(wt + (nb + n) * ts + kb) = u32x4{o[0], o[1], o[2], o[3]};
     }
   }
+  if (tid < kc / 8) reinterpret_cast<u32x4*>(gl)[tid] = gv;
   __syncthreads();                                      // W tile and gamma staged
   // x * gamma while r_t is on its way
   f32x2v xg[STEPS][kS][4];

@@ -91,32 +91,48 @@ __device__ __forceinline__ void store_f32(float* p, int n_valid, const float (&v
 
 }  // namespace
 
-// One token's inputs, read before any token of the wavefront is computed.
-template <bool BF16, int J, bool VEC>
+// One token's inputs, read before any token of the wavefront is computed.  The
+// loads are unconditional, so that they are all in flight together (a load in
+// a branch is awaited where the branch joins): t is a valid token (clusters
+// past T read token T - 1 and store nothing), lanes past E read the row start,
+// lanes j >= k read choice k - 1 and drop it.  HW / HS: weight / score
+// gradients are given.
+template <bool BF16, int J, bool VEC, bool HW, bool HS>
 __device__ __forceinline__ void load_token(const RouteBwdParams& p, int t, int lane_c, int e0, int nv,
                                            float (&x)[J], float (&h)[J], int& my_id,
                                            float& my_g) {
-#pragma unroll
-  for (int j = 0; j < J; ++j) { x[j] = 0.0f; h[j] = 0.0f; }
+  const int E = p.E, k = p.k;
   my_id = -1;
   my_g = 0.0f;
-  if (t >= p.T) return;
-  const int E = p.E, k = p.k;
-  if (nv > 0) {                                          // lanes past E read nothing
-    if constexpr (BF16)
-      load_bf16<J, VEC>(static_cast<const uint16_t*>(p.logits) + (size_t)t * E + e0, nv, x);
-    else
-      load_f32<J, VEC>(static_cast<const float*>(p.logits) + (size_t)t * E + e0, nv, x);
-    if (p.grad_scores != nullptr) load_f32<J, VEC>(p.grad_scores + (size_t)t * E + e0, nv, h);
+  if constexpr (HW) {
+    const size_t q = (size_t)t * k + (lane_c < k ? lane_c : k - 1);
+    my_id = p.ids[q];
+    my_g = p.grad_weights[q];
   }
-  if (p.grad_weights != nullptr && lane_c < k) {
-    my_id = p.ids[(size_t)t * k + lane_c];
-    my_g = p.grad_weights[(size_t)t * k + lane_c] * p.scale;
+  const size_t row = (size_t)t * E + (nv > 0 ? e0 : 0);
+  if constexpr (BF16)
+    load_bf16<J, VEC>(static_cast<const uint16_t*>(p.logits) + row, nv, x);
+  else
+    load_f32<J, VEC>(static_cast<const float*>(p.logits) + row, nv, x);
+#pragma unroll
+  for (int j = 0; j < J; ++j) h[j] = 0.0f;
+  if constexpr (HS) {
+    load_f32<J, VEC>(p.grad_scores + row, nv, h);
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+      if (j >= nv) h[j] = 0.0f;                          // lanes past E read the row start
+  }
+  if constexpr (HW) {
+    if (lane_c >= k) {
+      my_id = -1;
+      my_g = 0.0f;
+    }
+    my_g *= p.scale;
   }
 }
 
 // One token's gradient row, from its inputs; stored with streaming stores.
-template <int J, int L, bool VEC>
+template <int J, int L, bool VEC, bool HW, bool HS>
 __device__ __forceinline__ void token_grad(const RouteBwdParams& p, int t, bool tv, int lane, int e0,
                                            int nv, float (&x)[J], const float (&h)[J], int my_id,
                                            float my_g) {
@@ -142,7 +158,7 @@ __device__ __forceinline__ void token_grad(const RouteBwdParams& p, int t, bool 
     }
   }
   float pz[J];                                           // softmax over E (0 outside E)
-  if (!sigmoid && (p.mode == kBwdSoftmaxPre || p.grad_scores != nullptr)) {
+  if (!sigmoid && (p.mode == kBwdSoftmaxPre || HS)) {
     float m = kNegInf;
 #pragma unroll
     for (int j = 0; j < J; ++j) m = fmaxf(m, x[j]);
@@ -155,7 +171,7 @@ __device__ __forceinline__ void token_grad(const RouteBwdParams& p, int t, bool 
     for (int j = 0; j < J; ++j) pz[j] *= inv;
   }
 
-  if (p.grad_weights != nullptr) {
+  if constexpr (HW) {
     // the chosen experts' scaled weight gradients, at their owner lanes
     float g[J];
     uint32_t sel = 0;
@@ -241,7 +257,7 @@ __device__ __forceinline__ void token_grad(const RouteBwdParams& p, int t, bool 
     }
   }
 
-  if (p.grad_scores != nullptr) {
+  if constexpr (HS) {
     if (sigmoid) {                                       // q = s / sum_E s
       float Z = 0.0f;
 #pragma unroll
@@ -268,7 +284,7 @@ __device__ __forceinline__ void token_grad(const RouteBwdParams& p, int t, bool 
 
 // A token per cluster of L lanes (64 / L tokens per wavefront): token
 // (4 b + w) (64 / L) + lane / L.  Clusters past T compute but store nothing.
-template <bool BF16, int J, int L, bool VEC>
+template <bool BF16, int J, int L, bool VEC, bool HW, bool HS>
 __global__ void __launch_bounds__(kBwdThreads) route_bwd_kernel(RouteBwdParams p) {
   constexpr int kTpw = 64 / L;
   const int lane = threadIdx.x & 63;
@@ -280,16 +296,24 @@ __global__ void __launch_bounds__(kBwdThreads) route_bwd_kernel(RouteBwdParams p
   const int nv = min(J, max(0, p.E - e0));               // this lane's experts
   float x[J], h[J], g;
   int id;
-  load_token<BF16, J, VEC>(p, tv ? t : p.T, lane & (L - 1), e0, nv, x, h, id, g);
-  token_grad<J, L, VEC>(p, t, tv, lane, e0, nv, x, h, id, g);
+  load_token<BF16, J, VEC, HW, HS>(p, tv ? t : p.T - 1, lane & (L - 1), e0, nv, x, h, id, g);
+  token_grad<J, L, VEC, HW, HS>(p, t, tv, lane, e0, nv, x, h, id, g);
+}
+
+template <bool BF16, int J, int L, bool VEC>
+static void launch_bwd_v(const RouteBwdParams& p, dim3 grid, hipStream_t s) {
+  const bool hw = p.grad_weights != nullptr, hs = p.grad_scores != nullptr;   // one at least
+  if (hw && hs) MOE_LAUNCH((route_bwd_kernel<BF16, J, L, VEC, true, true>), grid, dim3(kBwdThreads), 0, s, p);
+  else if (hw) MOE_LAUNCH((route_bwd_kernel<BF16, J, L, VEC, true, false>), grid, dim3(kBwdThreads), 0, s, p);
+  else MOE_LAUNCH((route_bwd_kernel<BF16, J, L, VEC, false, true>), grid, dim3(kBwdThreads), 0, s, p);
 }
 
 template <bool BF16, int J, int L>
 static hipError_t launch_bwd_j(const RouteBwdParams& p, bool vec, hipStream_t s) {
   const int per_block = kBwdThreads / 64 * (64 / L);
   const dim3 grid((p.T + per_block - 1) / per_block);
-  if (vec) MOE_LAUNCH((route_bwd_kernel<BF16, J, L, true>), grid, dim3(kBwdThreads), 0, s, p);
-  else MOE_LAUNCH((route_bwd_kernel<BF16, J, L, false>), grid, dim3(kBwdThreads), 0, s, p);
+  if (vec) launch_bwd_v<BF16, J, L, true>(p, grid, s);
+  else launch_bwd_v<BF16, J, L, false>(p, grid, s);
   return hipGetLastError();
 }
 

@@ -62,8 +62,11 @@ __global__ void counts_kernel(int32_t* __restrict__ super_rows, int num_super, i
 constexpr int kScatterThreads = 256;
 constexpr int kDoneLanes = 16;          // sub-counters of the block count
 constexpr int kDoneStride = 64;         // 256 bytes apart: separate cache lines
-constexpr int kScatterPairsPerThread = kTokensPerBlock * 64 / kScatterThreads;   // k <= 64
 
+// NP = (token, choice) pairs per thread: 64 k / kScatterThreads rounded up to
+// a power of two (k <= 4, 8, 16, 32, 64).  The ids are loaded unconditionally
+// (clamped index) so that all NP loads are in flight together.
+template <int NP>
 __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int last_block;
@@ -81,13 +84,16 @@ __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams 
   const int t0 = blk * kTokensPerBlock;
   const int valid_pairs = min(npairs, (p.T - t0) * k);
 
-  // all global reads first
-  int idv[kScatterPairsPerThread];
+  // all global reads first (a block always holds a token: index 0 is in bounds)
+  int idv[NP];
 #pragma unroll
-  for (int i = 0; i < kScatterPairsPerThread; ++i) {
+  for (int i = 0; i < NP; ++i) {
     const int q = tid + i * kScatterThreads;
-    idv[i] = q < valid_pairs ? p.ids[(size_t)t0 * k + q] - p.off : -1;
+    idv[i] = p.ids[(size_t)t0 * k + (q < valid_pairs ? q : 0)];
   }
+#pragma unroll
+  for (int i = 0; i < NP; ++i)
+    idv[i] = tid + i * kScatterThreads < valid_pairs ? idv[i] - p.off : -1;
   const int grp = blk / p.group_blocks;
   const int g0 = grp * p.group_blocks;
   for (int e = tid; e < El; e += kScatterThreads) {
@@ -144,7 +150,7 @@ __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams 
     }
   }
 #pragma unroll
-  for (int i = 0; i < kScatterPairsPerThread; ++i) {
+  for (int i = 0; i < NP; ++i) {
     const int q = tid + i * kScatterThreads;
     const int el = idv[i];
     if (el >= 0 && el < El) atomicOr(&msk[el], 1ull << ((q * p.k_magic) >> 20));
@@ -153,7 +159,7 @@ __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams 
   const int total = po[El];
 
 #pragma unroll
-  for (int i = 0; i < kScatterPairsPerThread; ++i) {
+  for (int i = 0; i < NP; ++i) {
     const int q = tid + i * kScatterThreads;
     if (q >= valid_pairs) continue;
     const int tl = (int)((q * p.k_magic) >> 20);
@@ -266,7 +272,13 @@ hipError_t launch_counts(int32_t* super_rows, int num_super, int El, int32_t* co
 size_t scatter_lds_bytes(int El) { return (size_t)El * 8 + (size_t)(El + 1) * 4 + (size_t)El * 8; }
 
 hipError_t launch_scatter(const ScatterParams& p, int nb, hipStream_t s) {
-  MOE_LAUNCH(scatter_kernel, dim3(nb), dim3(kScatterThreads), scatter_lds_bytes(p.El), s, p);
+  const size_t lds = scatter_lds_bytes(p.El);
+  const int np = (kTokensPerBlock * p.k + kScatterThreads - 1) / kScatterThreads;
+  if (np <= 1) MOE_LAUNCH(scatter_kernel<1>, dim3(nb), dim3(kScatterThreads), lds, s, p);
+  else if (np <= 2) MOE_LAUNCH(scatter_kernel<2>, dim3(nb), dim3(kScatterThreads), lds, s, p);
+  else if (np <= 4) MOE_LAUNCH(scatter_kernel<4>, dim3(nb), dim3(kScatterThreads), lds, s, p);
+  else if (np <= 8) MOE_LAUNCH(scatter_kernel<8>, dim3(nb), dim3(kScatterThreads), lds, s, p);
+  else MOE_LAUNCH(scatter_kernel<16>, dim3(nb), dim3(kScatterThreads), lds, s, p);
   return hipGetLastError();
 }
 
