@@ -114,6 +114,8 @@ SMALL = [
     (512, 10, "softmax", True, 0, 0, 2, True, 1.0, "bf16", None),
     (1024, 16, "softmax", False, 0, 0, 2, True, 1.0, "f32", None),
     (2048, 40, "sigmoid", False, 16, 8, 2, True, 1.0, "bf16", 0.01),
+    (96, 24, "softmax", True, 0, 0, 2, True, 1.0, "bf16", None),    # 17 <= k <= 32
+    (128, 32, "sigmoid", False, 0, 0, 2, False, 1.0, "f32", 0.01),  # k = 32: list capacity
     (256, 64, "softmax", True, 0, 0, 2, True, 1.0, "bf16", None),   # k = 64
 ]
 
