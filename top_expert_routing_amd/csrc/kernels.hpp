@@ -38,6 +38,12 @@ constexpr int kMaxSuperRows = 64;
 
 template <int LPT>
 constexpr int kRouteBlock = (LPT * 64 < 512) ? LPT * 64 : 512;
+// Wavefronts per SIMD the register allocation must allow: with up to 8 lanes
+// per token the kernel fits in 128 VGPRs, so four wavefronts share a SIMD
+// (a 65536-token call then runs in one round: 4096 wavefronts on 1024 SIMDs);
+// wider clusters hold more per-lane state and are left unconstrained.
+template <int LPT>
+constexpr int kRouteMinWaves = LPT <= 8 ? 4 : 1;
 
 // Score variants, one kernel instance each: sigmoid (bias optional), softmax
 // without bias, softmax with bias (before or after top-k is a run-time flag).

@@ -373,7 +373,8 @@ __device__ void permute_in_block(const RouteParams& p, const uint64_t* hmask, in
 }
 
 template <int LPT, int EPL, bool BF16, int VAR>
-__global__ void __launch_bounds__(kRouteBlock<LPT>) route_kernel(RouteParams p) {
+__global__ void __launch_bounds__(kRouteBlock<LPT>)
+    __attribute__((amdgpu_waves_per_eu(kRouteMinWaves<LPT>))) route_kernel(RouteParams p) {
   constexpr int BLOCK = kRouteBlock<LPT>;
   constexpr int NCL = BLOCK / LPT;          // clusters (tokens in flight) per block
   constexpr int TPC = kTokensPerBlock / NCL;
