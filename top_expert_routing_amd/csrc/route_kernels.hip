@@ -66,7 +66,10 @@ constexpr int kDoneStride = 64;         // 256 bytes apart: separate cache lines
 // NP = (token, choice) pairs per thread: 64 k / kScatterThreads rounded up to
 // a power of two (k <= 4, 8, 16, 32, 64).  The ids are loaded unconditionally
 // (clamped index) so that all NP loads are in flight together.
-template <int NP>
+// S = 2: the counting rows and per-block rows of an expert are split between
+// two threads (every other row; El <= kScatterThreads / 2), so that up to 32
+// counting rows and 32 per-block rows need one round of loads, not two.
+template <int NP, int S>
 __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int last_block;
@@ -96,26 +99,65 @@ __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams 
     idv[i] = tid + i * kScatterThreads < valid_pairs ? idv[i] - p.off : -1;
   const int grp = blk / p.group_blocks;
   const int g0 = grp * p.group_blocks;
-  for (int e = tid; e < El; e += kScatterThreads) {
-    int tot = 0, pre = 0;
-    // 16 counting rows and 16 per-block rows in flight at a time
-    for (int r0 = 0; r0 < p.num_super || g0 + r0 < blk; r0 += 16) {
-      int sv[16], hv[16];
+  if constexpr (S == 1) {
+    for (int e = tid; e < El; e += kScatterThreads) {
+      int tot = 0, pre = 0;
+      // 16 counting rows and 16 per-block rows in flight at a time
+      for (int r0 = 0; r0 < p.num_super || g0 + r0 < blk; r0 += 16) {
+        int sv[16], hv[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sv[i] = r0 + i < p.num_super ? p.super_rows[(size_t)(r0 + i) * El + e] : 0;
-        hv[i] = g0 + r0 + i < blk ? p.hist[(size_t)(g0 + r0 + i) * El + e] : 0;
+        for (int i = 0; i < 16; ++i) {
+          sv[i] = r0 + i < p.num_super ? p.super_rows[(size_t)(r0 + i) * El + e] : 0;
+          hv[i] = g0 + r0 + i < blk ? p.hist[(size_t)(g0 + r0 + i) * El + e] : 0;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          tot += sv[i];
+          pre += (r0 + i < grp ? sv[i] : 0) + hv[i];
+        }
       }
+      cnt[e] = tot;
+      base[e] = pre;
+      po[e] = (tot + tile - 1) & ~(tile - 1);
+      msk[e] = 0;
+    }
+  } else {
+    // thread h * El + e sums rows h, h + 2, ... of expert e; the second half's
+    // sums reach the first half through LDS
+    int* part = cnt + El;                                // 2 El: tot, pre of half 1
+    const int h = tid >= El ? 1 : 0;
+    const int e = tid - h * El;
+    int tot = 0, pre = 0;
+    if (e < El) {
+      for (int r0 = h; r0 < p.num_super || g0 + r0 < blk; r0 += 32) {
+        int sv[16], hv[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        tot += sv[i];
-        pre += (r0 + i < grp ? sv[i] : 0) + hv[i];
+        for (int i = 0; i < 16; ++i) {
+          const int r = r0 + 2 * i;
+          sv[i] = r < p.num_super ? p.super_rows[(size_t)r * El + e] : 0;
+          hv[i] = g0 + r < blk ? p.hist[(size_t)(g0 + r) * El + e] : 0;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = r0 + 2 * i;
+          tot += sv[i];
+          pre += (r < grp ? sv[i] : 0) + hv[i];
+        }
+      }
+      if (h == 1) {
+        part[e] = tot;
+        part[El + e] = pre;
       }
     }
-    cnt[e] = tot;
-    base[e] = pre;
-    po[e] = (tot + tile - 1) & ~(tile - 1);
-    msk[e] = 0;
+    __syncthreads();
+    if (h == 0 && e < El) {
+      tot += part[e];
+      pre += part[El + e];
+      cnt[e] = tot;
+      base[e] = pre;
+      po[e] = (tot + tile - 1) & ~(tile - 1);
+      msk[e] = 0;
+    }
   }
   if (tid == 0) po[El] = 0;
   __syncthreads();
@@ -269,16 +311,26 @@ hipError_t launch_counts(int32_t* super_rows, int num_super, int El, int32_t* co
   return hipGetLastError();
 }
 
-size_t scatter_lds_bytes(int El) { return (size_t)El * 8 + (size_t)(El + 1) * 4 + (size_t)El * 8; }
+// msk (El u64), po (El + 1), base, cnt (El each), and the split partials (2 El)
+size_t scatter_lds_bytes(int El) { return (size_t)El * 8 + (size_t)(El + 1) * 4 + (size_t)El * 16; }
 
-hipError_t launch_scatter(const ScatterParams& p, int nb, hipStream_t s) {
+template <int S>
+static void launch_scatter_s(const ScatterParams& p, int nb, hipStream_t s) {
   const size_t lds = scatter_lds_bytes(p.El);
   const int np = (kTokensPerBlock * p.k + kScatterThreads - 1) / kScatterThreads;
-  if (np <= 1) MOE_LAUNCH(scatter_kernel<1>, dim3(nb), dim3(kScatterThreads), lds, s, p);
-  else if (np <= 2) MOE_LAUNCH(scatter_kernel<2>, dim3(nb), dim3(kScatterThreads), lds, s, p);
-  else if (np <= 4) MOE_LAUNCH(scatter_kernel<4>, dim3(nb), dim3(kScatterThreads), lds, s, p);
-  else if (np <= 8) MOE_LAUNCH(scatter_kernel<8>, dim3(nb), dim3(kScatterThreads), lds, s, p);
-  else MOE_LAUNCH(scatter_kernel<16>, dim3(nb), dim3(kScatterThreads), lds, s, p);
+  if (np <= 1) MOE_LAUNCH((scatter_kernel<1, S>), dim3(nb), dim3(kScatterThreads), lds, s, p);
+  else if (np <= 2) MOE_LAUNCH((scatter_kernel<2, S>), dim3(nb), dim3(kScatterThreads), lds, s, p);
+  else if (np <= 4) MOE_LAUNCH((scatter_kernel<4, S>), dim3(nb), dim3(kScatterThreads), lds, s, p);
+  else if (np <= 8) MOE_LAUNCH((scatter_kernel<8, S>), dim3(nb), dim3(kScatterThreads), lds, s, p);
+  else MOE_LAUNCH((scatter_kernel<16, S>), dim3(nb), dim3(kScatterThreads), lds, s, p);
+}
+
+hipError_t launch_scatter(const ScatterParams& p, int nb, hipStream_t s) {
+  // split the rows when an expert has more than 16 counting or per-block rows
+  // to read and two threads per expert fit the block
+  const int rows = p.num_super > p.group_blocks - 1 ? p.num_super : p.group_blocks - 1;
+  if (2 * p.El <= kScatterThreads && rows > 16) launch_scatter_s<2>(p, nb, s);
+  else launch_scatter_s<1>(p, nb, s);
   return hipGetLastError();
 }
 
