@@ -664,13 +664,16 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>)
       }
       C = k;
     }
-    // ranking tier: the smallest of 4..64 that holds every cluster's list in
-    // this wavefront (uniform, so the wavefront takes one path); the entries
+    // ranking tier: the smallest of 4, 8, 12, 16, 24, 32, 64 that holds every
+    // cluster's list in this wavefront (uniform, so the wavefront takes one
+    // path; the cost is about tier^2 / LPT compares per lane); the entries
     // between C and the tier are zeroed
     int tier;
     if (__ballot(C > 4) == 0ull) tier = 4;
     else if (__ballot(C > 8) == 0ull) tier = 8;
+    else if (__ballot(C > 12) == 0ull) tier = 12;
     else if (__ballot(C > 16) == 0ull) tier = 16;
+    else if (__ballot(C > 24) == 0ull) tier = 24;
     else if (__ballot(C > 32) == 0ull) tier = 32;
     else tier = 64;
     for (int j = C + lane_c; j < tier; j += LPT) mycand[j] = 0ull;
@@ -679,7 +682,9 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>)
     // ---- order the candidates, emit the top k ---------------------------------
     if (tier == 4) rank_tier<LPT, 4>(mycand, C, k, lane_c, myselidx);
     else if (tier == 8) rank_tier<LPT, 8>(mycand, C, k, lane_c, myselidx);
+    else if (tier == 12) rank_tier<LPT, 12>(mycand, C, k, lane_c, myselidx);
     else if (tier == 16) rank_tier<LPT, 16>(mycand, C, k, lane_c, myselidx);
+    else if (tier == 24) rank_tier<LPT, 24>(mycand, C, k, lane_c, myselidx);
     else if (tier == 32) rank_tier<LPT, 32>(mycand, C, k, lane_c, myselidx);
     else rank_tier<LPT, 64>(mycand, C, k, lane_c, myselidx);
     wave_lds_sync();
