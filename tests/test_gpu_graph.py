@@ -156,3 +156,38 @@ def test_front_end_graph_replays():
                               *o, workspace=ws2)
         torch.cuda.synchronize()
         assert torch.equal(o[1], ids_r), rep
+
+
+def test_concurrent_streams():
+    """Calls on different streams with their own workspaces run at the same
+    time (the library keeps no per-call state outside the workspace); each
+    result equals the same call made alone."""
+    import torch
+    import top_expert_routing_amd as mr
+    w1 = with_overrides(WORKLOADS["deepseek_v3_like"], T=8192)
+    w2 = with_overrides(WORKLOADS["qwen_moe_like"], T=8192)
+    calls = []
+    for w, seed in ((w1, 7400), (w2, 7401)):
+        logits, bias = route_inputs(w, T=w.T, seed=seed)
+        x = to_dev(logits, w.logits_dtype)
+        b = to_dev(bias, w.bias_dtype) if bias is not None else None
+        args = _args(mr, w, w.T)
+        ref = mr.route_permute(args, x, b, tile=w.tile)
+        calls.append((w, args, x, b, ref))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in calls]
+    outs = [mr.alloc_route_outputs(args, DEV, permute=True, tile=w.tile)
+            for w, args, _, _, _ in calls]
+    log("[gpu] two routing calls on two streams, ten rounds")
+    for rep in range(10):
+        for (w, args, x, b, _), s, o in zip(calls, streams, outs):
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                o.topk_ids.fill_(-7)
+                mr.route_permute(args, x, b, tile=w.tile, out=o)
+        torch.cuda.synchronize()
+        for (w, _, _, _, ref), o in zip(calls, outs):
+            total = int(ref.total_num_padded_tokens.item())
+            for f in _ROUTE_FIELDS:
+                assert torch.equal(getattr(o, f), getattr(ref, f)), (w.name, rep, f)
+            assert torch.equal(o.permuted_idx_to_token_idx[:total], ref.permuted_idx_to_token_idx[:total])
