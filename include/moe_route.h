@@ -361,8 +361,10 @@ int64_t moe_max_tiles(int32_t T, int32_t k, int32_t local_num_experts, int32_t t
  * events with the kernel's own start and end; a kind of several kernels
  * (AUX_FWD, FRONT_END) is bracketed by event records.  moe_profile_read() waits for the recorded events of one kernel kind and
  * returns their summed elapsed time and launch count since
- * moe_profile_begin().  Kernel kinds: MOE_KERNEL_*.  Not for use while
- * capturing a HIP graph. */
+ * moe_profile_begin().  Kernel kinds: MOE_KERNEL_*.  The profiling state is
+ * process-wide (one switch and one set of totals, guarded by a mutex, so the
+ * calls are thread-safe; launches from every thread are counted).  Not for
+ * use while capturing a HIP graph. */
 typedef enum moe_kernel_kind {
   MOE_KERNEL_ROUTE = 0,
   MOE_KERNEL_COUNTS = 1,
