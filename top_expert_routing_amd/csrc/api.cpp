@@ -267,6 +267,7 @@ moe::RouteParams make_params(const moe_route_args& a, const Shape& sh, const voi
   p.vec = ((size_t)a.num_experts * esz) % 16 == 0 && aligned(logits, 16) &&
           (sh.epl * esz) % 16 == 0;
   p.bias_vec = bias != nullptr && aligned(bias, 16);
+  p.scores_vec = scores != nullptr && aligned(scores, 16);
   p.loc_off = loc_off;
   p.loc_n = loc_n;
   p.hmask_len = super_rows != nullptr ? (loc_n + 1) & ~1 : 0;

@@ -68,6 +68,7 @@ struct RouteParams {
   float scale;
   int vec;                // 16-byte vector loads of logits allowed
   int bias_vec;           // 16-byte aligned float32 bias
+  int scores_vec;         // scores 16-byte aligned (16-byte stores of whole rows)
   int loc_off, loc_n;
   int hmask_len;          // LDS u64 words for the block bitmask (even)
   int cap;                // candidate list capacity per token (>= k)

@@ -710,31 +710,51 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>)
       ec.inv_s = inv_s;
       emit_selected<LPT, BF16, VAR>(ec, myselidx, rowc);
     }
-    if (tv) {
-      // ---- full-E scores for the aux loss --------------------------------------------
-      if (p.scores != nullptr) {
+    // ---- full-E scores for the aux loss --------------------------------------------
+    if (p.scores != nullptr) {
+      const float inv_ss = VAR == kVarSigmoid ? fast_rcp(ssum) : 0.0f;
+      float v[EPL];
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        if constexpr (VAR == kVarSigmoid) v[i] = x[i] * inv_ss;
+        else if (VAR == kVarSoftmaxBias && pre) v[i] = x[i];
+        else v[i] = exp_f32(x[i] - m) * inv_s;
+      }
+      // The wavefront's 64 / LPT tokens are consecutive, so their score rows
+      // are one span of memory.  They pass through the wavefront's own rows in
+      // LDS (free once the emission has read them), a chunk of tokens at a
+      // time, so that each store instruction writes 64 consecutive 16-byte
+      // pieces instead of 64 pieces one lane-slice apart.  Needs E % 4 == 0,
+      // a 16-byte aligned scores array and room for one row; else each lane
+      // stores its slice.
+      constexpr int TPW = 64 / LPT;
+      const int chunk = ((E & 3) == 0 && p.scores_vec) ? (TPW * L.row_stride) / E : 0;
+      if (chunk >= 1) {
+        const int lw = tid & 63;
+        const int tw = lw / LPT;                              // token within the wavefront
+        const int tfirst = t - tw;
+        float* stage = reinterpret_cast<float*>(smem + L.row) + (cl - tw) * L.row_stride;
+        for (int c0 = 0; c0 < TPW; c0 += chunk) {
+          wave_lds_sync();                                    // the rows, or the last chunk, are read
+          if (tw >= c0 && tw < c0 + chunk) {
+            float* dst = stage + (tw - c0) * E + e0;
+#pragma unroll
+            for (int i = 0; i < EPL; i += 4)
+              if (e0 + i < E)
+                *reinterpret_cast<f32x4*>(dst + i) = f32x4{v[i], v[i + 1], v[i + 2], v[i + 3]};
+          }
+          wave_lds_sync();
+          const int ntok = min(chunk, TPW - c0);
+          const int nval = max(0, min(ntok, p.T - (tfirst + c0)));   // tokens below T
+          const f32x4* src = reinterpret_cast<const f32x4*>(stage);
+          f32x4* out = reinterpret_cast<f32x4*>(p.scores + (size_t)(tfirst + c0) * E);
+          for (int q = lw; q < nval * (E / 4); q += 64) out[q] = src[q];
+        }
+      } else if (tv) {
         float* srow = p.scores + (size_t)t * E;
-        const float inv_ss = VAR == kVarSigmoid ? fast_rcp(ssum) : 0.0f;
-        float v[EPL];
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-          if constexpr (VAR == kVarSigmoid) v[i] = x[i] * inv_ss;
-          else if (VAR == kVarSoftmaxBias && pre) v[i] = x[i];
-          else v[i] = exp_f32(x[i] - m) * inv_s;
-        }
-        // 16-byte stores when rows are 16-byte aligned (E % 4 == 0; e0 and
-        // EPL are multiples of 4, so a group of four is all in or all out):
-        // a lane's scalar stores would each touch another cache line.
-        if ((E & 3) == 0) {
-#pragma unroll
-          for (int i = 0; i < EPL; i += 4)
-            if (e0 + i < E)
-              *reinterpret_cast<f32x4*>(srow + e0 + i) = f32x4{v[i], v[i + 1], v[i + 2], v[i + 3]};
-        } else {
-#pragma unroll
-          for (int i = 0; i < EPL; ++i)
-            if (e0 + i < E) srow[e0 + i] = v[i];
-        }
+        for (int i = 0; i < EPL; ++i)
+          if (e0 + i < E) srow[e0 + i] = v[i];
       }
     }
     wave_lds_sync();
