@@ -330,17 +330,39 @@ def cpu_baseline(w, sample_T: int, seconds: float):
     import oracle
     from workloads import route_inputs
     logits, bias = route_inputs(w, T=sample_T)
-    reps, t_total = 0, 0.0
-    while t_total < seconds or reps < 1:
+    times = []
+    while sum(times) < seconds or not times:
         t0 = time.perf_counter()
         r = oracle.route(logits, w.logits_dtype, w.k, score_fn=w.score_fn,
                          pre_softmax=w.pre_softmax, n_group=w.n_group,
                          topk_group=w.topk_group, group_topn=w.group_topn, renorm=w.renorm,
                          scale=w.scale, bias=bias, bias_dtype=w.bias_dtype)
         oracle.permute(r.ids, w.tile, num_experts=w.E)
-        t_total += time.perf_counter() - t0
-        reps += 1
-    return sample_T * reps / t_total, reps, t_total
+        times.append(time.perf_counter() - t0)
+    t_total = sum(times)
+    return sample_T * len(times) / t_total, len(times), t_total, sorted(times)[len(times) // 2]
+
+
+def host_info():
+    """The host the CPU baseline ran on: CPU model, CPUs, affinity, BLAS threads."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [{"api": d.get("internal_api"), "threads": d.get("num_threads")}
+                for d in threadpool_info()]
+    except Exception:                                   # threadpoolctl absent or failing
+        pass
+    return {"cpu_model": model, "cpu_count": os.cpu_count(),
+            "affinity": len(os.sched_getaffinity(0)), "blas": blas}
 
 
 def main():
@@ -471,11 +493,12 @@ def main():
     cpu = None
     if not a.no_cpu_baseline:
         sample_T = min(T, 4096)
-        tps, reps, secs = cpu_baseline(w, sample_T, a.cpu_seconds)
+        tps, reps, secs, med = cpu_baseline(w, sample_T, a.cpu_seconds)
         cpu = {"value": tps, "unit": "tokens/s", "cores": 1, "kind": "oracle",
                "sample": f"{sample_T} of {T} tokens of the same workload, oracle route + "
-                         f"permute, {reps} repetitions in {secs:.1f} s; NumPy single-threaded "
-                         f"(host reports {os.cpu_count()} CPUs)"}
+                         f"permute, {reps} repetitions in {secs:.1f} s (median "
+                         f"{med * 1e3:.1f} ms each); NumPy elementwise work on one core",
+               "median_tokens_per_s": sample_T / med, "host": host_info()}
 
     line = {
         "metric": "routed tokens/sec + achieved HBM GB/s, T=16384 E=256 k=8 grouped sigmoid",
