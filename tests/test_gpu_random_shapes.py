@@ -1,0 +1,71 @@
+"""GPU parity on seeded random routing configurations.
+
+Each case draws, from its own seed, a method (softmax before/after top-k or
+sigmoid, grouping with a top-1 or top-2 group score, renormalisation, scale,
+an optional bias), shapes (E up to 2048, k up to 64, a ragged T), dtypes
+(float32/bfloat16 logits, float32/bfloat16 weights), a tile size, an optional
+local-expert shard and the optional full-E scores, and runs moe_route_permute
+against the oracle under the usual parity rules.  Configurations outside the
+kernels' stated limits (MOE_EUNSUPPORTED) are skipped with the limit named.
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+
+from test_gpu_route import mr, run_and_check
+from workloads import RouteWorkload, route_inputs
+
+pytestmark = pytest.mark.gpu
+CASES = int(os.environ.get("MOE_RANDOM_CASES", "48"))
+
+
+def _config(i: int):
+    rng = np.random.default_rng(9000 + i)
+    score_fn = str(rng.choice(["softmax", "sigmoid"]))
+    pre = bool(rng.integers(2)) if score_fn == "softmax" else False
+    if rng.random() < 0.4:
+        gsz = int(rng.choice([4, 8, 16, 32, 64]))
+        n_group = int(rng.choice([2, 4, 8, 16]))
+        while gsz * n_group > 2048:
+            n_group //= 2
+        E = gsz * n_group
+        topk_group = int(rng.integers(1, n_group))
+        topn = int(rng.choice([1, 2]))
+        kmax = min(64, topk_group * gsz)
+    else:
+        E = int(rng.choice([8, 16, 24, 32, 60, 64, 96, 100, 128, 160, 256, 384, 512, 1000,
+                            1024, 2048]))
+        n_group = topk_group = 0
+        topn = 2
+        kmax = min(64, E)
+    k = int(rng.integers(1, kmax + 1))
+    T = int(rng.integers(1, max(2, min(2500, 2_000_000 // E))))
+    tile = int(rng.choice([1, 2, 4, 8, 16, 64, 256]))
+    bias_std = float(rng.choice([0.01, 0.1])) if rng.random() < 0.5 else None
+    w = RouteWorkload(name=f"random{i}", seed=9100 + i, T=T, E=E, k=k, score_fn=score_fn,
+                      pre_softmax=pre, n_group=n_group, topk_group=topk_group, group_topn=topn,
+                      renorm=bool(rng.integers(2)), scale=float(rng.choice([1.0, 2.5])),
+                      logits_dtype=str(rng.choice(["f32", "bf16"])),
+                      logits_std=float(rng.choice([0.5, 1.0, 2.0, 4.0])), bias_std=bias_std,
+                      bias_dtype=str(rng.choice(["f32", "bf16"])), tile=tile)
+    off, n_loc = 0, None
+    if rng.random() < 0.25 and E > 1:
+        off = int(rng.integers(0, E))
+        n_loc = int(rng.integers(1, E - off + 1))
+    return (w, str(rng.choice(["f32", "bf16"])), bool(rng.random() < 0.3), off, n_loc)
+
+
+@pytest.mark.parametrize("i", range(CASES))
+def test_random_configuration(i):
+    w, wdt, scores, off, n_loc = _config(i)
+    logits, bias = route_inputs(w)
+    try:
+        run_and_check(w, logits, bias, f"random {i}", weights_dtype=wdt, scores=scores,
+                      off=off, n_loc=n_loc)
+    except mr.MoeError as e:
+        if e.status == mr.MOE_EUNSUPPORTED:
+            pytest.skip(f"outside the kernels' limits: {e}")
+        raise
