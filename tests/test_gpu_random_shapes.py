@@ -69,3 +69,20 @@ def test_random_configuration(i):
         if e.status == mr.MOE_EUNSUPPORTED:
             pytest.skip(f"outside the kernels' limits: {e}")
         raise
+
+
+FE_CASES = int(os.environ.get("MOE_RANDOM_FE_CASES", "24"))
+
+
+@pytest.mark.parametrize("i", range(FE_CASES))
+def test_random_front_end(i):
+    # decode front end on random shapes within its limits: T <= 128, H a
+    # multiple of 128, E a multiple of 16 up to 512
+    from test_gpu_front_end import run_front_end
+    from workloads import FRONT_END
+    rng = np.random.default_rng(9500 + i)
+    T = int(rng.integers(1, 129))
+    H = 128 * int(rng.integers(1, 65))
+    E = 16 * int(rng.integers(1, 33))
+    run_front_end(FRONT_END, T, H, E, seed=9600 + i, act=str(rng.choice(["sigmoid", "softmax"])),
+                  dtype=str(rng.choice(["bf16", "f16"])), rbias=bool(rng.integers(2)))
