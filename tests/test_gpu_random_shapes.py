@@ -86,3 +86,54 @@ def test_random_front_end(i):
     E = 16 * int(rng.integers(1, 33))
     run_front_end(FRONT_END, T, H, E, seed=9600 + i, act=str(rng.choice(["sigmoid", "softmax"])),
                   dtype=str(rng.choice(["bf16", "f16"])), rbias=bool(rng.integers(2)))
+
+
+OTHER_CASES = int(os.environ.get("MOE_RANDOM_OTHER_CASES", "16"))
+
+
+@pytest.mark.parametrize("i", range(OTHER_CASES))
+def test_random_backward(i):
+    # routing backward (E <= 512): weight and/or score gradients, every mode
+    from test_gpu_route_backward import check_backward
+    rng = np.random.default_rng(9700 + i)
+    score_fn = str(rng.choice(["softmax", "sigmoid"]))
+    E = int(rng.choice([8, 16, 24, 32, 48, 64, 100, 128, 200, 256, 384, 512]))
+    k = int(rng.integers(1, min(E, 64) + 1))
+    w = RouteWorkload(name=f"bwd{i}", seed=9800 + i, T=1, E=E, k=k, score_fn=score_fn,
+                      pre_softmax=bool(rng.integers(2)) if score_fn == "softmax" else False,
+                      renorm=bool(rng.integers(2)), scale=float(rng.choice([1.0, 2.5])),
+                      logits_dtype=str(rng.choice(["f32", "bf16"])),
+                      logits_std=float(rng.choice([0.5, 1.0, 3.0])))
+    with_w = bool(rng.integers(2))
+    with_s = (not with_w) or bool(rng.integers(2))
+    T = int(rng.integers(1, 2000))
+    check_backward(w, T, 9900 + i, with_w=with_w, with_s=with_s, label=f"random {i}")
+
+
+@pytest.mark.parametrize("i", range(OTHER_CASES))
+def test_random_dense(i):
+    from test_gpu_dense import _route, check_dense
+    rng = np.random.default_rng(10000 + i)
+    E = int(rng.choice([8, 12, 64, 100, 128, 136, 256, 320, 512]))
+    k = int(rng.integers(1, min(E, 64) + 1))
+    T = int(rng.integers(1, 3000))
+    ids, wts = _route(T, E, k, 10100 + i)
+    probs = bool(rng.integers(2))
+    check_dense(ids, wts, E, w_dtype=str(rng.choice(["f32", "bf16"])),
+                want_probs=probs, want_map=(not probs) or bool(rng.integers(2)),
+                label=f"random {i}")
+
+
+@pytest.mark.parametrize("i", range(OTHER_CASES))
+def test_random_dispatch_combine(i):
+    from test_gpu_dispatch import check_combine, check_dispatch
+    rng = np.random.default_rng(10200 + i)
+    E = int(rng.choice([8, 16, 60, 128, 256]))
+    k = int(rng.integers(1, min(E, 16) + 1))
+    T = int(rng.integers(1, 600))
+    H = int(rng.choice([8, 24, 100, 512, 1024, 2880, 7168]))
+    tile = int(rng.choice([1, 4, 8, 16, 128]))
+    dtype = str(rng.choice(["bf16", "f32"]))
+    check_dispatch(T, E, k, H, tile, dtype, 10300 + i, label=f"random {i}")
+    check_combine(T, E, k, H, tile, dtype, 10400 + i, label=f"random {i}",
+                  w_dtype=str(rng.choice(["f32", "bf16"])))
