@@ -9,10 +9,10 @@
 //                    for a padding slot), 16-byte accesses, eight in flight
 //                    per lane.
 //   combine_kernel   one wavefront per token: out[t] = sum_j w[t, j] *
-//                    expert_out[expanded_idx_to_permuted_idx[t k + j]], the k
-//                    rows of a 512-element (bf16) or 256-element (f32) column
-//                    slab requested together, summed in choice order in
-//                    float32 (deterministic), rounded once (bf16: RNE).
+//                    expert_out[expanded_idx_to_permuted_idx[t k + j]], one
+//                    routed row at a time with up to 16 KiB of it requested
+//                    together, summed in choice order in float32
+//                    (deterministic), rounded once (bf16: RNE).
 // Both are HBM-bound row movers.
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -69,6 +69,10 @@ __global__ void __launch_bounds__(kMoveThreads)
 // One wavefront per token; BF16: bfloat16 rows (8 elements per lane per slab),
 // else float32 rows (4 per lane).  VEC: H a multiple of the lane width and
 // 16-byte aligned rows.
+#ifndef COMBINE_SLABS
+#define COMBINE_SLABS 16
+#endif
+
 template <bool BF16, bool VEC>
 __global__ void __launch_bounds__(kMoveThreads)
     combine_kernel(const void* __restrict__ expert_out, int T, int H, int k,
@@ -86,55 +90,48 @@ __global__ void __launch_bounds__(kMoveThreads)
                   : static_cast<const float*>(weights)[(size_t)t * k + lane];
   }
   constexpr int EPL = BF16 ? 8 : 4;                     // elements per lane per slab
-  constexpr int kMaxK = 64;
   if constexpr (VEC) {
-    constexpr int kSlabs = 2;                           // slabs whose rows are requested together
+    // One choice's row at a time, kSlabs 1 KiB column slabs of it requested
+    // together: long contiguous reads of each routed row gather best (a
+    // column strip of several rows at once measured slower)
+    constexpr int kSlabs = COMBINE_SLABS;
     for (int c0 = 0; c0 < H; c0 += kSlabs * 64 * EPL) {
       float acc[kSlabs][EPL];
 #pragma unroll
       for (int sl = 0; sl < kSlabs; ++sl)
 #pragma unroll
         for (int i = 0; i < EPL; ++i) acc[sl][i] = 0.0f;
-      // the k rows of these slabs, eight choices requested at a time, summed
-      // in choice order
-      for (int j0 = 0; j0 < k; j0 += 8) {
-        u32x4 r[kSlabs][8];
-        float wj[8];
+      // summed in choice order
+      for (int j = 0; j < k; ++j) {
+        const int slot = __builtin_amdgcn_readlane(my_slot, j);
+        if (slot < 0) continue;                         // uniform: a dropped choice
+        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), j));
+        u32x4 r[kSlabs];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int j = j0 + u < kMaxK ? j0 + u : 0;
-          const int slot = __builtin_amdgcn_readlane(my_slot, j);
-          const bool live = j0 + u < k && slot >= 0;
-          wj[u] = live ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), j)) : 0.0f;
-#pragma unroll
-          for (int sl = 0; sl < kSlabs; ++sl) {
-            const int c = c0 + sl * 64 * EPL + lane * EPL;
-            const size_t off = (size_t)slot * H + c;
-            r[sl][u] = (live && c < H)
-                           ? __builtin_nontemporal_load(
-                                 BF16 ? reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(expert_out) + off)
-                                      : reinterpret_cast<const u32x4*>(static_cast<const float*>(expert_out) + off))
-                           : u32x4{0, 0, 0, 0};
-          }
+        for (int sl = 0; sl < kSlabs; ++sl) {
+          const int c = c0 + sl * 64 * EPL + lane * EPL;
+          const size_t off = (size_t)slot * H + c;
+          r[sl] = c < H ? __builtin_nontemporal_load(
+                              BF16 ? reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(expert_out) + off)
+                                   : reinterpret_cast<const u32x4*>(static_cast<const float*>(expert_out) + off))
+                        : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
-        for (int sl = 0; sl < kSlabs; ++sl)
+        for (int sl = 0; sl < kSlabs; ++sl) {
+          if constexpr (BF16) {
+            const uint32_t wv[4] = {r[sl].x, r[sl].y, r[sl].z, r[sl].w};
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            if constexpr (BF16) {
-              const uint32_t wv[4] = {r[sl][u].x, r[sl][u].y, r[sl][u].z, r[sl][u].w};
-#pragma unroll
-              for (int h = 0; h < 4; ++h) {
-                acc[sl][2 * h] += wj[u] * bf16_lo(wv[h]);
-                acc[sl][2 * h + 1] += wj[u] * bf16_hi(wv[h]);
-              }
-            } else {
-              acc[sl][0] += wj[u] * __uint_as_float(r[sl][u].x);
-              acc[sl][1] += wj[u] * __uint_as_float(r[sl][u].y);
-              acc[sl][2] += wj[u] * __uint_as_float(r[sl][u].z);
-              acc[sl][3] += wj[u] * __uint_as_float(r[sl][u].w);
+            for (int h = 0; h < 4; ++h) {
+              acc[sl][2 * h] += wj * bf16_lo(wv[h]);
+              acc[sl][2 * h + 1] += wj * bf16_hi(wv[h]);
             }
+          } else {
+            acc[sl][0] += wj * __uint_as_float(r[sl].x);
+            acc[sl][1] += wj * __uint_as_float(r[sl].y);
+            acc[sl][2] += wj * __uint_as_float(r[sl].z);
+            acc[sl][3] += wj * __uint_as_float(r[sl].w);
           }
+        }
       }
 #pragma unroll
       for (int sl = 0; sl < kSlabs; ++sl) {
