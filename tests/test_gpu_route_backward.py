@@ -79,7 +79,8 @@ def test_backward_small_workloads(name):
 @pytest.mark.parametrize("E,k,T,dtype", [(16, 4, 1, "f32"), (64, 6, 257, "bf16"),
                                          (80, 8, 130, "f32"), (65, 5, 63, "bf16"),
                                          (256, 8, 4097, "bf16"), (512, 16, 300, "f32"),
-                                         (8, 8, 33, "f32")])
+                                         (8, 8, 33, "f32"), (128, 16, 515, "bf16"),
+                                         (120, 12, 77, "f32"), (128, 17, 64, "bf16")])
 def test_backward_modes_and_shapes(score_fn, pre, renorm, E, k, T, dtype):
     base = WORKLOADS["mixtral_like"]
     w = with_overrides(base, E=E, k=k, score_fn=score_fn, pre_softmax=pre, renorm=renorm,

@@ -12,8 +12,10 @@
 //
 //   grad_logits = d/dx ( sum_j g_j w'_j + sum_e h_e scores_e )
 //
-// A token per cluster of L lanes (L = 8/16/32 with four experts per lane for
-// E <= 32/64/128, else the whole wavefront with J = ceil(E / 64) per lane);
+// A token per cluster of L lanes (L = 8/16 with four experts per lane for
+// E <= 32/64, L = 16 with eight for E <= 128 (E a multiple of 8, k <= 16),
+// L = 32 with eight for E <= 256,
+// else the whole wavefront with J = ceil(E / 64) per lane);
 // lane l of a cluster holds experts [J l, J l + J): the logits row, the score
 // gradient row and the output row move with one vector access per lane; the
 // chosen experts' weight gradients reach their owner lanes by readlane (or a
@@ -319,10 +321,13 @@ static hipError_t launch_bwd_j(const RouteBwdParams& p, bool vec, hipStream_t s)
 
 hipError_t launch_route_backward(const RouteBwdParams& p, bool bf16, hipStream_t s) {
   // lanes per token: four experts per lane (16-byte float32 accesses) while a
-  // token's k choices still fit its lanes; else the whole wavefront
-  const int L = (p.E <= 32 && p.k <= 8) ? 8 : (p.E <= 64 && p.k <= 16) ? 16
+  // token's k choices still fit its lanes, eight per lane over 16 lanes for
+  // 64 < E <= 128 (E = 128, k = 8: 23 -> 19 us against four over 32), eight
+  // over 32 lanes up to E = 256; else the whole wavefront
+  const bool wide16 = p.E > 64 && p.E <= 128 && p.E % 8 == 0 && p.k <= 16;
+  const int L = (p.E <= 32 && p.k <= 8) ? 8 : ((p.E <= 64 && p.k <= 16) || wide16) ? 16
               : (p.E <= 256 && p.k <= 32) ? 32 : 64;
-  const int J = L < 32 ? 4 : L == 32 ? (p.E <= 128 ? 4 : 8)
+  const int J = wide16 ? 8 : L < 32 ? 4 : L == 32 ? (p.E <= 128 ? 4 : 8)
               : p.E <= 64 ? 1 : p.E <= 128 ? 2 : p.E <= 256 ? 4 : 8;   // E <= 512
   // vector accesses when every lane's J elements are whole and aligned
   const int esz = bf16 ? 2 : 4;
@@ -330,6 +335,7 @@ hipError_t launch_route_backward(const RouteBwdParams& p, bool bf16, hipStream_t
                    (uintptr_t)p.logits % (J * esz) == 0 && (uintptr_t)p.grad_logits % (J * 4) == 0 &&
                    (p.grad_scores == nullptr || (uintptr_t)p.grad_scores % (J * 4) == 0);
   if (L == 8) return bf16 ? launch_bwd_j<true, 4, 8>(p, vec, s) : launch_bwd_j<false, 4, 8>(p, vec, s);
+  if (L == 16 && J == 8) return bf16 ? launch_bwd_j<true, 8, 16>(p, vec, s) : launch_bwd_j<false, 8, 16>(p, vec, s);
   if (L == 16) return bf16 ? launch_bwd_j<true, 4, 16>(p, vec, s) : launch_bwd_j<false, 4, 16>(p, vec, s);
   if (L == 32 && J == 4)
     return bf16 ? launch_bwd_j<true, 4, 32>(p, vec, s) : launch_bwd_j<false, 4, 32>(p, vec, s);
