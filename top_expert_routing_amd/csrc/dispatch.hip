@@ -7,12 +7,14 @@
 //   dispatch_kernel  one wavefront per permuted row p < total: the row of token
 //                    permuted_idx_to_token_idx[p], copied bit for bit (zeros
 //                    for a padding slot), 16-byte accesses, eight in flight
-//                    per lane.
+//                    per lane, streaming stores (the routed rows are not read
+//                    back here; the token rows, read k times, stay cached).
 //   combine_kernel   one wavefront per token: out[t] = sum_j w[t, j] *
 //                    expert_out[expanded_idx_to_permuted_idx[t k + j]], one
 //                    routed row at a time with up to 16 KiB of it requested
 //                    together, summed in choice order in float32
-//                    (deterministic), rounded once (bf16: RNE).
+//                    (deterministic), rounded once (bf16: RNE), streaming
+//                    stores.
 // Both are HBM-bound row movers.
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -58,7 +60,7 @@ __global__ void __launch_bounds__(kMoveThreads)
 #pragma unroll
       for (int u = 0; u < kCopyInFlight; ++u) {
         const int64_t v = v0 + u * 64 + lane;
-        if (v < nv) reinterpret_cast<u32x4*>(dst)[v] = r[u];
+        if (v < nv) __builtin_nontemporal_store(r[u], reinterpret_cast<u32x4*>(dst) + v);
       }
     }
   } else {
@@ -140,10 +142,10 @@ __global__ void __launch_bounds__(kMoveThreads)
         if constexpr (BF16) {
           const u32x4 o{pack_bf16(acc[sl][0], acc[sl][1]), pack_bf16(acc[sl][2], acc[sl][3]),
                         pack_bf16(acc[sl][4], acc[sl][5]), pack_bf16(acc[sl][6], acc[sl][7])};
-          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + (size_t)t * H + c) = o;
+          __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + (size_t)t * H + c));
         } else {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(out) + (size_t)t * H + c) =
-              f32x4{acc[sl][0], acc[sl][1], acc[sl][2], acc[sl][3]};
+          __builtin_nontemporal_store(f32x4{acc[sl][0], acc[sl][1], acc[sl][2], acc[sl][3]},
+                                      reinterpret_cast<f32x4*>(static_cast<float*>(out) + (size_t)t * H + c));
         }
       }
     }
