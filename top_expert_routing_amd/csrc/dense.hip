@@ -8,7 +8,7 @@
 // J = ceil(E / 64)); lane l of a cluster writes experts [J l, J l + J) with
 // one vector store per output; lanes j < k of a cluster read the token's j-th
 // id and weight, and k readlanes (or cluster shuffles) bring each to the lane
-// owning the expert.  Write-bound: T E (4 + 1) bytes.
+// owning the expert; streaming stores.  Write-bound: T E (4 + 1) bytes.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -70,8 +70,8 @@ __global__ void __launch_bounds__(kDenseThreads)
 #pragma unroll
       for (int h = 0; h < J / 4; ++h) b[h] = (sel >> (4 * h)) & 1u | ((sel >> (4 * h + 1)) & 1u) << 8 |
                                               ((sel >> (4 * h + 2)) & 1u) << 16 | ((sel >> (4 * h + 3)) & 1u) << 24;
-      if constexpr (J == 4) *reinterpret_cast<uint32_t*>(rmap + base) = b[0];
-      else *reinterpret_cast<uint2*>(rmap + base) = make_uint2(b[0], b[1]);
+      if constexpr (J == 4) __builtin_nontemporal_store(b[0], reinterpret_cast<uint32_t*>(rmap + base));
+      else __builtin_nontemporal_store((uint64_t)b[0] | ((uint64_t)b[1] << 32), reinterpret_cast<uint64_t*>(rmap + base));
     }
   } else {
 #pragma unroll

@@ -725,8 +725,8 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>)
       // LDS (free once the emission has read them), a chunk of tokens at a
       // time, so that each store instruction writes 64 consecutive 16-byte
       // pieces instead of 64 pieces one lane-slice apart.  Needs E % 4 == 0,
-      // a 16-byte aligned scores array and room for one row; else each lane
-      // stores its slice.
+      // a 16-byte aligned scores array and room for one row (streaming stores:
+      // nothing here reads them back); else each lane stores its slice.
       constexpr int TPW = 64 / LPT;
       const int chunk = ((E & 3) == 0 && p.scores_vec) ? (TPW * L.row_stride) / E : 0;
       if (chunk >= 1) {
@@ -748,7 +748,7 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>)
           const int nval = max(0, min(ntok, p.T - (tfirst + c0)));   // tokens below T
           const f32x4* src = reinterpret_cast<const f32x4*>(stage);
           f32x4* out = reinterpret_cast<f32x4*>(p.scores + (size_t)(tfirst + c0) * E);
-          for (int q = lw; q < nval * (E / 4); q += 64) out[q] = src[q];
+          for (int q = lw; q < nval * (E / 4); q += 64) __builtin_nontemporal_store(src[q], out + q);
         }
       } else if (tv) {
         float* srow = p.scores + (size_t)t * E;
