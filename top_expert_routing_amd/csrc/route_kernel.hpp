@@ -411,20 +411,22 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>)
 
   // The bias is requested first (one block-wide pass into LDS), then the
   // first token's logits; the bias lands in LDS while the logits are in flight.
-  float bload = 0.0f;
-  if (kBias && tid < EP) {
-    if (tid >= E)
-      bload = -kInf;
-    else if (p.bias != nullptr)
-      bload = p.bias_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(p.bias)[tid])
-                          : static_cast<const float*>(p.bias)[tid];
-  }
+  // Its raw bits are loaded and decoded only after the logits are requested:
+  // a value used inside the branch that loads it is awaited at once.
+  uint32_t braw = 0u;
+  const bool bias_here = kBias && tid < EP && tid < E && p.bias != nullptr;
+  if (bias_here)
+    braw = p.bias_bf16 ? (uint32_t)static_cast<const uint16_t*>(p.bias)[tid]
+                       : __float_as_uint(static_cast<const float*>(p.bias)[tid]);
   RawRow<EPL, BF16> raw;
   {
     const int t = blk * kTokensPerBlock + cl;
     load_raw<EPL, BF16>(raw, p.logits, (size_t)t * E, e0, E, p.vec, t < p.T);
   }
   if constexpr (kBias) {
+    const float bload = tid >= E ? -kInf
+                        : !bias_here ? 0.0f
+                        : p.bias_bf16 ? __uint_as_float(braw << 16) : __uint_as_float(braw);
     for (int e = tid; e < EP; e += BLOCK) {          // EP > BLOCK only for very wide rows
       float b = e == tid ? bload : (e >= E ? -kInf : 0.0f);
       if (e != tid && e < E && p.bias != nullptr)
