@@ -77,6 +77,14 @@ def test_workload_full_size(name):
     run_and_check(w, logits, bias, f"{name} full", scores=(w.aux_coeff is not None))
 
 
+def test_deepseek_like_large_T():
+    # the headline method at T = 262144 (4096 route blocks, 64 counting rows of
+    # 64 blocks each), the size the benchmark also times
+    w = with_overrides(WORKLOADS["deepseek_v3_like"], T=262144)
+    logits, bias = route_inputs(w)
+    run_and_check(w, logits, bias, "deepseek_v3_like T=262144")
+
+
 @pytest.mark.parametrize("name", list(WORKLOADS))
 @pytest.mark.parametrize("T", [1, 63, 65, 257, 4097])
 def test_workload_ragged(name, T):
