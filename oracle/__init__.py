@@ -31,18 +31,21 @@ Parity pins: every function here is pinned by ``tests/test_oracle_*.py`` against
 closed forms, invariants, brute force on tiny inputs or library routines; see
 the header of each module for which pin covers which step.
 """
-from .routing import route, RouteResult, decode_input, selection_keys32, exact_keys64
+from .routing import (route, RouteResult, decode_input, selection_keys32, exact_keys64,
+                      weights_for_ids, within_near_ties)
 from .permutation import permute, PermuteResult, max_padded_tokens, max_tiles
 from .aux_loss import aux_loss_fwd, aux_loss_bwd
-from .front_end import rmsnorm, front_end_route, bf16_round_bits, FrontEndResult
+from .front_end import (rmsnorm, front_end_route, bf16_round_bits, FrontEndResult,
+                        affinities_for_ids)
 from .backward import route_backward
 from .dispatch import dispatch, combine
 from .dense import dense_outputs
 
 __all__ = [
     "route", "RouteResult", "decode_input", "selection_keys32", "exact_keys64",
+    "weights_for_ids", "within_near_ties",
     "permute", "PermuteResult", "max_padded_tokens", "max_tiles",
     "aux_loss_fwd", "aux_loss_bwd",
-    "rmsnorm", "front_end_route", "bf16_round_bits", "FrontEndResult",
+    "rmsnorm", "front_end_route", "bf16_round_bits", "FrontEndResult", "affinities_for_ids",
     "route_backward", "dispatch", "combine", "dense_outputs",
 ]

@@ -18,8 +18,9 @@ sigmoid affinities are sigma(z) of the selected logits with no renormalisation;
 softmax affinities are the softmax over the k selected logits; every other
 affinity is exactly zero; ties go to the lower expert index.
 
-Pins: tests/test_oracle_front_end.py (constant rows, linearity in gamma, the
-identity projection, library rounding of float16).
+Pins: tests/test_oracle_aux_front.py (constant rows, linearity in gamma, the
+identity projection, library rounding of float16, affinities of given ids
+against scipy's logistic and softmax).
 """
 from __future__ import annotations
 
@@ -103,7 +104,17 @@ def front_end_route(normed_bits, router_weights, k: int, act: str = "sigmoid",
         raise ValueError("need 1 <= k <= E")
     order = np.argsort(-z, axis=1, kind="stable")
     ids = order[:, :k].astype(np.int32)
-    zs = np.take_along_axis(z, ids.astype(np.int64), axis=1)
+    aff64 = affinities_for_ids(z, ids, act)
+    return FrontEndResult(logits=z, abs_products=absprod, ids=ids,
+                          affinities=bf16_round_bits(aff64), affinities64=aff64)
+
+
+def affinities_for_ids(z: np.ndarray, ids, act: str = "sigmoid") -> np.ndarray:
+    """Masked affinities [T, E] (float64, before rounding) of the given experts:
+    the activation of the chosen logits only -- sigmoid of each, or the softmax
+    over the k chosen -- at the chosen experts, zero everywhere else."""
+    ids = np.asarray(ids).astype(np.int64)
+    zs = np.take_along_axis(z, ids, axis=1)
     if act == "sigmoid":
         sel = 1.0 / (1.0 + np.exp(-zs))
     elif act == "softmax":
@@ -111,7 +122,6 @@ def front_end_route(normed_bits, router_weights, k: int, act: str = "sigmoid",
         sel = e / e.sum(axis=1, keepdims=True)
     else:
         raise ValueError(act)
-    aff64 = np.zeros((T, E), dtype=np.float64)
-    np.put_along_axis(aff64, ids.astype(np.int64), sel, axis=1)
-    return FrontEndResult(logits=z, abs_products=absprod, ids=ids,
-                          affinities=bf16_round_bits(aff64), affinities64=aff64)
+    aff64 = np.zeros(z.shape, dtype=np.float64)
+    np.put_along_axis(aff64, ids, sel, axis=1)
+    return aff64

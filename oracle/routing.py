@@ -27,11 +27,17 @@ are listed by descending key; the bias enters the selection key only, never a
 weight; renormalisation divides by the plain sum; full-E "scores" for the aux
 loss are the softmax over E, or sigmoid scores divided by their sum.
 
+Near ties (the parity rule the routing methods are held to): a token whose
+exact-key gap at a deciding position lies in (0, 1e-6) relative is exempt from
+bit-exact ids; ``within_near_ties`` states what such a token may still return.
+
 Pins: tests/test_oracle_routing.py (closed forms, invariants, library
-softmax, brute-force enumeration of every k-subset on tiny inputs).
+softmax, brute-force enumeration of every k-subset on tiny inputs, near-tie
+cases with gaps of 15 and 18 float32 ulps on each side of 1e-6).
 """
 from __future__ import annotations
 
+import itertools
 from dataclasses import dataclass
 from typing import Optional
 
@@ -128,6 +134,48 @@ def grouping_active(n_group: int, topk_group: int) -> bool:
     return n_group > 1 and 0 < topk_group < n_group
 
 
+def select_topk(keys32: np.ndarray, eligible: np.ndarray, k: int) -> np.ndarray:
+    """The k largest eligible keys of each row, listed by descending key; equal
+    keys go to the lower expert index (a stable sort of the negated keys)."""
+    masked = np.where(eligible, keys32, np.float32(-np.inf)).astype(np.float32)
+    order = np.argsort(-masked, axis=1, kind="stable")
+    ids = order[:, :k].astype(np.int32)
+    return ids
+
+
+def weights_for_ids(x: np.ndarray, ids, score_fn: str, pre_softmax: bool, renorm: bool,
+                    scale: float) -> np.ndarray:
+    """Routing weights (float64) of the given experts of each token.
+
+    ``x``: decoded logits [T, E] (float64); ``ids``: [T, k] chosen experts, in
+    any order (weight j belongs to ids[:, j]).  The bias never enters a weight.
+
+    sigmoid: s = 1 / (1 + exp(-x)) of the chosen, divided by their sum when
+    renormalising; softmax before top-k: the full softmax over E at the chosen,
+    divided by their sum when renormalising; softmax after top-k: the softmax
+    over the k chosen logits.  Then times ``scale``.
+    """
+    ids = np.asarray(ids).astype(np.int64)
+    xs = np.take_along_axis(x, ids, axis=1)
+    if score_fn == "sigmoid":
+        w = 1.0 / (1.0 + np.exp(-xs))
+        if renorm:
+            w = w / w.sum(axis=1, keepdims=True)
+    elif pre_softmax:
+        m = x.max(axis=1, keepdims=True)
+        p = np.exp(x - m)
+        p = p / p.sum(axis=1, keepdims=True)
+        w = np.take_along_axis(p, ids, axis=1)
+        if renorm:
+            w = w / w.sum(axis=1, keepdims=True)
+    else:
+        # softmax over the k selected logits; already sums to one
+        e = np.exp(xs - xs.max(axis=1, keepdims=True))
+        w = e / e.sum(axis=1, keepdims=True)
+    w = w * float(scale)
+    return w
+
+
 @dataclass
 class RouteResult:
     ids: np.ndarray          # int32 [T, k], descending key, ties -> lower index
@@ -138,6 +186,8 @@ class RouteResult:
     keys32: np.ndarray       # float32 [T, E], the decision keys (unmasked)
     keys64: np.ndarray       # float64 [T, E]
     eligible: np.ndarray     # bool [T, E], experts in kept groups
+    group_scores64: Optional[np.ndarray] = None   # float64 [T, n_group] when grouped
+    topk_group: int = 0
 
 
 def route(logits, logits_dtype: str, k: int, score_fn: str = "softmax",
@@ -174,28 +224,10 @@ def route(logits, logits_dtype: str, k: int, score_fn: str = "softmax",
         eligible = np.repeat(kept, gsz, axis=1)
 
     # 3. top-k: key descending, ties by ascending expert index
-    masked = np.where(eligible, key32, np.float32(-np.inf)).astype(np.float32)
-    order = np.argsort(-masked, axis=1, kind="stable")
-    ids = order[:, :k].astype(np.int32)
+    ids = select_topk(key32, eligible, k)
 
     # 4. weights (float64), bias never enters them
-    xs = np.take_along_axis(x, ids.astype(np.int64), axis=1)
-    if score_fn == "sigmoid":
-        w = 1.0 / (1.0 + np.exp(-xs))
-        if renorm:
-            w = w / w.sum(axis=1, keepdims=True)
-    elif pre_softmax:
-        m = x.max(axis=1, keepdims=True)
-        p = np.exp(x - m)
-        p = p / p.sum(axis=1, keepdims=True)
-        w = np.take_along_axis(p, ids.astype(np.int64), axis=1)
-        if renorm:
-            w = w / w.sum(axis=1, keepdims=True)
-    else:
-        # softmax over the k selected logits; already sums to one
-        e = np.exp(xs - xs.max(axis=1, keepdims=True))
-        w = e / e.sum(axis=1, keepdims=True)
-    w = w * float(scale)
+    w = weights_for_ids(x, ids, score_fn, pre_softmax, renorm, scale)
 
     # 5. full-E scores for the aux loss (no bias)
     if score_fn == "sigmoid":
@@ -212,7 +244,10 @@ def route(logits, logits_dtype: str, k: int, score_fn: str = "softmax",
     exempt = _near_ties(key64, eligible, k, n_group, topk_group, group_topn, grouped)
 
     return RouteResult(ids=ids, weights=w, scores=scores, counts=counts,
-                       exempt=exempt, keys32=key32, keys64=key64, eligible=eligible)
+                       exempt=exempt, keys32=key32, keys64=key64, eligible=eligible,
+                       group_scores64=(_group_scores(key64, n_group, group_topn)
+                                       if grouped else None),
+                       topk_group=topk_group if grouped else 0)
 
 
 def _rel_gaps(v: np.ndarray) -> np.ndarray:
@@ -240,3 +275,51 @@ def _near_ties(key64, eligible, k, n_group, topk_group, group_topn, grouped):
         ggap = _rel_gaps(gsrt[:, topk_group - 1:topk_group + 1])[:, 0]
         exempt |= (ggap > 0) & (ggap < NEAR_TIE_REL)
     return exempt
+
+
+def _kept_alternatives(res: RouteResult, t: int):
+    """Eligibility rows of token t under every kept-group set that near ties at
+    the kept-group boundary allow: groups whose exact score lies within
+    NEAR_TIE_REL (relative) of the topk_group-th best exact score may stand in
+    for one another; groups clearly above it are always kept.  The oracle's own
+    kept set comes first."""
+    yield res.eligible[t]
+    if res.group_scores64 is None:
+        return
+    gs = res.group_scores64[t]
+    G = gs.shape[0]
+    gsz = res.keys64.shape[1] // G
+    edge = -np.sort(-gs)[res.topk_group - 1]
+    near = np.abs(gs - edge) <= NEAR_TIE_REL * abs(edge)
+    sure = (gs > edge) & ~near
+    need = res.topk_group - int(sure.sum())
+    for combo in itertools.combinations(np.nonzero(near)[0].tolist(), need):
+        kept = sure.copy()
+        kept[list(combo)] = True
+        yield np.repeat(kept, gsz)
+
+
+def within_near_ties(res: RouteResult, t: int, ids_row) -> bool:
+    """Whether ``ids_row`` is an acceptable top-k for token t of ``res`` given
+    its near ties (the rule for exempt tokens).
+
+    Acceptable: k distinct experts, all eligible under one kept-group set that
+    the group near ties allow, and for every position j the exact key of
+    ids_row[j] within NEAR_TIE_REL (relative) of the exact key of that kept
+    set's j-th choice.  A near tie may thus swap two choices or replace the
+    k-th choice by an expert whose key is within the tolerance of it; nothing
+    else may differ."""
+    k = res.ids.shape[1]
+    E = res.keys64.shape[1]
+    row = np.asarray(ids_row).astype(np.int64).reshape(-1)
+    if row.shape[0] != k or np.any(row < 0) or np.any(row >= E) or np.unique(row).size != k:
+        return False
+    for elig in _kept_alternatives(res, t):
+        if not np.all(elig[row]):
+            continue
+        ref = select_topk(res.keys32[t:t + 1], elig[None, :], k)[0].astype(np.int64)
+        a = res.keys64[t, row]
+        b = res.keys64[t, ref]
+        if np.all(np.abs(a - b) <= NEAR_TIE_REL * np.abs(b)):
+            return True
+    return False

@@ -1,5 +1,6 @@
 """Pins of the aux-loss and front-end oracles (no GPU)."""
 import numpy as np
+import scipy.special
 import pytest
 
 import oracle
@@ -156,6 +157,34 @@ def pin_identity_projection():
 
 def test_p13_identity_projection():
     pin_identity_projection()
+
+
+def pin_affinities_for_ids():
+    rng = np.random.default_rng(6)
+    T, E, k = 24, 20, 5
+    z = rng.standard_normal((T, E)) * 2.0
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)])       # not the top-k
+    sel = np.take_along_axis(z, ids, 1)
+    a = F.affinities_for_ids(z, ids, "sigmoid")
+    assert np.allclose(np.take_along_axis(a, ids, 1), scipy.special.expit(sel), rtol=1e-12)
+    mask = np.ones_like(a, bool)
+    np.put_along_axis(mask, ids, False, 1)
+    assert np.all(a[mask] == 0.0)
+    b = F.affinities_for_ids(z, ids, "softmax")
+    assert np.allclose(np.take_along_axis(b, ids, 1), scipy.special.softmax(sel, axis=1),
+                       rtol=1e-12)
+    assert np.all(b[mask] == 0.0)
+    # the order the ids are listed in does not matter
+    assert np.array_equal(F.affinities_for_ids(z, ids[:, ::-1], "sigmoid"), a)
+    # at the routed ids they are the routing's affinities
+    hidden, gamma, W, _ = front_end_inputs(FRONT_END, T=4, H=256, E=32)
+    _, normed = oracle.rmsnorm(hidden, gamma, FRONT_END.eps)
+    res = oracle.front_end_route(normed, W, 4, act="softmax")
+    assert np.array_equal(F.affinities_for_ids(res.logits, res.ids, "softmax"), res.affinities64)
+
+
+def test_affinities_for_ids():
+    pin_affinities_for_ids()
 
 
 def test_front_end_workload_shapes():

@@ -21,10 +21,11 @@ ORACLE_DIR = os.path.dirname(oracle.__file__)
 PINS = [
     T_R.pin_weights_sum_to_scale, T_R.pin_sigmoid_bias_semantics, T_R.pin_brute_force,
     T_R.pin_pre_renorm_equals_post, T_R.pin_special_cases, T_R.pin_grouping_reductions,
-    T_R.pin_scores_counts_decode,
+    T_R.pin_scores_counts_decode, T_R.pin_near_tie_classification, T_R.pin_within_near_ties,
+    T_R.pin_weights_for_ids,
     T_P.pin_permutation_invariants, T_P.pin_counting_sort, T_P.pin_local_expert_shard,
     T_AF.pin_aux_closed_form, T_AF.pin_aux_finite_difference, T_AF.pin_rmsnorm,
-    T_AF.pin_bf16_rounding, T_AF.pin_identity_projection,
+    T_AF.pin_bf16_rounding, T_AF.pin_identity_projection, T_AF.pin_affinities_for_ids,
     T_G.pin_golden_routing, T_G.pin_golden_permutation, T_G.pin_golden_aux_loss,
     T_G.pin_golden_rmsnorm,
     T_B.pin_backward_finite_differences, T_B.pin_backward_invariants,
@@ -45,9 +46,9 @@ MUTATIONS = [
     ("routing", "        w = 1.0 / (1.0 + np.exp(-xs))\n        if renorm:\n            w = w / w.sum(axis=1, keepdims=True)",
      "        w = 1.0 / (1.0 + np.exp(-xs))",
      "sigmoid weights not renormalised"),
-    ("routing", "        w = 1.0 / (1.0 + np.exp(-xs))",
-     "        w = 1.0 / (1.0 + np.exp(-xs)) + (0.0 if bias64 is None else np.take_along_axis(np.broadcast_to(bias64, x.shape), ids.astype(np.int64), axis=1))",
-     "bias leaks into the sigmoid weights"),
+    ("routing", "    w = weights_for_ids(x, ids, score_fn, pre_softmax, renorm, scale)",
+     "    w = weights_for_ids(x + (0.0 if b is None else b[None, :]), ids, score_fn, pre_softmax, renorm, scale)",
+     "bias leaks into the weights"),
     ("routing", "    for i in range(group_topn):\n", "    for i in range(1):\n",
      "group score is the group max, not the top-n sum"),
     ("routing", 'order = np.argsort(-score, axis=1, kind="stable")',
@@ -60,6 +61,26 @@ MUTATIONS = [
      "ids listed by index instead of by descending key"),
     ("routing", "        scores = p / p.sum(axis=1, keepdims=True)\n\n    counts",
      "        scores = p\n\n    counts", "full-E softmax scores not normalised"),
+    ("routing", "upto = min(k + 1, E)", "upto = min(k, E)",
+     "near ties: the k-th/(k+1)-th gap is not examined"),
+    ("routing", "        exempt |= (ggap > 0) & (ggap < NEAR_TIE_REL)\n", "",
+     "near ties: the kept-group boundary gap is not examined"),
+    ("routing", "masked = np.where(eligible, key64, -np.inf)", "masked = key64",
+     "near ties: gaps measured over experts of dropped groups too"),
+    ("routing", "exempt = np.any((gap > 0) & (gap < NEAR_TIE_REL), axis=1)",
+     "exempt = np.any(gap < NEAR_TIE_REL, axis=1)", "near ties: exact ties counted as near ties"),
+    ("routing", "ggap = _rel_gaps(gsrt[:, topk_group - 1:topk_group + 1])[:, 0]",
+     "ggap = _rel_gaps(gsrt[:, topk_group:topk_group + 2])[:, 0]",
+     "near ties: the group gap taken one position late"),
+    ("routing", "near = np.abs(gs - edge) <= NEAR_TIE_REL * abs(edge)", "near = gs == edge",
+     "acceptance: near-tied groups may not stand in for each other"),
+    ("routing", "if np.all(np.abs(a - b) <= NEAR_TIE_REL * np.abs(b)):",
+     "if np.all(a - b <= NEAR_TIE_REL * np.abs(b)):",
+     "acceptance: a choice far below the oracle's is accepted"),
+    ("routing", "if not np.all(elig[row]):", "if False:",
+     "acceptance: experts of dropped groups accepted"),
+    ("routing", "    xs = np.take_along_axis(x, ids, axis=1)", "    xs = np.take_along_axis(x, np.sort(ids, axis=1), axis=1)",
+     "weights for given ids: weights listed in index order, not the ids' order"),
     ("permutation", "padded[e + 1] = padded[e] + -(-counts[e] // tile) * tile",
      "padded[e + 1] = padded[e] + counts[e]", "segments not padded to the tile"),
     ("permutation", "slots = padded[e] + np.arange(t_idx.size, dtype=np.int64)",
@@ -87,6 +108,9 @@ MUTATIONS = [
     ("front_end", "    z = a @ w\n", "    z = a[:, ::-1] @ w\n", "hidden features reversed in the projection"),
     ("front_end", "        sel = 1.0 / (1.0 + np.exp(-zs))", "        sel = 1.0 / (1.0 + np.exp(-zs)); sel = sel / sel.sum(axis=1, keepdims=True)",
      "sigmoid affinities renormalised"),
+    ("front_end", "    np.put_along_axis(aff64, ids, sel, axis=1)",
+     "    np.put_along_axis(aff64, np.sort(ids, axis=1), sel, axis=1)",
+     "affinities placed at the experts in index order"),
     ("backward", "                ds = (g - c) / S", "                ds = g / S",
      "backward: renormalisation's coupling term dropped"),
     ("backward", "            dsig = s * (1.0 - s)\n            np.add.at(grad",

@@ -229,14 +229,128 @@ def test_scores_counts_decode():
 
 
 # ---- near-tie classification ----------------------------------------------------------------
+# The parity rule: a token whose exact-key gap at a deciding position -- the
+# k-th/(k+1)-th gap, a gap inside the top k, or with grouping the gap at the
+# kept-group boundary -- lies in (0, 1e-6) relative is exempt; exact ties never
+# are.  With softmax after top-k the key is the float32 logit itself, so the
+# gaps below are exact: u = 2**-24 is the float32 spacing just below 1, a gap of
+# 15u (8.9e-7) is inside the window and 18u (1.07e-6) is outside it.
+
+U = 2.0 ** -24
+IN, OUT = 15 * U, 18 * U
+
+
+def _post(x, k, **kw):
+    return oracle.route(np.asarray(x, np.float32), "f32", k, score_fn="softmax",
+                        pre_softmax=False, **kw)
+
+
+def pin_near_tie_classification():
+    assert IN < R.NEAR_TIE_REL < OUT
+    rows = [
+        ([3.0, 1.0, 1.0 - IN, -1.0, -2.0, -3.0], True),    # k-th/(k+1)-th gap inside
+        ([3.0, 1.0, 1.0 - OUT, -1.0, -2.0, -3.0], False),  # ... just outside
+        ([1.0, 1.0 - IN, -1.0, -2.0, -3.0, -4.0], True),   # gap inside the top k
+        ([1.0, 1.0 - OUT, -1.0, -2.0, -3.0, -4.0], False),
+        ([3.0, 2.0, 1.0, 1.0 - IN, -2.0, -3.0], False),    # (k+1)/(k+2): decides nothing
+        ([3.0, 1.0, 1.0, -1.0, -2.0, -3.0], False),        # exact tie: index rule
+        ([1.0 - IN, 3.0, -1.0, 1.0, -2.0, -3.0], True),    # order of the row is irrelevant
+    ]
+    r = _post([x for x, _ in rows], 2)
+    assert r.exempt.tolist() == [e for _, e in rows], r.exempt.tolist()
+    assert r.ids[5].tolist() == [0, 1]
+    # grouped (3 groups of 2, keep 1, top-2-sum score): the group gap at the
+    # boundary decides; expert gaps are measured among kept experts only
+    g = [
+        ([1.0, 1.0, 1.0, 1.0 - 2 * IN, -3.0, -3.0], True),   # group scores 2 vs 2 - 30u: rel 15u
+        ([1.0, 1.0, 1.0, 1.0 - 2 * OUT, -3.0, -3.0], False),
+        ([3.0, 3.0, 1.0, 1.0 - 2 * IN, 1.0, 1.0], False),    # near tie below the boundary
+        ([0.5, 0.5, 0.0, 0.0, 0.5 - IN / 2, -1.0], False),   # kept group 0; the near-tie
+                                                             # partner lies in a dropped group
+    ]
+    r = _post([x for x, _ in g], 2, n_group=3, topk_group=1, group_topn=2)
+    assert r.exempt.tolist() == [e for _, e in g], r.exempt.tolist()
+    # k-th/(k+1)-th near tie between two kept experts (4 groups, keep 2, k = 3)
+    x = [2.0, 1.9, 1.0, 1.0 - IN, -5.0, -5.0, -5.0, -5.0]
+    r = _post([x, [2.0, 1.9, 1.0, 1.0 - OUT, -5.0, -5.0, -5.0, -5.0]], 3, n_group=4,
+              topk_group=2, group_topn=1)
+    assert r.exempt.tolist() == [True, False]
+
 
 def test_near_tie_classification():
-    x = np.array([[1.0, 2.0, 2.0 + 1e-6, 0.0],      # gap ~5e-7 inside the top 2: exempt
-                  [1.0, 2.0, 2.0, 0.0],             # exact tie: never exempt
-                  [1.0, 2.0, 3.0, 0.5]], np.float32)  # clear gaps
-    r = oracle.route(x, "f32", 2, score_fn="softmax", pre_softmax=False)
-    assert r.exempt.tolist() == [True, False, False]
-    assert r.ids[1].tolist() == [1, 2]
+    pin_near_tie_classification()
+
+
+def pin_within_near_ties():
+    W = R.within_near_ties
+    # every token of seeded runs accepts the oracle's own ids
+    for w in WORKLOADS.values():
+        res, _, _ = _route_w(w, T=128)
+        assert all(W(res, t, res.ids[t]) for t in range(128)), w.name
+    # ungrouped: a near tie at the k-th position may swap in the (k+1)-th expert
+    r = _post([[3.0, 1.0, 1.0 - IN, -1.0, -2.0, -3.0],
+               [3.0, 1.0, 1.0 - OUT, -1.0, -2.0, -3.0]], 2)
+    assert W(r, 0, [0, 1]) and W(r, 0, [0, 2])
+    assert not W(r, 0, [2, 0])                      # but not reorder far keys
+    assert not W(r, 0, [0, 3])                      # nor take a far lower expert
+    assert not W(r, 1, [0, 2])                      # an 18-ulp gap decides
+    assert not W(r, 0, [0, 0]) and not W(r, 0, [0, 6]) and not W(r, 0, [0, -1])
+    assert not W(r, 0, [0, 1, 2])
+    # a near tie inside the top k may swap the two
+    r = _post([[1.0, 1.0 - IN, -1.0, -2.0], [1.0, 1.0 - OUT, -1.0, -2.0]], 2)
+    assert W(r, 0, [1, 0]) and not W(r, 1, [1, 0])
+    # grouped: near-tied groups at the boundary may stand in for each other
+    r = _post([[1.0, 1.0, 1.0, 1.0 - 2 * IN, -3.0, -3.0],
+               [1.0, 1.0, 1.0, 1.0 - 2 * OUT, -3.0, -3.0]], 2,
+              n_group=3, topk_group=1, group_topn=2)
+    assert r.ids[0].tolist() == [0, 1]
+    assert W(r, 0, [2, 3]) and not W(r, 1, [2, 3])
+    assert not W(r, 0, [2, 0])                      # experts of two groups: no kept set
+    assert not W(r, 0, [4, 5])                      # a group far below the boundary
+    # 4 groups keep 2: one sure group and two near-tied candidates for the other slot
+    x = np.array([[5.0, 5.0, 1.0, 1.0, 1.0, 1.0 - 2 * IN, -9.0, -9.0]], np.float32)
+    r = _post(x, 3, n_group=4, topk_group=2, group_topn=2)
+    assert r.ids[0].tolist() == [0, 1, 2]
+    assert W(r, 0, [0, 1, 4]) and not W(r, 0, [0, 1, 6]) and not W(r, 0, [2, 3, 4])
+
+
+def test_within_near_ties():
+    pin_within_near_ties()
+
+
+def pin_weights_for_ids():
+    rng = np.random.default_rng(21)
+    T, E, k = 32, 12, 4
+    x = rng.standard_normal((T, E)).astype(np.float32)
+    x64 = x.astype(np.float64)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)   # not the top-k
+    sel = np.take_along_axis(x64, ids.astype(np.int64), axis=1)
+    sig = scipy.special.expit(sel)
+    full = np.take_along_axis(scipy.special.softmax(x64, axis=1), ids.astype(np.int64), axis=1)
+    cases = [
+        (("sigmoid", False, True, 2.5), 2.5 * sig / sig.sum(1, keepdims=True)),
+        (("sigmoid", False, False, 1.0), sig),
+        (("softmax", True, False, 1.0), full),
+        (("softmax", True, True, 3.0), 3.0 * full / full.sum(1, keepdims=True)),
+        (("softmax", False, True, 1.0), scipy.special.softmax(sel, axis=1)),
+    ]
+    for (fn, pre, ren, sc), want in cases:
+        got = R.weights_for_ids(x64, ids, fn, pre, ren, sc)
+        assert np.allclose(got, want, rtol=1e-12, atol=0), (fn, pre, ren)
+        # listing the ids in another order lists the weights in that order
+        perm = ids[:, ::-1]
+        assert np.allclose(R.weights_for_ids(x64, perm, fn, pre, ren, sc), got[:, ::-1],
+                           rtol=1e-12, atol=0)
+    # at the chosen ids they are the routing weights
+    for w in WORKLOADS.values():
+        res, logits, _ = _route_w(w, T=64)
+        got = R.weights_for_ids(R.decode_input(logits, w.logits_dtype), res.ids, w.score_fn,
+                                w.pre_softmax, w.renorm, w.scale)
+        assert np.allclose(got, res.weights, rtol=1e-12, atol=0), w.name
+
+
+def test_weights_for_ids():
+    pin_weights_for_ids()
 
 
 def test_workload_shapes_route():
