@@ -51,7 +51,10 @@ def parse():
     ap.add_argument("--no-other-configs", action="store_true",
                     help="skip the other workloads (reported under other_configs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="seconds of oracle work timed for the headline cpu_baseline")
+    ap.add_argument("--cpu-seconds-other", type=float, default=3.0,
+                    help="seconds of oracle work timed beside each other workload")
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="finish with plain device copies of this many MiB (the reference "
@@ -117,9 +120,10 @@ def route_permute_bytes(w, T, total, ntiles):
             2 * ntiles * 4 + w.E * 4 + (w.E + 1) * 4 + 8)
 
 
-def other_configs(mr, torch, np, dev, rotate_mb, K):
+def other_configs(mr, torch, np, dev, rotate_mb, K, cpu_seconds=None):
     """The other workloads, each cold (rotating sets past 2x the MALL): ms per
-    call and algorithmic GB/s."""
+    call and algorithmic GB/s; with cpu_seconds, the oracle timed beside each
+    (cpu_baseline) and the near-tie count of the GPU's output."""
     from workloads import WORKLOADS, FRONT_END, front_end_inputs, route_inputs, with_overrides
     res = {}
 
@@ -180,6 +184,9 @@ def other_configs(mr, torch, np, dev, rotate_mb, K):
             entry["aux_forward"] = {"us_per_call": fwd * 1e3, "gbs": ab / (fwd * 1e-3) / 1e9}
             entry["aux_backward"] = {"us_per_call": bwd * 1e3, "gbs": ab / (bwd * 1e-3) / 1e9}
             del grads, probs
+        if cpu_seconds:
+            entry["near_ties"] = near_tie_entry(w, logits, bias, o0.topk_ids.cpu().numpy())
+            entry["cpu_baseline"] = cpu_baseline_entry(w, cpu_seconds, max_T=8192)
         res[name] = entry
         del sets, o0
 
@@ -269,6 +276,34 @@ def other_configs(mr, torch, np, dev, rotate_mb, K):
         "route_kernel_frac_of_peak": route_b / (route_us * 1e-6) / 1e9 / HBM_PEAK_GBS if route_us else None}
     del lsets, x0, o0
 
+    # the headline method with bfloat16 routing weights (FlashInfer's
+    # topk_weights dtype): the same step, 2-byte weights
+    w = WORKLOADS["deepseek_v3_like"]
+    logits, bias = route_inputs(w)
+    x0 = dev_logits(w, logits)
+    b0 = torch.from_numpy(bias).to(dev)
+    args = mr.make_route_args(w.T, w.E, w.k, score_fn=w.score_fn, n_group=w.n_group,
+                              topk_group=w.topk_group, group_topn=w.group_topn, renorm=w.renorm,
+                              scale=w.scale, logits_dtype=w.logits_dtype, bias_dtype=w.bias_dtype,
+                              weights_dtype="bf16")
+    o0 = mr.alloc_route_outputs(args, dev, permute=True, tile=w.tile)
+    sb = x0.numel() * x0.element_size() + sum(
+        t.numel() * t.element_size() for t in vars(o0).values() if isinstance(t, torch.Tensor))
+    R = n_sets(sb, rotate_mb)
+    hsets = [(x0 if r == 0 else x0.clone(),
+              o0 if r == 0 else mr.alloc_route_outputs(args, dev, permute=True, tile=w.tile))
+             for r in range(R)]
+    ms = graph_ms(torch, lambda i: mr.route_permute(args, hsets[i % R][0], b0, tile=w.tile,
+                                                    out=hsets[i % R][1]), K)
+    total = int(o0.total_num_padded_tokens.item())
+    ntiles = int(o0.num_non_exiting_ctas.item())
+    nbytes = route_permute_bytes(w, w.T, total, ntiles) - w.T * w.k * 2
+    res["deepseek_v3_like_bf16_weights"] = {
+        "workload": w.description + "; bf16 topk_weights",
+        "us_per_call": ms * 1e3, "tokens_per_s": w.T / (ms * 1e-3), "algorithmic_bytes": nbytes,
+        "gbs": nbytes / (ms * 1e-3) / 1e9, "buffer_sets": R}
+    del hsets, x0, o0
+
     # token dispatch and combine around the expert GEMM, DeepSeek-V3-like route
     # at the front end's hidden size (7168, bf16), rows of synthetic N(0,1)
     w = WORKLOADS["deepseek_v3_like"]
@@ -308,13 +343,16 @@ def other_configs(mr, torch, np, dev, rotate_mb, K):
         "buffer_sets": R}
     del dsets, csets, o
 
-    res["decode_front_end"] = front_end_bench(mr, torch, np, dev, rotate_mb, K)
+    res["decode_front_end"] = front_end_bench(mr, torch, np, dev, rotate_mb, K, cpu_seconds)
     return res
 
 
-def front_end_bench(mr, torch, np, dev, rotate_mb, K):
+def front_end_bench(mr, torch, np, dev, rotate_mb, K, cpu_seconds=None):
     """The decode front end (RMSNorm -> projection -> top-k), cold (rotating sets):
-    microseconds per call, algorithmic GB/s and projection TFLOP/s."""
+    microseconds per call, algorithmic GB/s and projection TFLOP/s; with
+    cpu_seconds, the near-tie count of its output under the float32-summation
+    rule and the oracle timed on the host (BLAS threads pinned to the CPUs this
+    process may use)."""
     from workloads import FRONT_END, front_end_inputs
     f = FRONT_END
     hidden, gamma, W, _ = front_end_inputs(f)
@@ -349,10 +387,40 @@ def front_end_bench(mr, torch, np, dev, rotate_mb, K):
     kernel_us = pms / pn * 1e3 if pn else None
     fb = 2 * f.T * f.H * 2 + f.H * 2 + f.H * f.E * 2 + f.T * f.k * 4 + f.T * f.E * 2
     flops = 2 * f.T * f.H * f.E
-    return {"workload": f.description, "us_per_call": ms * 1e3,
-            "tokens_per_s": f.T / (ms * 1e-3), "algorithmic_bytes": fb,
-            "gbs": fb / (ms * 1e-3) / 1e9, "mfma_tflops": flops / (ms * 1e-3) / 1e12,
-            "kernel_us_per_call": kernel_us, "buffer_sets": R}
+    entry = {"workload": f.description, "us_per_call": ms * 1e3,
+             "tokens_per_s": f.T / (ms * 1e-3), "algorithmic_bytes": fb,
+             "gbs": fb / (ms * 1e-3) / 1e9, "mfma_tflops": flops / (ms * 1e-3) / 1e12,
+             "kernel_us_per_call": kernel_us, "buffer_sets": R}
+    if cpu_seconds:
+        import oracle
+        from threadpoolctl import threadpool_limits
+        h, _, nm, ids, _ = fsets[0]
+        normed_bits = nm.view(torch.int16).cpu().numpy().view(np.uint16)
+        depth = mr.rmsnorm_gate_route_sum_depth(f.H)
+        ncpu = len(os.sched_getaffinity(0))
+        with threadpool_limits(limits=ncpu):
+            res = oracle.front_end_route(normed_bits, W, f.k, act=f.act)
+            ex, *_ = oracle.fp32_sum_near_ties(res, f.k, depth)
+            differ = np.any(ids.cpu().numpy() != res.ids, axis=1)
+            entry["near_ties"] = {
+                "rule": f"deciding logit gap below the float32 summation bound, depth {depth}",
+                "near_tie_tokens": int(ex.sum()), "ids_differ_from_oracle": int(differ.sum()),
+                "differing_outside_near_ties": int(np.sum(differ & ~ex)), "tokens": f.T}
+            times = []
+            while sum(times) < cpu_seconds or not times:
+                t0 = time.perf_counter()
+                _, nb = oracle.rmsnorm(hidden, gamma, f.eps)
+                oracle.front_end_route(nb, W, f.k, act=f.act)
+                times.append(time.perf_counter() - t0)
+        med = sorted(times)[len(times) // 2]
+        entry["cpu_baseline"] = {
+            "value": f.T * len(times) / sum(times), "unit": "tokens/s", "cores": ncpu,
+            "kind": "oracle",
+            "sample": f"all {f.T} tokens, oracle RMSNorm + float64 projection + top-k, "
+                      f"{len(times)} repetitions in {sum(times):.1f} s (median {med * 1e3:.1f} ms); "
+                      f"BLAS limited to the {ncpu} CPUs of this process's affinity",
+            "median_tokens_per_s": f.T / med}
+    return entry
 
 
 def copy_calibration(torch, dev, mb):
@@ -385,6 +453,32 @@ def cpu_baseline(w, sample_T: int, seconds: float):
         times.append(time.perf_counter() - t0)
     t_total = sum(times)
     return sample_T * len(times) / t_total, len(times), t_total, sorted(times)[len(times) // 2]
+
+
+def cpu_baseline_entry(w, seconds: float, max_T: int = 4096):
+    """cpu_baseline object for a routing workload: the oracle timed on the host."""
+    sample_T = min(w.T, max_T)
+    tps, reps, secs, med = cpu_baseline(w, sample_T, seconds)
+    return {"value": tps, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{sample_T} of {w.T} tokens of the same workload, oracle route + "
+                      f"permute, {reps} repetitions in {secs:.1f} s (median "
+                      f"{med * 1e3:.1f} ms each); NumPy elementwise work on one core",
+            "median_tokens_per_s": sample_T / med}
+
+
+def near_tie_entry(w, logits, bias, ids_gpu):
+    """Near-tie tokens of a workload by the oracle's rule (a deciding exact-key
+    gap in (0, 1e-6) relative), and how many tokens' ids the GPU returned
+    differently from the oracle (each of them must be a near-tie token)."""
+    import numpy as np
+    import oracle
+    ref = oracle.route(logits, w.logits_dtype, w.k, score_fn=w.score_fn,
+                       pre_softmax=w.pre_softmax, n_group=w.n_group, topk_group=w.topk_group,
+                       group_topn=w.group_topn, renorm=w.renorm, scale=w.scale, bias=bias,
+                       bias_dtype=w.bias_dtype)
+    differ = np.any(ids_gpu != ref.ids, axis=1)
+    return {"near_tie_tokens": int(ref.exempt.sum()), "ids_differ_from_oracle": int(differ.sum()),
+            "differing_outside_near_ties": int(np.sum(differ & ~ref.exempt)), "tokens": int(w.T)}
 
 
 def host_info():
@@ -532,17 +626,15 @@ def main():
 
     others = None
     if not a.no_other_configs and a.workload == "deepseek_v3_like":
-        others = other_configs(mr, torch, np, dev, a.rotate_mb, min(K, 50))
+        others = other_configs(mr, torch, np, dev, a.rotate_mb, min(K, 50),
+                               cpu_seconds=None if a.no_cpu_baseline else a.cpu_seconds_other)
 
     cpu = None
+    near = None
     if not a.no_cpu_baseline:
-        sample_T = min(T, 4096)
-        tps, reps, secs, med = cpu_baseline(w, sample_T, a.cpu_seconds)
-        cpu = {"value": tps, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-               "sample": f"{sample_T} of {T} tokens of the same workload, oracle route + "
-                         f"permute, {reps} repetitions in {secs:.1f} s (median "
-                         f"{med * 1e3:.1f} ms each); NumPy elementwise work on one core",
-               "median_tokens_per_s": sample_T / med, "host": host_info()}
+        cpu = cpu_baseline_entry(w, a.cpu_seconds)
+        cpu["host"] = host_info()
+        near = near_tie_entry(w, logits_np, bias_np, sets[0][1].topk_ids.cpu().numpy())
 
     line = {
         "metric": "routed tokens/sec + achieved HBM GB/s, T=16384 E=256 k=8 grouped sigmoid",
@@ -579,6 +671,7 @@ def main():
             "algorithmic_bytes_per_launch": route_bytes,
         },
         "cpu_baseline": cpu,
+        "near_ties": near,
         "wall_s_timed_region": wall,
     }
     if warm is not None:

@@ -348,6 +348,13 @@ size_t moe_aux_loss_workspace_size(int64_t rows, int32_t num_experts);
 size_t rmsnorm_gate_route_workspace_size(int32_t T, int32_t H, int32_t E);
 size_t rmsnorm_gate_route_sync_region_bytes(void);
 
+/* Depth of the float32 accumulation chain of rmsnorm_gate_route's projection
+ * at hidden size H (MFMA steps of one k-chunk + number of chunks + the 32
+ * products one MFMA sums + 1): each logit errs by at most depth * 2^-24 *
+ * sum_h |normed * W| from the exact product, the bound by which near-tie
+ * tokens of the front end are classified.  -1 for an invalid H. */
+int32_t rmsnorm_gate_route_sum_depth(int32_t H);
+
 /* Output-size helpers for moe_route_permute ([FI] Returns): an upper bound on
  * total_num_padded_tokens, T*k + E_loc*(tile-1), and on the tile count,
  * that bound / tile.  Return -1 for invalid arguments. */

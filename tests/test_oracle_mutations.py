@@ -26,6 +26,7 @@ PINS = [
     T_P.pin_permutation_invariants, T_P.pin_counting_sort, T_P.pin_local_expert_shard,
     T_AF.pin_aux_closed_form, T_AF.pin_aux_finite_difference, T_AF.pin_rmsnorm,
     T_AF.pin_bf16_rounding, T_AF.pin_identity_projection, T_AF.pin_affinities_for_ids,
+    T_AF.pin_fp32_sum_near_ties,
     T_G.pin_golden_routing, T_G.pin_golden_permutation, T_G.pin_golden_aux_loss,
     T_G.pin_golden_rmsnorm,
     T_B.pin_backward_finite_differences, T_B.pin_backward_invariants,

@@ -31,6 +31,7 @@ __all__ = [
     "moe_route_workspace_size", "moe_route_count_region_bytes", "moe_aux_loss_workspace_size",
     "moe_profile_begin", "moe_profile_end", "moe_profile_read",
     "rmsnorm_gate_route_workspace_size", "rmsnorm_gate_route_sync_region_bytes",
+    "rmsnorm_gate_route_sum_depth",
     "moe_max_padded_tokens", "moe_max_tiles",
     "make_route_args", "route", "route_permute", "MoeError", "moe_route_args", "LIB_PATH",
     "MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_EWORKSPACE", "MOE_EHIP",
@@ -172,6 +173,10 @@ def rmsnorm_gate_route_workspace_size(T: int, H: int, E: int) -> int:
 
 def rmsnorm_gate_route_sync_region_bytes() -> int:
     return int(_lib.lib.rmsnorm_gate_route_sync_region_bytes())
+
+
+def rmsnorm_gate_route_sum_depth(H: int) -> int:
+    return int(_lib.lib.rmsnorm_gate_route_sum_depth(H))
 
 
 def moe_max_padded_tokens(T: int, k: int, local_num_experts: int, tile: int) -> int:

@@ -24,6 +24,7 @@ EXPORTED = [
     "moe_dispatch", "moe_combine", "moe_topk_to_dense",
     "moe_route_workspace_size", "moe_route_count_region_bytes", "moe_aux_loss_workspace_size",
     "rmsnorm_gate_route_workspace_size", "rmsnorm_gate_route_sync_region_bytes",
+    "rmsnorm_gate_route_sum_depth",
     "moe_max_padded_tokens", "moe_max_tiles",
     "moe_status_string", "moe_last_error_message", "moe_last_hip_error",
     "moe_profile_begin", "moe_profile_end", "moe_profile_read",
@@ -112,6 +113,8 @@ def _load():
     lib.rmsnorm_gate_route_workspace_size.restype = sz
     lib.rmsnorm_gate_route_sync_region_bytes.argtypes = []
     lib.rmsnorm_gate_route_sync_region_bytes.restype = sz
+    lib.rmsnorm_gate_route_sum_depth.argtypes = [i32]
+    lib.rmsnorm_gate_route_sum_depth.restype = i32
     lib.moe_max_padded_tokens.argtypes = [i32, i32, i32, i32]
     lib.moe_max_padded_tokens.restype = i64
     lib.moe_max_tiles.argtypes = [i32, i32, i32, i32]

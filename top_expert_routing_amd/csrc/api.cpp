@@ -676,6 +676,12 @@ size_t rmsnorm_gate_route_workspace_size(int32_t T, int32_t H, int32_t E) {
 
 size_t rmsnorm_gate_route_sync_region_bytes(void) { return moe::kFrontEndSyncBytes; }
 
+int32_t rmsnorm_gate_route_sum_depth(int32_t H) {
+  if (H < 128 || H % 128 || H > 16384) return -1;
+  const int kc = moe::front_end_kchunk(H);
+  return kc / 32 + H / kc + 32 + 1;
+}
+
 moe_status rmsnorm_gate_route(const void* hidden, const void* gamma, const void* router_weights,
                               const void* router_bias, int32_t dtype, int32_t T, int32_t H,
                               int32_t E, float eps, int32_t top_k, int32_t act_fn, void* normed,

@@ -35,9 +35,10 @@ __device__ __forceinline__ float unord_key(uint32_t o) {
 
 // Selection order as one unsigned 64-bit integer: larger key first, then the
 // lower expert index (its complement is larger).  Distinct experts never
-// compare equal.
+// compare equal.  -0 is folded into +0 first (x + 0.0f), so that two zero keys
+// are equal and the index decides between them.
 __device__ __forceinline__ uint64_t pack_key(float key, int idx) {
-  return ((uint64_t)ord_key(key) << 32) | (uint64_t)(~(uint32_t)idx);
+  return ((uint64_t)ord_key(key + 0.0f) << 32) | (uint64_t)(~(uint32_t)idx);
 }
 __device__ __forceinline__ int unpack_idx(uint64_t p) { return (int)(~(uint32_t)p); }
 

@@ -610,7 +610,10 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>)
     }
     // candidate bits: key[i] >= tau.  The sign bit of key[i] - tau marks the
     // keys below tau (-inf stays -inf; equal keys give +0); alignbit shifts it
-    // in, top element first, so that bit i belongs to element i.
+    // in, top element first, so that bit i belongs to element i.  A zero tau
+    // is taken as -0: then both -0 and +0 keys give +0 (x - x = +0, +0 - -0 =
+    // +0) and count as equal to it.
+    tau = tau == 0.0f ? -0.0f : tau;
     uint32_t below_hi = 0, below_lo = 0;
 #pragma unroll
     for (int i = EPL / 2 - 1; i >= 0; --i) {
