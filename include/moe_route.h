@@ -205,6 +205,34 @@ moe_status moe_route_permute(const moe_route_args* args, int32_t tile_tokens_dim
                              int32_t* cta_idx_xy_to_mn_limit, void* workspace,
                              size_t workspace_bytes, hipStream_t stream);
 
+/* moe_route_permute without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Arguments, outputs and results are those of
+ * moe_route_permute; the scratch (counting region and per-block counts) is a
+ * library-owned device array of moe_route_permute_noalloc_max_scratch_bytes()
+ * bytes (8 MiB), one per device, held until the process ends.  A call whose
+ * moe_route_workspace_size() exceeds it (more than about 1.96 million pairs
+ * of a 64-token block and a local expert: T = 262144 with 256 local experts
+ * fits, twice that does not) fails with MOE_EUNSUPPORTED before anything is
+ * enqueued.  The call allocates nothing: no hipMalloc, no host or
+ * device allocation of any kind.  The first call on a device (and the first
+ * after a call on it returned MOE_EHIP) enqueues a zero-fill kernel of the
+ * counting region ahead of its work; every completed call leaves that region
+ * zero.  All calls on one device share the array: calls that overlap on one
+ * device (different streams, or different host threads) race and must be
+ * ordered by the caller. */
+moe_status moe_route_permute_noalloc(const moe_route_args* args, int32_t tile_tokens_dim,
+                                     int32_t local_expert_offset, int32_t local_num_experts,
+                                     const void* logits, const void* bias, int32_t* topk_ids,
+                                     void* topk_weights, float* scores, int32_t* expert_counts,
+                                     int32_t* padded_offsets, int32_t* total_num_padded_tokens,
+                                     int32_t* num_non_exiting_ctas,
+                                     int32_t* expanded_idx_to_permuted_idx,
+                                     int32_t* permuted_idx_to_token_idx,
+                                     int32_t* cta_idx_xy_to_batch_idx,
+                                     int32_t* cta_idx_xy_to_mn_limit, hipStream_t stream);
+size_t moe_route_permute_noalloc_max_scratch_bytes(void);
+
 /* Load-balancing aux loss ([TE] FusedAuxLoss, forward and backward, with the
  * arguments of fused_moe_aux_loss):
  *

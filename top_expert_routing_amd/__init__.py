@@ -34,6 +34,7 @@ __all__ = [
     "rmsnorm_gate_route_sum_depth",
     "moe_max_padded_tokens", "moe_max_tiles",
     "make_route_args", "route", "route_permute", "MoeError", "moe_route_args", "LIB_PATH",
+    "moe_route_permute_noalloc", "moe_route_permute_noalloc_max_scratch_bytes",
     "MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_EWORKSPACE", "MOE_EHIP",
     "MOE_F32", "MOE_BF16", "MOE_F16", "MOE_SOFTMAX", "MOE_SIGMOID",
 ]
@@ -101,6 +102,26 @@ def moe_route_permute(args: moe_route_args, tile_tokens_dim: int, local_expert_o
         _ptr(permuted_idx_to_token_idx), _ptr(cta_idx_xy_to_batch_idx),
         _ptr(cta_idx_xy_to_mn_limit), _ptr(workspace), ctypes.c_size_t(ws_bytes),
         _stream(stream)))
+
+
+def moe_route_permute_noalloc(args: moe_route_args, tile_tokens_dim: int,
+                              local_expert_offset: int, local_num_experts: int, logits, bias,
+                              topk_ids, topk_weights, scores, expert_counts, padded_offsets,
+                              total_num_padded_tokens, num_non_exiting_ctas,
+                              expanded_idx_to_permuted_idx, permuted_idx_to_token_idx,
+                              cta_idx_xy_to_batch_idx, cta_idx_xy_to_mn_limit,
+                              stream=None) -> None:
+    _check(_lib.lib.moe_route_permute_noalloc(
+        ctypes.byref(args), tile_tokens_dim, local_expert_offset, local_num_experts,
+        _ptr(logits), _ptr(bias), _ptr(topk_ids), _ptr(topk_weights), _ptr(scores),
+        _ptr(expert_counts), _ptr(padded_offsets), _ptr(total_num_padded_tokens),
+        _ptr(num_non_exiting_ctas), _ptr(expanded_idx_to_permuted_idx),
+        _ptr(permuted_idx_to_token_idx), _ptr(cta_idx_xy_to_batch_idx),
+        _ptr(cta_idx_xy_to_mn_limit), _stream(stream)))
+
+
+def moe_route_permute_noalloc_max_scratch_bytes() -> int:
+    return int(_lib.lib.moe_route_permute_noalloc_max_scratch_bytes())
 
 
 def moe_aux_loss(probs, tokens_per_expert, rows: int, total_num_tokens: int, num_experts: int,

@@ -20,7 +20,8 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EUNSUPPORTED", 3: "MOE_EWO
 
 # Every symbol the header declares.
 EXPORTED = [
-    "moe_route", "moe_route_permute", "moe_aux_loss", "rmsnorm_gate_route", "moe_route_backward",
+    "moe_route", "moe_route_permute", "moe_route_permute_noalloc",
+    "moe_route_permute_noalloc_max_scratch_bytes", "moe_aux_loss", "rmsnorm_gate_route", "moe_route_backward",
     "moe_dispatch", "moe_combine", "moe_topk_to_dense",
     "moe_route_workspace_size", "moe_route_count_region_bytes", "moe_aux_loss_workspace_size",
     "rmsnorm_gate_route_workspace_size", "rmsnorm_gate_route_sync_region_bytes",
@@ -90,6 +91,10 @@ def _load():
     lib.moe_route.restype = i32
     lib.moe_route_permute.argtypes = [args_p, i32, i32, i32] + [vp] * 14 + [sz, vp]
     lib.moe_route_permute.restype = i32
+    lib.moe_route_permute_noalloc.argtypes = [args_p, i32, i32, i32] + [vp] * 13 + [vp]
+    lib.moe_route_permute_noalloc.restype = i32
+    lib.moe_route_permute_noalloc_max_scratch_bytes.argtypes = []
+    lib.moe_route_permute_noalloc_max_scratch_bytes.restype = sz
     lib.moe_aux_loss.argtypes = [vp, vp, i64, i64, i32, i32, f32, vp, vp, vp, vp, sz, vp]
     lib.moe_aux_loss.restype = i32
     lib.moe_route_backward.argtypes = [args_p, vp, vp, vp, vp, vp, vp]

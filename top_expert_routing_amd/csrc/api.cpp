@@ -203,6 +203,7 @@ int num_blocks(int T) { return (T + moe::kTokensPerBlock - 1) / moe::kTokensPerB
 // calls.
 constexpr size_t kCountRowsBytes = (size_t)moe::kMaxSuperRows * kMaxExperts * sizeof(int32_t);
 constexpr size_t kCountRegionBytes = kCountRowsBytes + 17 * 256;   // + the block counters
+static_assert(kCountRegionBytes % 256 == 0, "the per-block counts follow 256-byte aligned");
 
 struct CountPlan {
   int nb = 0, group_blocks = 1, num_super = 1;
@@ -287,6 +288,172 @@ moe_status launch_route_checked(const moe::RouteParams& p, const Shape& sh, bool
     return moe::launch_route(p, sh.lpt, sh.epl, bf16, num_blocks(p.T), stream);
   });
   if (e != hipSuccess) return hip_fail(e, "route_kernel launch");
+  return MOE_OK;
+}
+
+// Scratch of moe_route_permute: the caller's workspace.
+struct CallerWorkspace {
+  void* ptr;
+  size_t bytes;
+  moe_status get(size_t need, void** ws, hipStream_t) {
+    if (ptr == nullptr || bytes < need) return fail(MOE_EWORKSPACE, "workspace needs %zu bytes", need);
+    if (!aligned(ptr, 256)) return fail(MOE_EINVAL, "workspace must be 256-byte aligned");
+    *ws = ptr;
+    return MOE_OK;
+  }
+};
+
+// Scratch of moe_route_permute_noalloc: a file-scope device array of fixed
+// size, one instance on every device the library runs on.  Host code never
+// uses the array's name as an address (on the host it is a stand-in symbol):
+// the device address comes from hipGetSymbolAddress, taken once per device
+// with that device current, and only that address is passed to kernels.
+// Its counting region must be zero on entry to a call and every completed
+// call leaves it zero; a zero-fill kernel runs before the first call on a
+// device and after a call on it failed to launch (the region may then be
+// dirty).  Every call on one device shares the array: calls that overlap on
+// one device race.
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+static_assert(kScratchBytes > kCountRegionBytes, "scratch holds the counting region");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kScratchMaxDevices = 64;
+struct ScratchState {
+  std::mutex mu;
+  void* ptr[kScratchMaxDevices] = {};
+  bool dirty[kScratchMaxDevices] = {};
+};
+ScratchState& scratch_state() {
+  static ScratchState* s = new ScratchState();
+  return *s;
+}
+
+struct StaticScratch {
+  int device = -1;
+  moe_status get(size_t need, void** ws, hipStream_t stream) {
+    if (need > kScratchBytes)
+      return fail(MOE_EUNSUPPORTED,
+                  "this call needs %zu bytes of scratch; moe_route_permute_noalloc holds %zu "
+                  "(use moe_route_permute with a workspace)",
+                  need, kScratchBytes);
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kScratchMaxDevices)
+      return fail(MOE_EUNSUPPORTED, "device index %d >= %d", dev, kScratchMaxDevices);
+    ScratchState& S = scratch_state();
+    std::lock_guard<std::mutex> lk(S.mu);
+    if (S.ptr[dev] == nullptr) {
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+      if (p == nullptr || !aligned(p, 256)) return fail(MOE_EHIP, "scratch address not aligned");
+      S.ptr[dev] = p;
+      S.dirty[dev] = true;
+    }
+    device = dev;
+    if (S.dirty[dev]) {
+      e = moe::launch_zero_fill(S.ptr[dev], kCountRegionBytes, stream);
+      if (e != hipSuccess) return hip_fail(e, "scratch zero-fill launch");
+      S.dirty[dev] = false;
+    }
+    *ws = S.ptr[dev];
+    return MOE_OK;
+  }
+};
+
+// moe_route_permute with its scratch from `wsp` (the caller's workspace or the
+// library's static scratch), asked for only after every argument is validated.
+template <class WS>
+moe_status route_permute_impl(const moe_route_args* args, int32_t tile, int32_t loc_off,
+                              int32_t loc_n, const void* logits, const void* bias,
+                              int32_t* topk_ids, void* topk_weights, float* scores,
+                              int32_t* expert_counts, int32_t* padded_offsets,
+                              int32_t* total_num_padded_tokens, int32_t* num_non_exiting_ctas,
+                              int32_t* e2p, int32_t* p2t, int32_t* batch_idx, int32_t* mn_limit,
+                              WS& wsp, hipStream_t stream) {
+  Shape sh;
+  moe_status st = validate_route(args, &sh);
+  if (st != MOE_OK) return st;
+  const moe_route_args& a = *args;
+  const int T = a.num_tokens, E = a.num_experts;
+  if (!is_pow2(tile) || tile > 1024)
+    return fail(MOE_EINVAL, "tile_tokens_dim must be a power of two in [1, 1024]");
+  if (loc_off < 0 || loc_n < 1 || (int64_t)loc_off + loc_n > E)
+    return fail(MOE_EINVAL, "local experts [off, off + n) must lie inside [0, E)");
+  if (expert_counts == nullptr || padded_offsets == nullptr ||
+      total_num_padded_tokens == nullptr || num_non_exiting_ctas == nullptr)
+    return fail(MOE_EINVAL, "bookkeeping outputs are required");
+  if ((int64_t)T * a.top_k + (int64_t)loc_n * (tile - 1) > INT32_MAX)
+    return fail(MOE_EUNSUPPORTED, "padded token count exceeds int32");
+  if (T == 0) {
+    hipError_t e = moe::launch_empty_outputs(expert_counts, loc_n, padded_offsets,
+                                             total_num_padded_tokens, num_non_exiting_ctas,
+                                             stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "empty_outputs launch");
+  }
+  if (logits == nullptr || topk_ids == nullptr || topk_weights == nullptr || e2p == nullptr ||
+      p2t == nullptr || batch_idx == nullptr || mn_limit == nullptr)
+    return fail(MOE_EINVAL, "a required pointer is NULL");
+  if (a.weights_dtype == MOE_F32 && !aligned(topk_weights, 4))
+    return fail(MOE_EINVAL, "topk_weights must be 4-byte aligned");
+  const size_t need = route_ws_bytes(a, loc_n, true);
+  void* workspace = nullptr;
+  st = wsp.get(need, &workspace, stream);
+  if (st != MOE_OK) return st;
+  const CountPlan cp = count_plan(T);
+  int32_t* rows = ws_count_rows(workspace);
+  int32_t* hist = ws_hist(workspace);
+
+  if (cp.nb == 1) {
+    // every token in one route block: the route kernel finishes the
+    // permutation from its own bitmask (no counting rows, no second launch)
+    moe::RouteParams p = make_params(a, sh, logits, bias, topk_ids, topk_weights, scores, nullptr,
+                                     nullptr, cp.group_blocks, loc_off, loc_n);
+    p.fused = 1;
+    p.hmask_len = (loc_n + 1) & ~1;                     // the bitmask, without counting rows
+    p.tile = tile;
+    p.tile_shift = log2_exact(tile);
+    p.e2p = e2p;
+    p.p2t = p2t;
+    p.counts = expert_counts;
+    p.padded_offsets = padded_offsets;
+    p.total_out = total_num_padded_tokens;
+    p.nctas_out = num_non_exiting_ctas;
+    p.batch_idx = batch_idx;
+    p.mn_limit = mn_limit;
+    return launch_route_checked(p, sh, a.logits_dtype == MOE_BF16, stream);
+  }
+  const moe::RouteParams p = make_params(a, sh, logits, bias, topk_ids, topk_weights, scores,
+                                         rows, hist, cp.group_blocks, loc_off, loc_n);
+  st = launch_route_checked(p, sh, a.logits_dtype == MOE_BF16, stream);
+  if (st != MOE_OK) return st;
+
+  moe::ScatterParams q{};
+  q.ids = topk_ids;
+  q.T = T;
+  q.k = a.top_k;
+  q.El = loc_n;
+  q.off = loc_off;
+  q.tile = tile;
+  q.tile_shift = log2_exact(tile);
+  q.k_magic = (uint32_t)(((1u << 20) + (uint32_t)a.top_k - 1u) / (uint32_t)a.top_k);
+  q.super_rows = rows;
+  q.hist = hist;
+  q.done = ws_done(workspace);
+  q.group_blocks = cp.group_blocks;
+  q.num_super = cp.num_super;
+  q.counts = expert_counts;
+  q.e2p = e2p;
+  q.p2t = p2t;
+  q.padded_offsets = padded_offsets;
+  q.total_out = total_num_padded_tokens;
+  q.nctas_out = num_non_exiting_ctas;
+  q.batch_idx = batch_idx;
+  q.mn_limit = mn_limit;
+  hipError_t e = launch_with_profile(MOE_KERNEL_SCATTER, stream,
+                                     [&] { return moe::launch_scatter(q, cp.nb, stream); });
+  if (e != hipSuccess) return hip_fail(e, "scatter_kernel launch");
   return MOE_OK;
 }
 
@@ -424,90 +591,30 @@ moe_status moe_route_permute(const moe_route_args* args, int32_t tile, int32_t l
                              int32_t* e2p, int32_t* p2t, int32_t* batch_idx, int32_t* mn_limit,
                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
   clear_error();
-  Shape sh;
-  moe_status st = validate_route(args, &sh);
-  if (st != MOE_OK) return st;
-  const moe_route_args& a = *args;
-  const int T = a.num_tokens, E = a.num_experts;
-  if (!is_pow2(tile) || tile > 1024)
-    return fail(MOE_EINVAL, "tile_tokens_dim must be a power of two in [1, 1024]");
-  if (loc_off < 0 || loc_n < 1 || (int64_t)loc_off + loc_n > E)
-    return fail(MOE_EINVAL, "local experts [off, off + n) must lie inside [0, E)");
-  if (expert_counts == nullptr || padded_offsets == nullptr ||
-      total_num_padded_tokens == nullptr || num_non_exiting_ctas == nullptr)
-    return fail(MOE_EINVAL, "bookkeeping outputs are required");
-  if ((int64_t)T * a.top_k + (int64_t)loc_n * (tile - 1) > INT32_MAX)
-    return fail(MOE_EUNSUPPORTED, "padded token count exceeds int32");
-  if (T == 0) {
-    hipError_t e = moe::launch_empty_outputs(expert_counts, loc_n, padded_offsets,
-                                             total_num_padded_tokens, num_non_exiting_ctas,
-                                             stream);
-    return e == hipSuccess ? MOE_OK : hip_fail(e, "empty_outputs launch");
-  }
-  if (logits == nullptr || topk_ids == nullptr || topk_weights == nullptr || e2p == nullptr ||
-      p2t == nullptr || batch_idx == nullptr || mn_limit == nullptr)
-    return fail(MOE_EINVAL, "a required pointer is NULL");
-  if (a.weights_dtype == MOE_F32 && !aligned(topk_weights, 4))
-    return fail(MOE_EINVAL, "topk_weights must be 4-byte aligned");
-  const size_t need = route_ws_bytes(a, loc_n, true);
-  if (workspace == nullptr || workspace_bytes < need)
-    return fail(MOE_EWORKSPACE, "workspace needs %zu bytes", need);
-  if (!aligned(workspace, 256)) return fail(MOE_EINVAL, "workspace must be 256-byte aligned");
-  const CountPlan cp = count_plan(T);
-  int32_t* rows = ws_count_rows(workspace);
-  int32_t* hist = ws_hist(workspace);
-
-  if (cp.nb == 1) {
-    // every token in one route block: the route kernel finishes the
-    // permutation from its own bitmask (no counting rows, no second launch)
-    moe::RouteParams p = make_params(a, sh, logits, bias, topk_ids, topk_weights, scores, nullptr,
-                                     nullptr, cp.group_blocks, loc_off, loc_n);
-    p.fused = 1;
-    p.hmask_len = (loc_n + 1) & ~1;                     // the bitmask, without counting rows
-    p.tile = tile;
-    p.tile_shift = log2_exact(tile);
-    p.e2p = e2p;
-    p.p2t = p2t;
-    p.counts = expert_counts;
-    p.padded_offsets = padded_offsets;
-    p.total_out = total_num_padded_tokens;
-    p.nctas_out = num_non_exiting_ctas;
-    p.batch_idx = batch_idx;
-    p.mn_limit = mn_limit;
-    return launch_route_checked(p, sh, a.logits_dtype == MOE_BF16, stream);
-  }
-  const moe::RouteParams p = make_params(a, sh, logits, bias, topk_ids, topk_weights, scores,
-                                         rows, hist, cp.group_blocks, loc_off, loc_n);
-  st = launch_route_checked(p, sh, a.logits_dtype == MOE_BF16, stream);
-  if (st != MOE_OK) return st;
-
-  moe::ScatterParams q{};
-  q.ids = topk_ids;
-  q.T = T;
-  q.k = a.top_k;
-  q.El = loc_n;
-  q.off = loc_off;
-  q.tile = tile;
-  q.tile_shift = log2_exact(tile);
-  q.k_magic = (uint32_t)(((1u << 20) + (uint32_t)a.top_k - 1u) / (uint32_t)a.top_k);
-  q.super_rows = rows;
-  q.hist = hist;
-  q.done = ws_done(workspace);
-  q.group_blocks = cp.group_blocks;
-  q.num_super = cp.num_super;
-  q.counts = expert_counts;
-  q.e2p = e2p;
-  q.p2t = p2t;
-  q.padded_offsets = padded_offsets;
-  q.total_out = total_num_padded_tokens;
-  q.nctas_out = num_non_exiting_ctas;
-  q.batch_idx = batch_idx;
-  q.mn_limit = mn_limit;
-  hipError_t e = launch_with_profile(MOE_KERNEL_SCATTER, stream,
-                                     [&] { return moe::launch_scatter(q, cp.nb, stream); });
-  if (e != hipSuccess) return hip_fail(e, "scatter_kernel launch");
-  return MOE_OK;
+  CallerWorkspace ws{workspace, workspace_bytes};
+  return route_permute_impl(args, tile, loc_off, loc_n, logits, bias, topk_ids, topk_weights,
+                            scores, expert_counts, padded_offsets, total_num_padded_tokens,
+                            num_non_exiting_ctas, e2p, p2t, batch_idx, mn_limit, ws, stream);
 }
+
+moe_status moe_route_permute_noalloc(const moe_route_args* args, int32_t tile, int32_t loc_off,
+                                     int32_t loc_n, const void* logits, const void* bias,
+                                     int32_t* topk_ids, void* topk_weights, float* scores,
+                                     int32_t* expert_counts, int32_t* padded_offsets,
+                                     int32_t* total_num_padded_tokens,
+                                     int32_t* num_non_exiting_ctas, int32_t* e2p, int32_t* p2t,
+                                     int32_t* batch_idx, int32_t* mn_limit, hipStream_t stream) {
+  clear_error();
+  StaticScratch ws;
+  const moe_status st = route_permute_impl(
+      args, tile, loc_off, loc_n, logits, bias, topk_ids, topk_weights, scores, expert_counts,
+      padded_offsets, total_num_padded_tokens, num_non_exiting_ctas, e2p, p2t, batch_idx,
+      mn_limit, ws, stream);
+  if (st == MOE_EHIP && ws.device >= 0) scratch_state().dirty[ws.device] = true;
+  return st;
+}
+
+size_t moe_route_permute_noalloc_max_scratch_bytes(void) { return kScratchBytes; }
 
 size_t moe_aux_loss_workspace_size(int64_t rows, int32_t num_experts) {
   if (rows < 0 || num_experts < 1) return 0;

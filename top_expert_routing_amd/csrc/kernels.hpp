@@ -145,6 +145,8 @@ hipError_t launch_counts(int32_t* super_rows, int num_super, int El, int32_t* co
 hipError_t launch_scatter(const ScatterParams& p, int nb, hipStream_t s);
 hipError_t launch_empty_outputs(int32_t* counts, int El, int32_t* padded_offsets, int32_t* total,
                                 int32_t* nctas, hipStream_t s);
+// Zero `bytes` (a multiple of 16) at the 16-byte aligned device address p.
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s);
 
 // Backward of the routing outputs (see route_backward.hip).
 enum { kBwdSigmoid = 0, kBwdSoftmaxPre = 1, kBwdSoftmaxPost = 2 };

@@ -268,6 +268,14 @@ __global__ void empty_outputs_kernel(int32_t* counts, int El, int32_t* padded_of
   }
 }
 
+// Zero-fill of a 16-byte aligned region of n16 16-byte words (a kernel, so that
+// it may be captured into a HIP graph where a memset node may not).
+__global__ void zero_fill_kernel(u32x4* __restrict__ p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
 // ---- host-side launchers -------------------------------------------------------------
 
 // Instances of the route kernel, one translation unit per score variant.
@@ -331,6 +339,14 @@ hipError_t launch_scatter(const ScatterParams& p, int nb, hipStream_t s) {
   const int rows = p.num_super > p.group_blocks - 1 ? p.num_super : p.group_blocks - 1;
   if (2 * p.El <= kScatterThreads && rows > 16) launch_scatter_s<2>(p, nb, s);
   else launch_scatter_s<1>(p, nb, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t s) {
+  const size_t n16 = bytes / 16;
+  const int blocks = (int)((n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024);
+  if (blocks > 0)
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(blocks), dim3(256), 0, s, static_cast<u32x4*>(p), n16);
   return hipGetLastError();
 }
 
