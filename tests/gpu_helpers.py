@@ -115,3 +115,18 @@ def fetch_permutation(out) -> dict:
         batch_idx=out.cta_idx_xy_to_batch_idx.cpu().numpy().astype(np.int64),
         mn_limit=out.cta_idx_xy_to_mn_limit.cpu().numpy().astype(np.int64),
     )
+
+
+def count_region_ready(ws, label=""):
+    """The routing workspace's counting region is ready for the next call: its
+    two sets of counting rows are followed by a header whose first word names
+    the set the next call adds into, and that set must be entirely zero."""
+    import torch
+    from top_expert_routing_amd import moe_route_count_region_bytes
+    region = moe_route_count_region_bytes()
+    set_bytes = (region - 256) // 2
+    hdr = ws[2 * set_bytes:2 * set_bytes + 16].view(torch.int32).cpu().tolist()
+    nxt = hdr[0]
+    assert nxt in (0, 1), (label, hdr)
+    used = ws[nxt * set_bytes:(nxt + 1) * set_bytes]
+    assert int(used.count_nonzero().item()) == 0, f"{label}: counting set {nxt} not clear"

@@ -1,19 +1,20 @@
 """GPU: the entry points captured into a HIP graph and replayed.
 
 The benchmark replays moe_route_permute, moe_aux_loss and rmsnorm_gate_route
-from captured graphs, whose kernels clear the routing counting region and the
-front-end synchronisation region themselves (no memset nodes).  Each test
-captures one call, then replays it several times with the program's own eager
-work and synchronisations between the replays, poisoning the outputs before
-every replay; every replay must reproduce the eager call's outputs bit for bit,
-and the cleared regions must be zero again afterwards.
+from captured graphs, whose kernels keep the routing counting region and the
+front-end synchronisation region ready themselves (no memset nodes).  Each
+test captures one call, then replays it several times with the program's own
+eager work and synchronisations between the replays, poisoning the outputs
+before every replay; every replay must reproduce the eager call's outputs bit
+for bit, the front end's region must be zero again afterwards and the routing
+workspace's set of counting rows for the next call must be clear.
 """
 from __future__ import annotations
 
 import numpy as np
 import pytest
 
-from gpu_helpers import log, to_dev
+from gpu_helpers import count_region_ready, log, to_dev
 from workloads import FRONT_END, WORKLOADS, front_end_inputs, route_inputs, with_overrides
 
 pytestmark = pytest.mark.gpu
@@ -63,7 +64,6 @@ def test_route_permute_graph_replays(name, T):
     g = _capture(lambda: mr.route_permute(args, x, b, tile=w.tile, out=out))
     total = int(ref.total_num_padded_tokens.item())
     ntiles = int(ref.num_non_exiting_ctas.item())
-    region = mr.moe_route_count_region_bytes()
     for rep in range(REPLAYS):
         for f in _ROUTE_FIELDS + ("permuted_idx_to_token_idx", "cta_idx_xy_to_batch_idx",
                                   "cta_idx_xy_to_mn_limit"):
@@ -75,7 +75,7 @@ def test_route_permute_graph_replays(name, T):
         assert torch.equal(out.permuted_idx_to_token_idx[:total], ref.permuted_idx_to_token_idx[:total])
         assert torch.equal(out.cta_idx_xy_to_batch_idx[:ntiles], ref.cta_idx_xy_to_batch_idx[:ntiles])
         assert torch.equal(out.cta_idx_xy_to_mn_limit[:ntiles], ref.cta_idx_xy_to_mn_limit[:ntiles])
-        assert int(out.workspace[:region].count_nonzero().item()) == 0, (name, rep)
+        count_region_ready(out.workspace, f"{name} replay {rep}")
         # the program's own eager work between replays, on other buffers
         other = mr.route_permute(args, x2, b, tile=w.tile)
         torch.cuda.synchronize()

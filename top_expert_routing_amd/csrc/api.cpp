@@ -197,12 +197,14 @@ moe_status validate_route(const moe_route_args* a, Shape* shape) {
 
 int num_blocks(int T) { return (T + moe::kTokensPerBlock - 1) / moe::kTokensPerBlock; }
 
-// Routing workspace: [counting rows | done counter][per-block counts].  The
-// first region has a fixed size (kMaxSuperRows rows of up to kMaxExperts), so
-// that it lies at the same place whatever the call's sizes; it is zero between
-// calls.
-constexpr size_t kCountRowsBytes = (size_t)moe::kMaxSuperRows * kMaxExperts * sizeof(int32_t);
-constexpr size_t kCountRegionBytes = kCountRowsBytes + 17 * 256;   // + the block counters
+// Routing workspace: [counting rows, two sets | their header][per-block
+// counts].  The first region has a fixed size (two sets of kMaxSuperRows rows
+// of up to kMaxExperts, a 256-byte header), so that it lies at the same place
+// whatever the call's sizes; it must be zero before the first call and every
+// call leaves it ready for the next (kernels.hpp: kCountSetInts).
+static_assert(kMaxExperts == moe::kMaxCountExperts, "counting rows hold every expert");
+constexpr size_t kCountRowsBytes = (size_t)moe::kCountSetInts * sizeof(int32_t);   // one set
+constexpr size_t kCountRegionBytes = 2 * kCountRowsBytes + 256;   // two sets + their header
 static_assert(kCountRegionBytes % 256 == 0, "the per-block counts follow 256-byte aligned");
 
 struct CountPlan {
@@ -225,8 +227,8 @@ size_t route_ws_bytes(const moe_route_args& a, int loc_n, bool permute) {
          (permute ? align256((size_t)num_blocks(a.num_tokens) * loc_n * sizeof(int32_t)) : 0);
 }
 int32_t* ws_count_rows(void* ws) { return static_cast<int32_t*>(ws); }
-uint32_t* ws_done(void* ws) {
-  return reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kCountRowsBytes);
+uint32_t* ws_count_hdr(void* ws) {
+  return reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + 2 * kCountRowsBytes);
 }
 int32_t* ws_hist(void* ws) {
   return reinterpret_cast<int32_t*>(static_cast<char*>(ws) + kCountRegionBytes);
@@ -236,9 +238,11 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 moe::RouteParams make_params(const moe_route_args& a, const Shape& sh, const void* logits,
                              const void* bias, int32_t* ids, void* weights, float* scores,
-                             int32_t* super_rows, int32_t* hist, int group_blocks, int loc_off,
-                             int loc_n) {
+                             int32_t* super_rows, uint32_t* count_hdr, int32_t* hist,
+                             int group_blocks, int num_super, int loc_off, int loc_n) {
   moe::RouteParams p{};
+  p.count_hdr = count_hdr;
+  p.num_super = num_super;
   p.logits = logits;
   p.bias = bias;
   p.ids = ids;
@@ -281,7 +285,7 @@ moe_status launch_route_checked(const moe::RouteParams& p, const Shape& sh, bool
   const int rwpl = (p.variant == moe::kVarSoftmax && bf16) ? sh.epl / 2 : sh.epl;
   const size_t lds = moe::route_lds_bytes(sh.lpt, rwpl, sh.epl, p.hmask_len, p.cap, p.k,
                                           p.grouped ? p.n_group : 0) +
-                     (p.fused ? (((size_t)p.loc_n + 1) * 4 + 15) & ~(size_t)15 : 0);
+                     (p.fused ? (((size_t)p.loc_n + 1) * 4 + 32 + 15) & ~(size_t)15 : 0);
   if (lds > 160 * 1024)
     return fail(MOE_EUNSUPPORTED, "route kernel needs %zu bytes of LDS", lds);
   hipError_t e = launch_with_profile(MOE_KERNEL_ROUTE, stream, [&] {
@@ -409,7 +413,8 @@ moe_status route_permute_impl(const moe_route_args* args, int32_t tile, int32_t 
     // every token in one route block: the route kernel finishes the
     // permutation from its own bitmask (no counting rows, no second launch)
     moe::RouteParams p = make_params(a, sh, logits, bias, topk_ids, topk_weights, scores, nullptr,
-                                     nullptr, cp.group_blocks, loc_off, loc_n);
+                                     nullptr, nullptr, cp.group_blocks, cp.num_super, loc_off,
+                                     loc_n);
     p.fused = 1;
     p.hmask_len = (loc_n + 1) & ~1;                     // the bitmask, without counting rows
     p.tile = tile;
@@ -425,7 +430,8 @@ moe_status route_permute_impl(const moe_route_args* args, int32_t tile, int32_t 
     return launch_route_checked(p, sh, a.logits_dtype == MOE_BF16, stream);
   }
   const moe::RouteParams p = make_params(a, sh, logits, bias, topk_ids, topk_weights, scores,
-                                         rows, hist, cp.group_blocks, loc_off, loc_n);
+                                         rows, ws_count_hdr(workspace), hist, cp.group_blocks,
+                                         cp.num_super, loc_off, loc_n);
   st = launch_route_checked(p, sh, a.logits_dtype == MOE_BF16, stream);
   if (st != MOE_OK) return st;
 
@@ -440,7 +446,7 @@ moe_status route_permute_impl(const moe_route_args* args, int32_t tile, int32_t 
   q.k_magic = (uint32_t)(((1u << 20) + (uint32_t)a.top_k - 1u) / (uint32_t)a.top_k);
   q.super_rows = rows;
   q.hist = hist;
-  q.done = ws_done(workspace);
+  q.count_hdr = ws_count_hdr(workspace);
   q.group_blocks = cp.group_blocks;
   q.num_super = cp.num_super;
   q.counts = expert_counts;
@@ -562,6 +568,7 @@ moe_status moe_route(const moe_route_args* args, const void* logits, const void*
   if (a.weights_dtype == MOE_F32 && !aligned(topk_weights, 4))
     return fail(MOE_EINVAL, "topk_weights must be 4-byte aligned");
   int32_t* rows = nullptr;
+  uint32_t* hdr = nullptr;
   const CountPlan cp = count_plan(T);
   if (expert_counts != nullptr) {
     const size_t need = route_ws_bytes(a, E, false);
@@ -569,14 +576,15 @@ moe_status moe_route(const moe_route_args* args, const void* logits, const void*
       return fail(MOE_EWORKSPACE, "workspace needs %zu bytes", need);
     if (!aligned(workspace, 256)) return fail(MOE_EINVAL, "workspace must be 256-byte aligned");
     rows = ws_count_rows(workspace);
+    hdr = ws_count_hdr(workspace);
   }
   const moe::RouteParams p = make_params(a, sh, logits, bias, topk_ids, topk_weights, scores,
-                                         rows, nullptr, cp.group_blocks, 0, E);
+                                         rows, hdr, nullptr, cp.group_blocks, cp.num_super, 0, E);
   st = launch_route_checked(p, sh, a.logits_dtype == MOE_BF16, stream);
   if (st != MOE_OK) return st;
   if (rows != nullptr) {
     hipError_t e = launch_with_profile(MOE_KERNEL_COUNTS, stream, [&] {
-      return moe::launch_counts(rows, cp.num_super, E, expert_counts, stream);
+      return moe::launch_counts(rows, hdr, cp.num_super, E, expert_counts, stream);
     });
     if (e != hipSuccess) return hip_fail(e, "counts_kernel launch");
   }

@@ -222,6 +222,42 @@ __device__ __forceinline__ void bitonic_desc(uint64_t (&v)[NS / LPT], int lane_c
   }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wavefront (lane i gets the sum
+// of lanes 0..i), all in DPP moves: shifts by 1, 2, 4, 8 inside each 16-lane
+// row (lanes without a source add 0), then row_bcast:15 adds row 0's total to
+// row 1 and row 2's to row 3, and row_bcast:31 adds lanes 0..31's total to
+// rows 2 and 3.  Every lane executes every move.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr + 1, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr + 2, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr + 4, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr + 8, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31 -> rows 2, 3
+  return v;
+}
+
+// Exclusive prefix sum of one value per thread over a block of THREADS
+// threads (a multiple of 64), in thread order; `total` gets the block's sum.
+// tmp: LDS for THREADS / 64 ints.  Contains two block barriers.
+template <int THREADS>
+__device__ __forceinline__ int block_excl_scan(int v, int* tmp, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) tmp[w] = incl;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < THREADS / 64; ++i) {
+    const int s = tmp[i];
+    before += i < w ? s : 0;
+    tot += s;
+  }
+  __syncthreads();
+  total = tot;
+  return before + incl - v;
+}
+
 // Exclusive prefix sum over the cluster (lane c gets the sum of lanes < c).
 template <int W>
 __device__ __forceinline__ int cl_excl_scan(int v, int lane_c) {

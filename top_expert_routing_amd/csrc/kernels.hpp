@@ -31,10 +31,18 @@ LaunchStamp& launch_stamp();
 constexpr int kTokensPerBlock = 64;   // tokens per route/scatter block (one u64 bitmask)
 
 // Per-expert counting: each route block adds its counts into one of at most
-// kMaxSuperRows rows (blocks [s*G, (s+1)*G) into row s).  Those rows live at
-// the start of the routing workspace, must be zero on entry and are zero again
-// when a call completes: the consumer of the rows clears them.
+// kMaxSuperRows rows (blocks [s*G, (s+1)*G) into row s).  The rows live at the
+// start of the routing workspace in two sets that calls of moe_route_permute
+// use in turn, so that no reader has to find out that it read them last: the
+// scatter blocks of one call clear the set the previous call used.  A header
+// of four words follows the sets:
+//   hdr[0]  the set the next route kernel adds into,
+//   hdr[1]  the set the current call's readers read (written by route block 0),
+//   hdr[2 + s]  how many ints of set s the call that last used it touched.
+// A set is entirely zero whenever a route kernel starts adding into it.
 constexpr int kMaxSuperRows = 64;
+constexpr int kMaxCountExperts = 2048;
+constexpr int kCountSetInts = kMaxSuperRows * kMaxCountExperts;
 
 template <int LPT>
 constexpr int kRouteBlock = (LPT * 64 < 512) ? LPT * 64 : 512;
@@ -55,9 +63,11 @@ struct RouteParams {
   int32_t* ids;           // [T, k]
   void* weights;          // [T, k] f32 or bf16
   float* scores;          // nullable [T, E]
-  int32_t* super_rows;    // nullable: per-expert counting rows (counting on when set)
+  int32_t* super_rows;    // nullable: the two sets of counting rows (counting on when set)
+  uint32_t* count_hdr;    // their header (see kCountSetInts)
   int32_t* hist;          // nullable [nb, loc_n]: per-block counts, for the permutation
   int group_blocks;       // blocks that add into one counting row
+  int num_super;          // counting rows this call uses
   int T, E, k;
   int variant;            // kVar*
   int pre;                // softmax before top-k
@@ -92,10 +102,9 @@ struct ScatterParams {
   int T, k, El, off, tile;
   int tile_shift;         // tile = 1 << tile_shift
   uint32_t k_magic;       // ceil(2^20 / k): (q * k_magic) >> 20 = q / k for q < 4096
-  int32_t* super_rows;    // [num_super, El], cleared by the last block
+  int32_t* super_rows;    // the two sets of counting rows, [num_super, El] used of each
+  uint32_t* count_hdr;    // their header (see kCountSetInts)
   const int32_t* hist;    // [nb, El] per-block counts
-  uint32_t* done;         // block counters ([0] top, [64 * (j + 1)] sub-counter j), reset by
-                          // their last user: 17 * 256 bytes
   int group_blocks, num_super;
   int32_t* counts;        // out [El]
   int32_t* e2p;
@@ -140,8 +149,8 @@ __host__ __device__ inline RouteLds route_lds_layout(int lpt, int rwpl, int epl,
 size_t route_lds_bytes(int lpt, int rwpl, int epl, int hmask_len, int cap, int k, int n_group);
 size_t scatter_lds_bytes(int El);
 hipError_t launch_route(const RouteParams& p, int lpt, int epl, bool bf16, int nb, hipStream_t s);
-hipError_t launch_counts(int32_t* super_rows, int num_super, int El, int32_t* counts,
-                         hipStream_t s);
+hipError_t launch_counts(int32_t* super_rows, const uint32_t* count_hdr, int num_super, int El,
+                         int32_t* counts, hipStream_t s);
 hipError_t launch_scatter(const ScatterParams& p, int nb, hipStream_t s);
 hipError_t launch_empty_outputs(int32_t* counts, int El, int32_t* padded_offsets, int32_t* total,
                                 int32_t* nctas, hipStream_t s);

@@ -314,30 +314,25 @@ __device__ __forceinline__ void emit_selected(const EmitCtx& c, const int* mysel
 // trtllm_gen_routing, Returns: the padded offsets, both index maps and the
 // per-tile expert and row limit): counts are popcounts, the padded offsets a
 // scan, and token t's slot for expert e is offset(e) + the number of lower
-// tokens that chose e (stable by token).  po: LDS for loc_n + 1 ints.
+// tokens that chose e (stable by token).  po: LDS for loc_n + 1 ints and 8
+// more (the scan's wave sums).
 template <int BLOCK>
 __device__ void permute_in_block(const RouteParams& p, const uint64_t* hmask, int* po) {
   const int tid = threadIdx.x;
   const int El = p.loc_n, k = p.k, tile = p.tile;
   __syncthreads();                                      // the bitmask and the ids are complete
-  if (tid < 64) {                                       // exclusive scan of the padded sizes
-    const int n = El + 1;
-    const int per = (n + 63) / 64;
-    const int lo = min(n, tid * per), hi = min(n, lo + per);
-    int sum = 0;
-    for (int e = lo; e < hi; ++e)
-      sum += e < El ? ((__popcll(hmask[e]) + tile - 1) & ~(tile - 1)) : 0;
-    int incl = sum;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int u = __shfl_up(incl, o, 64);
-      if (tid >= o) incl += u;
-    }
-    int run = incl - sum;
-    for (int e = lo; e < hi; ++e) {
-      po[e] = run;
-      run += e < El ? ((__popcll(hmask[e]) + tile - 1) & ~(tile - 1)) : 0;
-    }
+  // exclusive scan of the padded sizes over the block, BLOCK experts a round
+  int* scan_tmp = po + El + 1;                          // BLOCK / 64 ints
+  int carry = 0;
+  for (int e0 = 0; e0 < El; e0 += BLOCK) {             // uniform trip count
+    const int e = e0 + tid;
+    const int v = e < El ? ((__popcll(hmask[e]) + tile - 1) & ~(tile - 1)) : 0;
+    int round_total;
+    const int ex = block_excl_scan<BLOCK>(v, scan_tmp, round_total);
+    if (e < El) po[e] = carry + ex;
+    carry += round_total;
   }
+  if (tid == 0) po[El] = carry;
   __syncthreads();
   // both index maps; every (token, choice) of the call is in this block
   for (int q = tid; q < p.T * k; q += BLOCK) {
@@ -436,6 +431,8 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>)
     }
   }
   const bool counting = p.super_rows != nullptr || p.fused;
+  // the set of counting rows this call adds into (requested early, used last)
+  const uint32_t cset = p.super_rows != nullptr ? p.count_hdr[0] : 0u;
   if (counting)
     for (int e = tid; e < p.loc_n; e += BLOCK) hmask[e] = 0;
   __syncthreads();
@@ -767,7 +764,12 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>)
 
   if (counting && p.super_rows != nullptr) {
     __syncthreads();
-    int32_t* srow = p.super_rows + (size_t)(blk / p.group_blocks) * p.loc_n;
+    int32_t* srow = p.super_rows + (size_t)cset * kCountSetInts +
+                    (size_t)(blk / p.group_blocks) * p.loc_n;
+    if (blk == 0 && tid == 0) {          // for this call's readers
+      p.count_hdr[1] = cset;
+      p.count_hdr[2 + cset] = (uint32_t)(p.num_super * p.loc_n);
+    }
     for (int e = tid; e < p.loc_n; e += BLOCK) {
       const int c = __popcll(hmask[e]);
       if (p.hist != nullptr) p.hist[(size_t)blk * p.loc_n + e] = c;
@@ -782,7 +784,7 @@ hipError_t launch_route_inst(const RouteParams& p, int nb, hipStream_t s) {
   constexpr int BLOCK = kRouteBlock<LPT>;
   const size_t lds = route_lds_bytes(LPT, kRawRow<VAR, BF16> ? RawRow<EPL, BF16>::kWords : EPL,
                                      EPL, p.hmask_len, p.cap, p.k, p.grouped ? p.n_group : 0) +
-                     (p.fused ? (((size_t)p.loc_n + 1) * 4 + 15) & ~(size_t)15 : 0);
+                     (p.fused ? (((size_t)p.loc_n + 1) * 4 + 32 + 15) & ~(size_t)15 : 0);
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&route_kernel<LPT, EPL, BF16, VAR>),

@@ -27,8 +27,9 @@
 //                   group, padded offsets, the stable in-block rank (popcount
 //                   of lower bits of the bitmask), slot = offset + base + rank;
 //                   writes both index maps, the padding, and the per-tile
-//                   expert / row limit.  The last block to finish reading the
-//                   counting rows clears them for the next call.
+//                   expert / row limit.  Calls use two sets of counting rows
+//                   in turn; the scatter blocks clear the set the previous
+//                   call used, so no block has to find out that it was last.
 // (moe_route with counts launches counts_kernel instead of scatter_kernel.)
 // Integer additions commute, so the atomics leave no trace of their order:
 // every output is a pure function of the input and two runs are bit-identical.
@@ -37,11 +38,13 @@
 
 namespace moe {
 
-// Per-expert totals of moe_route: sums the counting rows and clears them.
-__global__ void counts_kernel(int32_t* __restrict__ super_rows, int num_super, int El,
-                              int32_t* __restrict__ counts) {
+// Per-expert totals of moe_route: sums the call's set of counting rows and
+// clears it (each expert's rows are read by one thread only).
+__global__ void counts_kernel(int32_t* __restrict__ super_rows, const uint32_t* count_hdr,
+                              int num_super, int El, int32_t* __restrict__ counts) {
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= El) return;
+  super_rows += (size_t)count_hdr[1] * kCountSetInts;
   int tot = 0;
   for (int r = 0; r < num_super; ++r) {
     int32_t* a = super_rows + (size_t)r * El + e;
@@ -52,16 +55,15 @@ __global__ void counts_kernel(int32_t* __restrict__ super_rows, int num_super, i
 }
 
 // Scatter: one block per 64-token block of the route kernel.
-//   1. expert totals and this block's base ranks from the counting rows (rows
-//      of earlier groups) and the per-block counts of earlier blocks of its
-//      own group; the block that finishes those reads last clears the rows;
+//   1. expert totals and this block's base ranks from the call's set of
+//      counting rows (rows of earlier groups) and the per-block counts of
+//      earlier blocks of its own group; the blocks clear the other set, which
+//      the previous call used, for the next call;
 //   2. padded offsets (a scan over the experts), the block's token bitmask per
 //      expert, slot = offset + base + popcount of the lower token bits;
-//   3. the tiles of the experts [b*El/nb, (b+1)*El/nb): expert, row limit and
-//      the -1 padding of each segment's last tile.
+//   3. the tiles of the experts b, b + nb, b + 2 nb, ...: expert, row limit
+//      and the -1 padding of each segment's last tile.
 constexpr int kScatterThreads = 256;
-constexpr int kDoneLanes = 16;          // sub-counters of the block count
-constexpr int kDoneStride = 64;         // 256 bytes apart: separate cache lines
 
 // NP = (token, choice) pairs per thread: 64 k / kScatterThreads rounded up to
 // a power of two (k <= 4, 8, 16, 32, 64).  The ids are loaded unconditionally
@@ -72,7 +74,6 @@ constexpr int kDoneStride = 64;         // 256 bytes apart: separate cache lines
 template <int NP, int S>
 __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int last_block;
   const int El = p.El;
   uint64_t* msk = reinterpret_cast<uint64_t*>(smem);
   int* po = reinterpret_cast<int*>(msk + El);           // El + 1
@@ -99,6 +100,9 @@ __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams 
     idv[i] = tid + i * kScatterThreads < valid_pairs ? idv[i] - p.off : -1;
   const int grp = blk / p.group_blocks;
   const int g0 = grp * p.group_blocks;
+  const uint32_t cset = p.count_hdr[1];                  // the set this call's route kernel used
+  const int32_t* srows = p.super_rows + (size_t)cset * kCountSetInts;
+  const int prev_ext = (int)p.count_hdr[2 + (1u - cset)];   // ints the previous user of the other touched
   if constexpr (S == 1) {
     for (int e = tid; e < El; e += kScatterThreads) {
       int tot = 0, pre = 0;
@@ -107,7 +111,7 @@ __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams 
         int sv[16], hv[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          sv[i] = r0 + i < p.num_super ? p.super_rows[(size_t)(r0 + i) * El + e] : 0;
+          sv[i] = r0 + i < p.num_super ? srows[(size_t)(r0 + i) * El + e] : 0;
           hv[i] = g0 + r0 + i < blk ? p.hist[(size_t)(g0 + r0 + i) * El + e] : 0;
         }
 #pragma unroll
@@ -134,7 +138,7 @@ __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams 
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int r = r0 + 2 * i;
-          sv[i] = r < p.num_super ? p.super_rows[(size_t)r * El + e] : 0;
+          sv[i] = r < p.num_super ? srows[(size_t)r * El + e] : 0;
           hv[i] = g0 + r < blk ? p.hist[(size_t)(g0 + r) * El + e] : 0;
         }
 #pragma unroll
@@ -161,42 +165,34 @@ __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams 
   }
   if (tid == 0) po[El] = 0;
   __syncthreads();
-  // Every thread's counting-row reads have returned (their sums are in LDS):
-  // count this block, on one of kDoneLanes sub-counters (blocks b = j mod
-  // kDoneLanes) so that no address takes more than nb / kDoneLanes atomics;
-  // the last block of each sub-counter then counts on the top counter.  The
-  // return value is awaited only at the end, so that its latency overlaps the
-  // rest of the block's work.
-  const int dj = blk % kDoneLanes;
-  const unsigned dn = (unsigned)((nb - dj + kDoneLanes - 1) / kDoneLanes);   // blocks of sub-counter dj
-  unsigned done_before = 0u;
-  if (tid == kScatterThreads - 64) done_before = atomicAdd(p.done + (dj + 1) * kDoneStride, 1u);
-
-  // wave 0: exclusive scan of the padded sizes; everyone: token bitmasks
-  if (tid < 64) {
-    const int n = El + 1;
-    const int per = (n + 63) / 64;
-    const int lo = min(n, tid * per), hi = min(n, lo + per);
-    int sum = 0;
-    for (int i = lo; i < hi; ++i) sum += po[i];
-    int incl = sum;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int u = __shfl_up(incl, o, 64);
-      if (tid >= o) incl += u;
-    }
-    int run = incl - sum;
-    for (int i = lo; i < hi; ++i) {
-      const int v = po[i];
-      po[i] = run;
-      run += v;
-    }
+  // The other set was used by the previous call and fully read by its
+  // scatter: clear it (strided over the blocks) for the next call, which adds
+  // into it.
+  {
+    int32_t* other = p.super_rows + (size_t)(1u - cset) * kCountSetInts;
+    for (int i = blk * kScatterThreads + tid; i < prev_ext; i += nb * kScatterThreads) other[i] = 0;
+    if (blk == 0 && tid == 0) p.count_hdr[0] = 1u - cset;
   }
+
+  // token bitmasks (LDS atomics), then the exclusive scan of the padded sizes
+  // over the block, 256 experts per round (wavefront scans in DPP moves)
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     const int q = tid + i * kScatterThreads;
     const int el = idv[i];
     if (el >= 0 && el < El) atomicOr(&msk[el], 1ull << ((q * p.k_magic) >> 20));
   }
+  int* scan_tmp = cnt + El;                              // kScatterThreads / 64 ints
+  int carry = 0;
+  for (int e0 = 0; e0 < El; e0 += kScatterThreads) {   // uniform trip count
+    const int e = e0 + tid;
+    const int v = e < El ? po[e] : 0;
+    int round_total;
+    const int ex = block_excl_scan<kScatterThreads>(v, scan_tmp, round_total);
+    if (e < El) po[e] = carry + ex;
+    carry += round_total;
+  }
+  if (tid == 0) po[El] = carry;
   __syncthreads();
   const int total = po[El];
 
@@ -215,10 +211,8 @@ __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams 
     p.e2p[(size_t)t0 * k + q] = slot;
   }
 
-  // tiles of this block's experts
-  const int e_lo = (int)((int64_t)blk * El / nb);
-  const int e_hi = (int)((int64_t)(blk + 1) * El / nb);
-  for (int e = e_lo; e < e_hi; ++e) {
+  // tiles of this block's experts: b, b + nb, b + 2 nb, ... (no division)
+  for (int e = blk; e < El; e += nb) {
     const int seg = po[e];
     const int seg_end = seg + cnt[e];
     const int ntile = (po[e + 1] - seg) >> p.tile_shift;
@@ -239,20 +233,6 @@ __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams 
       *p.nctas_out = total >> p.tile_shift;
     }
   }
-  // the last block to finish reading the counting rows clears them
-  if (tid == kScatterThreads - 64) {
-    bool last = false;
-    if (done_before == dn - 1u) {                  // last of its sub-counter
-      p.done[(dj + 1) * kDoneStride] = 0u;         // nobody else touches it in this call
-      const unsigned nsub = (unsigned)min(nb, kDoneLanes);
-      last = atomicAdd(p.done, 1u) == nsub - 1u;
-      if (last) p.done[0] = 0u;
-    }
-    last_block = last;
-  }
-  __syncthreads();
-  if (last_block)
-    for (int i = tid; i < p.num_super * El; i += kScatterThreads) p.super_rows[i] = 0;
 }
 
 // T = 0: the bookkeeping outputs still hold their defined values.
@@ -312,15 +292,17 @@ hipError_t launch_route(const RouteParams& p, int lpt, int epl, bool bf16, int n
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_counts(int32_t* super_rows, int num_super, int El, int32_t* counts,
-                         hipStream_t s) {
-  MOE_LAUNCH(counts_kernel, dim3((El + 255) / 256), dim3(256), 0, s, super_rows, num_super, El,
-             counts);
+hipError_t launch_counts(int32_t* super_rows, const uint32_t* count_hdr, int num_super, int El,
+                         int32_t* counts, hipStream_t s) {
+  MOE_LAUNCH(counts_kernel, dim3((El + 255) / 256), dim3(256), 0, s, super_rows, count_hdr,
+             num_super, El, counts);
   return hipGetLastError();
 }
 
 // msk (El u64), po (El + 1), base, cnt (El each), and the split partials (2 El)
-size_t scatter_lds_bytes(int El) { return (size_t)El * 8 + (size_t)(El + 1) * 4 + (size_t)El * 16; }
+size_t scatter_lds_bytes(int El) {
+  return (size_t)El * 8 + (size_t)(El + 1) * 4 + (size_t)El * 16 + 16;   // + the scan's wave sums
+}
 
 template <int S>
 static void launch_scatter_s(const ScatterParams& p, int nb, hipStream_t s) {
