@@ -236,6 +236,19 @@ int32_t* ws_hist(void* ws) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Compute units of the current device (cached per device; 0 if unknown).
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 moe::RouteParams make_params(const moe_route_args& a, const Shape& sh, const void* logits,
                              const void* bias, int32_t* ids, void* weights, float* scores,
                              int32_t* super_rows, uint32_t* count_hdr, int32_t* hist,
@@ -277,12 +290,19 @@ moe::RouteParams make_params(const moe_route_args& a, const Shape& sh, const voi
   p.loc_n = loc_n;
   p.hmask_len = super_rows != nullptr ? (loc_n + 1) & ~1 : 0;
   p.cap = a.top_k <= 32 ? 32 : 64;
+  // sigmoid of bfloat16 logits with more blocks than one round on the device:
+  // raw logits in the LDS row (half its size; two blocks fit a CU, so one
+  // block's logit loads overlap the other's work)
+  const int cus = device_cu_count();
+  p.sig_raw = a.score_fn == MOE_SIGMOID && a.logits_dtype == MOE_BF16 && cus > 0 &&
+              num_blocks(a.num_tokens) > cus;
   return p;
 }
 
 moe_status launch_route_checked(const moe::RouteParams& p, const Shape& sh, bool bf16,
                                 hipStream_t stream) {
-  const int rwpl = (p.variant == moe::kVarSoftmax && bf16) ? sh.epl / 2 : sh.epl;
+  const int rwpl =
+      ((p.variant == moe::kVarSoftmax || p.sig_raw) && bf16) ? sh.epl / 2 : sh.epl;
   const size_t lds = moe::route_lds_bytes(sh.lpt, rwpl, sh.epl, p.hmask_len, p.cap, p.k,
                                           p.grouped ? p.n_group : 0) +
                      (p.fused ? (((size_t)p.loc_n + 1) * 4 + 32 + 15) & ~(size_t)15 : 0);

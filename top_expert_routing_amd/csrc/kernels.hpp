@@ -82,6 +82,7 @@ struct RouteParams {
   int loc_off, loc_n;
   int hmask_len;          // LDS u64 words for the block bitmask (even)
   int cap;                // candidate list capacity per token (>= k)
+  int sig_raw;            // sigmoid, bfloat16 logits: keep the raw logits in the LDS row
   // A call whose tokens fit one block (T <= 64) finishes the permutation in
   // the route kernel itself, from the block's LDS bitmask (no counting rows,
   // no scatter launch): set `fused` and these outputs.

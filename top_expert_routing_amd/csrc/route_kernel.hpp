@@ -88,15 +88,26 @@ __device__ __forceinline__ void decode_raw(const RawRow<EPL, BF16>& r, float (&x
 
 // The cluster's row in LDS, dynamically indexable: for the softmax variant the
 // raw logit words (two bf16 or one float32 per word; the logit is the score
-// basis there), otherwise the float32 score basis of every expert.
+// basis there), otherwise the float32 score basis of every expert -- except
+// that the sigmoid variant with bfloat16 logits may keep the raw words too
+// (`sig_raw`, half the LDS: a grid of several rounds of blocks then fits two
+// blocks per CU) and recompute the sigmoid of the few experts it reads back.
 template <int VAR, bool BF16>
 constexpr bool kRawRow = VAR == kVarSoftmax;
+template <int VAR, bool BF16>
+constexpr bool kSigRawOk = VAR == kVarSigmoid && BF16;
 
 template <int VAR, bool BF16>
-__device__ __forceinline__ float row_basis(const uint32_t* rowc, int e) {
+__device__ __forceinline__ float row_basis(const uint32_t* rowc, int e, bool sig_raw) {
   if constexpr (kRawRow<VAR, BF16> && BF16) {
     const uint32_t w = rowc[e >> 1];
     return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+  } else if constexpr (kSigRawOk<VAR, BF16>) {
+    if (sig_raw) {
+      const uint32_t w = rowc[e >> 1];
+      return sigmoid_f32((e & 1) ? bf16_hi(w) : bf16_lo(w));      // sigmoid(-inf) = 0
+    }
+    return __uint_as_float(rowc[e]);
   } else {
     return __uint_as_float(rowc[e]);
   }
@@ -171,6 +182,7 @@ struct EmitCtx {
   int32_t* ids;
   void* weights;
   bool weights_bf16, renorm, counting, pre;
+  bool sig_raw;           // the row holds raw bfloat16 logits of the sigmoid variant
   int mode, k, loc_off, loc_n;
   float scale;
   uint64_t* hmask;
@@ -189,7 +201,7 @@ __device__ __forceinline__ void emit_selected(const EmitCtx& c, const int* mysel
   if (k <= LPT) {                             // one rank per lane
     const bool v = c.lane_c < k;
     const int e = v ? myselidx[c.lane_c] : 0;
-    const float r = row_basis<VAR, BF16>(rowc, e);
+    const float r = row_basis<VAR, BF16>(rowc, e, c.sig_raw);
     float ref = 0.0f;
     if (c.mode == kEmitSoftSel) ref = cl_max<LPT>(v ? r : -kInf);
     float inv_den = c.inv_s;
@@ -225,7 +237,7 @@ __device__ __forceinline__ void emit_selected(const EmitCtx& c, const int* mysel
     }
 #pragma unroll
     for (int q = 0; q < KQ; ++q)
-      r[q] = row_basis<VAR, BF16>(rowc, e[q]);
+      r[q] = row_basis<VAR, BF16>(rowc, e[q], c.sig_raw);
     float ref = 0.0f;
     if (c.mode == kEmitSoftSel) {
       float mx = -kInf;
@@ -271,14 +283,14 @@ __device__ __forceinline__ void emit_selected(const EmitCtx& c, const int* mysel
   if (c.mode == kEmitSoftSel) {
     float mx = -kInf;
     for (int n = c.lane_c; n < k; n += LPT)
-      mx = fmaxf(mx, row_basis<VAR, BF16>(rowc, myselidx[n]));
+      mx = fmaxf(mx, row_basis<VAR, BF16>(rowc, myselidx[n], c.sig_raw));
     ref = cl_max<LPT>(mx);
   }
   float inv_den = c.inv_s;
   if (c.mode != kEmitExactPre) {
     float part = 0.0f;
     for (int n = c.lane_c; n < k; n += LPT) {
-      const float r = row_basis<VAR, BF16>(rowc, myselidx[n]);
+      const float r = row_basis<VAR, BF16>(rowc, myselidx[n], c.sig_raw);
       part += c.mode == kEmitPlain ? r : exp_f32(r - ref);
     }
     inv_den = fast_rcp(cl_sum<LPT>(part));
@@ -287,7 +299,7 @@ __device__ __forceinline__ void emit_selected(const EmitCtx& c, const int* mysel
   const float sub = c.mode == kEmitExactPre ? c.m : ref;
   for (int n = c.lane_c; n < k; n += LPT) {
     const int e = myselidx[n];
-    const float r = row_basis<VAR, BF16>(rowc, e);
+    const float r = row_basis<VAR, BF16>(rowc, e, c.sig_raw);
     float w;
     if (c.mode == kEmitPlain)
       w = c.renorm ? r * inv_den : r;
@@ -376,7 +388,8 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>)
   constexpr int EP = LPT * EPL;             // padded row length
   constexpr int WPL = RawRow<EPL, BF16>::kWords;
   constexpr bool kRaw = kRawRow<VAR, BF16>;
-  constexpr int RWPL = kRaw ? WPL : EPL;     // row words per lane
+  const bool sig_raw = kSigRawOk<VAR, BF16> && p.sig_raw != 0;
+  const int RWPL = (kRaw || sig_raw) ? WPL : EPL;   // row words per lane
   static_assert(TPC * NCL == kTokensPerBlock, "block shape");
   static_assert(EPL <= 32, "lane masks are 32-bit");
   constexpr bool kBias = VAR != kVarSoftmax;   // the softmax variant has no bias
@@ -462,7 +475,7 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>)
     const int tl = it * NCL + cl;               // token within the block
     const int t = blk * kTokensPerBlock + tl;
     const bool tv = t < p.T;
-    if constexpr (kRaw) {                      // the raw row, dynamically indexable
+    if (kRaw || sig_raw) {                     // the raw row, dynamically indexable
       if constexpr (WPL % 4 == 0) {
 #pragma unroll
         for (int v = 0; v < WPL; v += 4)
@@ -509,7 +522,7 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>)
         }
       }
     }
-    if constexpr (!kRaw) {                     // the score basis, dynamically indexable
+    if (!(kRaw || sig_raw)) {                  // the score basis, dynamically indexable
 #pragma unroll
       for (int i = 0; i < EPL; i += 4)
         *reinterpret_cast<f32x4*>(myrow + i) = f32x4{x[i], x[i + 1], x[i + 2], x[i + 3]};
@@ -625,25 +638,33 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>)
     int C = cl_sum_i<LPT>(pc);
 
     if (C <= p.cap) {
-      // compact the candidates, two set bits per round; the key is formed
-      // again from the raw logit (bit-identical to the register copy)
+      // compact the candidates, up to four set bits per round; the key is
+      // formed again from the row (bit-identical to the register copy).  All
+      // of a round's LDS reads are issued before its writes, and a round's
+      // missing candidates write to the cluster's spare slot p.cap + 1 (never
+      // ranked: the tier is at most the capacity) instead of branching, which
+      // would put each read behind the previous write.
       uint32_t mm = cmask;
       int pos = coff;
-      while (mm) {                              // two set bits per round, reads batched
-        const int i0 = __builtin_ctz(mm);
-        mm &= mm - 1u;
-        const bool h1 = mm != 0u;
-        const int i1 = h1 ? __builtin_ctz(mm) : i0;
-        mm &= h1 ? mm - 1u : mm;
-        float k0 = row_basis<VAR, BF16>(rowc, e0 + i0);
-        float k1 = row_basis<VAR, BF16>(rowc, e0 + i1);
-        if constexpr (kBias) {
-          k0 += bias_s[e0 + i0];
-          k1 += bias_s[e0 + i1];
+      const int spare = p.cap + 1;
+      while (mm) {
+        int ii[4];
+        bool hv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          hv[q] = mm != 0u;
+          ii[q] = hv[q] ? __builtin_ctz(mm) : 0;
+          mm &= hv[q] ? mm - 1u : mm;
         }
-        mycand[pos] = pack_key(k0, e0 + i0);
-        if (h1) mycand[pos + 1] = pack_key(k1, e0 + i1);
-        pos += h1 ? 2 : 1;
+        float kk[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          kk[q] = row_basis<VAR, BF16>(rowc, e0 + ii[q], sig_raw);
+          if constexpr (kBias) kk[q] += bias_s[e0 + ii[q]];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) mycand[hv[q] ? pos + q : spare] = pack_key(kk[q], e0 + ii[q]);
+        pos += (int)hv[0] + (int)hv[1] + (int)hv[2] + (int)hv[3];
       }
     } else {
       // many keys tie at tau: k rounds of a cluster-wide maximum instead
@@ -695,6 +716,7 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>)
       ec.ids = p.ids;
       ec.weights = p.weights;
       ec.weights_bf16 = p.weights_bf16 != 0;
+      ec.sig_raw = sig_raw;
       ec.renorm = p.renorm != 0;
       ec.counting = counting;
       ec.pre = pre;
@@ -782,7 +804,8 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>)
 template <int LPT, int EPL, bool BF16, int VAR>
 hipError_t launch_route_inst(const RouteParams& p, int nb, hipStream_t s) {
   constexpr int BLOCK = kRouteBlock<LPT>;
-  const size_t lds = route_lds_bytes(LPT, kRawRow<VAR, BF16> ? RawRow<EPL, BF16>::kWords : EPL,
+  const bool raw_row = kRawRow<VAR, BF16> || (kSigRawOk<VAR, BF16> && p.sig_raw != 0);
+  const size_t lds = route_lds_bytes(LPT, raw_row ? RawRow<EPL, BF16>::kWords : EPL,
                                      EPL, p.hmask_len, p.cap, p.k, p.grouped ? p.n_group : 0) +
                      (p.fused ? (((size_t)p.loc_n + 1) * 4 + 32 + 15) & ~(size_t)15 : 0);
   if (lds > 64 * 1024) {
