@@ -173,7 +173,7 @@ def other_configs(mr, torch, np, dev, rotate_mb, K, cpu_seconds=None):
             probs = [o.scores for _, o in sets]
             counts = o0.expert_counts
             loss = torch.empty(1, dtype=torch.float32, device=dev)
-            wsa = torch.empty(max(mr.moe_aux_loss_workspace_size(w.T, w.E), 1), dtype=torch.uint8,
+            wsa = torch.zeros(max(mr.moe_aux_loss_workspace_size(w.T, w.E), 1), dtype=torch.uint8,
                               device=dev)
             grads = [torch.empty((w.T, w.E), dtype=torch.float32, device=dev) for _ in range(R)]
             fwd = graph_ms(torch, lambda i: mr.moe_aux_loss(probs[i % R], counts, w.T, w.T, w.E, w.k,

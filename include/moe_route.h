@@ -21,12 +21,13 @@
  *   caller.  The library never allocates, frees, synchronises, or copies device
  *   memory to the host.  Scratch memory comes from the caller's `workspace`
  *   (device memory, 256-byte aligned, at least the size the matching
- *   *_workspace_size() helper returns).  For moe_aux_loss its contents on
- *   entry are ignored.  The ROUTING workspace (moe_route with expert_counts,
- *   moe_route_permute) starts with a counting region (the first
- *   moe_route_count_region_bytes() bytes), and the FRONT-END workspace
+ *   *_workspace_size() helper returns).  The ROUTING workspace (moe_route
+ *   with expert_counts, moe_route_permute) starts with a counting region (the
+ *   first moe_route_count_region_bytes() bytes), the FRONT-END workspace
  *   (rmsnorm_gate_route) with a synchronisation region (the first
- *   rmsnorm_gate_route_sync_region_bytes() bytes).  That region must be
+ *   rmsnorm_gate_route_sync_region_bytes() bytes), and the AUX-LOSS workspace
+ *   (moe_aux_loss with loss) with one of moe_aux_loss_sync_region_bytes()
+ *   bytes; the rest of every workspace is ignored on entry.  That region must be
  *   zero-filled before the workspace's first use; every call leaves it
  *   zero-filled again when its work completes, so one workspace serves any
  *   sequence of calls of any sizes on one stream.  After an MOE_EHIP failure
@@ -249,7 +250,17 @@ size_t moe_route_permute_noalloc_max_scratch_bytes(void);
  * grad_loss          nullable [1] float32 device scalar; NULL means 1.
  * grad_probs         nullable out [rows, E] float32: runs the backward.
  * At least one of loss / grad_probs must be given.
- * workspace          >= moe_aux_loss_workspace_size(rows, E) bytes. */
+ * workspace          >= moe_aux_loss_workspace_size(rows, E) bytes, used by the
+ *                    forward only (NULL is fine for a backward-only call); its
+ *                    first moe_aux_loss_sync_region_bytes() bytes (the whole
+ *                    of it) are zero on entry and again when the call's work
+ *                    completes (see the conventions above).
+ * The forward is one launch and deterministic: the same inputs give the same
+ * bits on every call.  Its blocks hand their partial sums to the last block
+ * through the workspace; that block's wait is bounded, and one that runs out
+ * (no block that was dispatched before it finished within seconds: not seen
+ * in practice) writes *loss as the float32 NaN with bits 0x7FC0A0A0 and leaves
+ * the workspace dirty: zero it again before the next forward. */
 moe_status moe_aux_loss(const float* probs, const int32_t* tokens_per_expert, int64_t rows,
                         int64_t total_num_tokens, int32_t num_experts, int32_t top_k,
                         float coeff, float* loss, const float* grad_loss, float* grad_probs,
@@ -366,13 +377,15 @@ moe_status rmsnorm_gate_route(const void* hidden, const void* gamma, const void*
 /* Workspace sizes in bytes (0 = none needed).  Pure host functions.
  * moe_route_workspace_size() covers both routing entry points; its first
  * moe_route_count_region_bytes() bytes are the counting region described in
- * the conventions above, and rmsnorm_gate_route_sync_region_bytes() is the
- * front end's synchronisation region (both constants, independent of the
- * sizes). */
+ * the conventions above; rmsnorm_gate_route_sync_region_bytes() and
+ * moe_aux_loss_sync_region_bytes() are the synchronisation regions of the
+ * front end and of the aux-loss forward (all three constants, independent of
+ * the sizes). */
 size_t moe_route_workspace_size(const moe_route_args* args, int32_t tile_tokens_dim,
                                 int32_t local_num_experts);
 size_t moe_route_count_region_bytes(void);
 size_t moe_aux_loss_workspace_size(int64_t rows, int32_t num_experts);
+size_t moe_aux_loss_sync_region_bytes(void);
 size_t rmsnorm_gate_route_workspace_size(int32_t T, int32_t H, int32_t E);
 size_t rmsnorm_gate_route_sync_region_bytes(void);
 

@@ -133,7 +133,11 @@ def test_size_helpers():
     assert mr.moe_route_workspace_size(args, 8, 256) == region + 256 * 256 * 4
     assert mr.moe_route_workspace_size(mr.make_route_args(1, 8, 2), 8, 8) == region + 256
     assert mr.moe_route_workspace_size(args, 8, 256) % 256 == 0
-    assert mr.moe_aux_loss_workspace_size(65536, 128) > 0
+    # the aux forward's workspace is one sync region: a 64-bit partial slot for
+    # each of at most 2048 blocks, whatever the sizes
+    assert mr.moe_aux_loss_sync_region_bytes() == 2048 * 8
+    for rows, E in ((65536, 128), (0, 8), (10 ** 7, 128), (1, 2048)):
+        assert mr.moe_aux_loss_workspace_size(rows, E) == 2048 * 8
 
 
 def test_status_strings():

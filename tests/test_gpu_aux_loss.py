@@ -103,3 +103,29 @@ def test_aux_empty_rows():
     log("[gpu] aux rows=0")
     loss, _ = _run(np.zeros((0, E), np.float32), counts, 100, E, k, 0.1, bwd=False)
     assert loss == 0.0
+
+
+def test_aux_workspace_reuse_and_determinism():
+    # one workspace for forwards of decreasing and increasing sizes: the sync
+    # region is zero after every call, and repeating a call gives the same bits
+    sync = mr.moe_aux_loss_sync_region_bytes()
+    E, k = 128, 8
+    big = 400000
+    ws = torch.zeros(mr.moe_aux_loss_workspace_size(big, E), dtype=torch.uint8, device=DEV)
+    rng = np.random.default_rng(4242)
+    for rows in (big, 1000, 1, 70001, 0, big):
+        log(f"[gpu] aux reuse rows={rows}")
+        probs = rng.random((rows, E), dtype=np.float32)
+        counts = rng.integers(0, 5000, E).astype(np.int32)
+        p = torch.from_numpy(probs).to(DEV)
+        c = torch.from_numpy(counts).to(DEV)
+        outs = []
+        for _ in range(3):
+            loss = torch.full((1,), np.nan, dtype=torch.float32, device=DEV)
+            mr.moe_aux_loss(p, c, rows, max(rows, 1), E, k, 1e-2, loss=loss, workspace=ws)
+            torch.cuda.synchronize()
+            assert int(ws[:sync].count_nonzero()) == 0, rows
+            outs.append(loss.item())
+        assert outs[0] == outs[1] == outs[2], (rows, outs)
+        ref = oracle.aux_loss_fwd(probs, counts, max(rows, 1), E, k, 1e-2)
+        assert abs(outs[0] - ref) <= RTOL * abs(ref), (rows, outs[0], ref)

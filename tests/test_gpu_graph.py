@@ -108,6 +108,7 @@ def test_aux_loss_graph_replays():
         torch.cuda.synchronize()
         assert torch.equal(loss, loss_ref), rep
         assert torch.equal(grad, grad_ref), rep
+        assert int(ws[:mr.moe_aux_loss_sync_region_bytes()].count_nonzero()) == 0, rep
         # eager work between replays: the same op on other data, sharing nothing
         other = torch.empty_like(loss_ref)
         ws2 = torch.zeros_like(ws)

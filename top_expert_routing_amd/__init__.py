@@ -29,7 +29,7 @@ __all__ = [
     "moe_route", "moe_route_permute", "moe_aux_loss", "rmsnorm_gate_route", "moe_route_backward",
     "moe_dispatch", "moe_combine", "moe_topk_to_dense",
     "moe_route_workspace_size", "moe_route_count_region_bytes", "moe_aux_loss_workspace_size",
-    "moe_profile_begin", "moe_profile_end", "moe_profile_read",
+    "moe_aux_loss_sync_region_bytes", "moe_profile_begin", "moe_profile_end", "moe_profile_read",
     "rmsnorm_gate_route_workspace_size", "rmsnorm_gate_route_sync_region_bytes",
     "rmsnorm_gate_route_sum_depth",
     "moe_max_padded_tokens", "moe_max_tiles",
@@ -186,6 +186,10 @@ def moe_route_count_region_bytes() -> int:
 
 def moe_aux_loss_workspace_size(rows: int, num_experts: int) -> int:
     return int(_lib.lib.moe_aux_loss_workspace_size(ctypes.c_int64(rows), num_experts))
+
+
+def moe_aux_loss_sync_region_bytes() -> int:
+    return int(_lib.lib.moe_aux_loss_sync_region_bytes())
 
 
 def rmsnorm_gate_route_workspace_size(T: int, H: int, E: int) -> int:

@@ -24,6 +24,7 @@ EXPORTED = [
     "moe_route_permute_noalloc_max_scratch_bytes", "moe_aux_loss", "rmsnorm_gate_route", "moe_route_backward",
     "moe_dispatch", "moe_combine", "moe_topk_to_dense",
     "moe_route_workspace_size", "moe_route_count_region_bytes", "moe_aux_loss_workspace_size",
+    "moe_aux_loss_sync_region_bytes",
     "rmsnorm_gate_route_workspace_size", "rmsnorm_gate_route_sync_region_bytes",
     "rmsnorm_gate_route_sum_depth",
     "moe_max_padded_tokens", "moe_max_tiles",
@@ -114,6 +115,8 @@ def _load():
     lib.moe_route_count_region_bytes.restype = sz
     lib.moe_aux_loss_workspace_size.argtypes = [i64, i32]
     lib.moe_aux_loss_workspace_size.restype = sz
+    lib.moe_aux_loss_sync_region_bytes.argtypes = []
+    lib.moe_aux_loss_sync_region_bytes.restype = sz
     lib.rmsnorm_gate_route_workspace_size.argtypes = [i32, i32, i32]
     lib.rmsnorm_gate_route_workspace_size.restype = sz
     lib.rmsnorm_gate_route_sync_region_bytes.argtypes = []

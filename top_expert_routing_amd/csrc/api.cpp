@@ -646,8 +646,10 @@ size_t moe_route_permute_noalloc_max_scratch_bytes(void) { return kScratchBytes;
 
 size_t moe_aux_loss_workspace_size(int64_t rows, int32_t num_experts) {
   if (rows < 0 || num_experts < 1) return 0;
-  return align256((size_t)moe::aux_fwd_blocks(rows, num_experts) * sizeof(double));
+  return moe::kAuxSyncBytes;
 }
+
+size_t moe_aux_loss_sync_region_bytes(void) { return moe::kAuxSyncBytes; }
 
 moe_status moe_aux_loss(const float* probs, const int32_t* tokens_per_expert, int64_t rows,
                         int64_t total_num_tokens, int32_t E, int32_t top_k, float coeff,
@@ -675,9 +677,9 @@ moe_status moe_aux_loss(const float* probs, const int32_t* tokens_per_expert, in
   if (loss != nullptr) {
     const int nb = moe::aux_fwd_blocks(rows, E);
     hipError_t e = launch_with_profile(MOE_KERNEL_AUX_FWD, stream, [&] {
-      return moe::launch_aux_fwd(probs, tokens_per_expert, rows, E, scale,
-                                 static_cast<double*>(workspace), nb, loss, stream);
-    }, /*single_kernel=*/false);
+      return moe::launch_aux_fwd(probs, tokens_per_expert, rows, E, scale, workspace, nb, loss,
+                                 stream);
+    });
     if (e != hipSuccess) return hip_fail(e, "aux forward launch");
   }
   if (grad_probs != nullptr && rows > 0) {

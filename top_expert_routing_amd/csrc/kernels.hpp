@@ -204,9 +204,16 @@ int front_end_kchunk(int H);
 size_t front_end_workspace_bytes(int T, int H, int E);
 hipError_t launch_front_end(const FrontEndParams& q, hipStream_t s);
 
+// The aux-loss forward's workspace is one synchronisation region of this many
+// bytes (a 64-bit partial slot per block, at most kAuxMaxBlocks blocks): zero
+// before the first call, zero again after every call.  A forward whose summing
+// block gave up waiting writes the loss as the float32 NaN kAuxTimeoutNaN.
+constexpr int kAuxMaxBlocks = 2048;
+constexpr int kAuxSyncBytes = kAuxMaxBlocks * 8;
+constexpr uint32_t kAuxTimeoutNaN = 0x7fc0a0a0u;
 int aux_fwd_blocks(int64_t rows, int E);
 hipError_t launch_aux_fwd(const float* probs, const int32_t* counts, int64_t rows, int E,
-                          double scale, double* partial, int nb, float* loss, hipStream_t s);
+                          double scale, void* sync, int nb, float* loss, hipStream_t s);
 hipError_t launch_aux_bwd(const int32_t* counts, int64_t rows, int E, double scale,
                           const float* grad_loss, float* grad, hipStream_t s);
 
