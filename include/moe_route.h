@@ -29,9 +29,13 @@
  *   (moe_aux_loss with loss) with one of moe_aux_loss_sync_region_bytes()
  *   bytes; the rest of every workspace is ignored on entry.  That region must be
  *   zero-filled before the workspace's first use; every call leaves it
- *   zero-filled again when its work completes, so one workspace serves any
+ *   zero-filled again when its work completes (apart from the front end's
+ *   failure count, see rmsnorm_gate_route), so one workspace serves any
  *   sequence of calls of any sizes on one stream.  After an MOE_EHIP failure
- *   mid-call, zero it again.  All arrays are dense and row-major.
+ *   mid-call, zero it again.  A region that is not clean never moves an access
+ *   outside the workspace and the caller's arrays; what it does to the results
+ *   is stated at each entry point (routing: see moe_route_permute).  All
+ *   arrays are dense and row-major.
  * Streams: all work is enqueued on `stream` (0 = the null stream); outputs are
  *   valid once that work completes.  Calls on different streams that share a
  *   workspace race.  Calls are otherwise re-entrant and thread-safe.
@@ -193,7 +197,21 @@ moe_status moe_route(const moe_route_args* args, const void* logits, const void*
  *                     tile's valid rows in permuted space,
  *                     min((c + 1) * tile, segment start + count).
  * workspace           >= moe_route_workspace_size(args, tile, E_loc) bytes.
- * The other arguments are as for moe_route (scores nullable). */
+ * The other arguments are as for moe_route (scores nullable).
+ *
+ * A counting region that is not clean on entry (never zeroed, or left by an
+ * MOE_EHIP mid-call) leaves topk_ids / topk_weights / scores exact and moves
+ * no write outside the output arrays.  The bookkeeping detects it when the
+ * region's header is out of range, a count falls outside [0, T k] or the
+ * padded offsets overflow: then total_num_padded_tokens,
+ * num_non_exiting_ctas and every expert_counts entry are -1, the other
+ * bookkeeping outputs are not valid, and the region is clean again for the
+ * next call.  Garbage that looks like counts (small non-negative values
+ * under a valid header) goes undetected: the bookkeeping of a call whose
+ * counting rows hold it is off by it (still in bounds), and the call after
+ * that call clears those rows.  moe_route with
+ * expert_counts reports a detected dirty region as -1 in every count (a
+ * count outside [0, T k] as -1 in that count) and leaves the region clean. */
 moe_status moe_route_permute(const moe_route_args* args, int32_t tile_tokens_dim,
                              int32_t local_expert_offset, int32_t local_num_experts,
                              const void* logits, const void* bias, int32_t* topk_ids,
@@ -260,7 +278,9 @@ size_t moe_route_permute_noalloc_max_scratch_bytes(void);
  * through the workspace; that block's wait is bounded, and one that runs out
  * (no block that was dispatched before it finished within seconds: not seen
  * in practice) writes *loss as the float32 NaN with bits 0x7FC0A0A0 and leaves
- * the workspace dirty: zero it again before the next forward. */
+ * the workspace dirty: zero it again before the next forward.  A dirty slot
+ * (non-zero on entry) is taken for a published partial: the forward that
+ * reads it gives a wrong loss and returns it to zero. */
 moe_status moe_aux_loss(const float* probs, const int32_t* tokens_per_expert, int64_t rows,
                         int64_t total_num_tokens, int32_t num_experts, int32_t top_k,
                         float coeff, float* loss, const float* grad_loss, float* grad_probs,
@@ -294,6 +314,21 @@ moe_status moe_route_backward(const moe_route_args* args, const void* logits,
                               const int32_t* topk_ids, const float* grad_weights,
                               const float* grad_scores, float* grad_logits, hipStream_t stream);
 
+/* Dense form of moe_route's top-k outputs ([TE] I/O Contract: the probs and
+ * routing_map outputs of fused_topk_with_score_function, each [T, E]):
+ *
+ *   probs[t, e]       = topk_weights[t, j] where topk_ids[t, j] == e, else 0
+ *   routing_map[t, e] = 1 where token t chose expert e, else 0
+ *
+ * Values are copied, not recomputed (bf16 weights are widened exactly).
+ * topk_ids [T, k] int32 (ids outside [0, E) are ignored), topk_weights [T, k]
+ * in weights_dtype (MOE_F32 or MOE_BF16); probs: nullable out [T, E] float32;
+ * routing_map: nullable out [T, E] uint8 (bool); at least one is given.
+ * E <= 512, k in [1, 64].  No workspace. */
+moe_status moe_topk_to_dense(int32_t T, int32_t E, int32_t top_k, const int32_t* topk_ids,
+                             const void* topk_weights, int32_t weights_dtype, float* probs,
+                             uint8_t* routing_map, hipStream_t stream);
+
 /* Token dispatch and combine either side of the grouped expert GEMM ([LMD]
  * Description: dispatch sends tokens to expert buffers by the routing
  * decision, combine returns expert outputs to token order with the routing
@@ -319,21 +354,6 @@ moe_status moe_route_backward(const moe_route_args* args, const void* logits,
  *                  permuted_hidden (moe_max_padded_tokens()).
  * No workspace.  Rows move with 16-byte accesses when rows and pointers are
  * 16-byte aligned, element by element otherwise. */
-/* Dense form of moe_route's top-k outputs ([TE] I/O Contract: the probs and
- * routing_map outputs of fused_topk_with_score_function, each [T, E]):
- *
- *   probs[t, e]       = topk_weights[t, j] where topk_ids[t, j] == e, else 0
- *   routing_map[t, e] = 1 where token t chose expert e, else 0
- *
- * Values are copied, not recomputed (bf16 weights are widened exactly).
- * topk_ids [T, k] int32 (ids outside [0, E) are ignored), topk_weights [T, k]
- * in weights_dtype (MOE_F32 or MOE_BF16); probs: nullable out [T, E] float32;
- * routing_map: nullable out [T, E] uint8 (bool); at least one is given.
- * E <= 512, k in [1, 64].  No workspace. */
-moe_status moe_topk_to_dense(int32_t T, int32_t E, int32_t top_k, const int32_t* topk_ids,
-                             const void* topk_weights, int32_t weights_dtype, float* probs,
-                             uint8_t* routing_map, hipStream_t stream);
-
 moe_status moe_dispatch(const void* hidden, int32_t dtype, int32_t T, int32_t H,
                         const int32_t* permuted_idx_to_token_idx,
                         const int32_t* total_num_padded_tokens, int64_t max_padded_tokens,
@@ -366,8 +386,14 @@ moe_status moe_combine(const void* expert_out, int32_t dtype, int32_t T, int32_t
  * wait in-kernel (polling the synchronisation region) for the normalisation
  * scale of their tokens; then the selection.  Should a wait ever exceed its
  * spin limit (it cannot while blocks are dispatched in index order), the call
- * still completes and writes -1 into topk_ids; zero the region again after
- * that. */
+ * still completes, writes -1 into every topk_ids entry and adds one to the
+ * uint32 failure count at byte offset 4 of the workspace, which the library
+ * never clears (read it with a device-to-host copy when -1 ids need an
+ * explanation; a caller may reset it); the region is clean again for the next
+ * call.  A region that was not zero on entry: a dirty failure word is
+ * ignored (each call clears it first); a dirty normalisation-scale slot of a
+ * token t < T gives that call wrong ids and affinities, and the call returns
+ * the slot to zero. */
 moe_status rmsnorm_gate_route(const void* hidden, const void* gamma, const void* router_weights,
                               const void* router_bias, int32_t dtype, int32_t T, int32_t H,
                               int32_t E, float eps, int32_t top_k, int32_t act_fn, void* normed,

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -227,6 +228,19 @@ size_t route_ws_bytes(const moe_route_args& a, int loc_n, bool permute) {
          (permute ? align256((size_t)num_blocks(a.num_tokens) * loc_n * sizeof(int32_t)) : 0);
 }
 int32_t* ws_count_rows(void* ws) { return static_cast<int32_t*>(ws); }
+// Polls before a front-end wait gives up.  MOE_ROUTE_FRONT_END_SPIN_LIMIT (an
+// integer in [0, the default]) lowers it, read on every call: a limit of 0
+// makes every wait give up at once, which exercises the give-up path (-1 ids,
+// the failure count) with every kernel still ending normally.
+int front_end_spin_limit() {
+  const char* v = std::getenv("MOE_ROUTE_FRONT_END_SPIN_LIMIT");
+  if (v == nullptr || *v == '\0') return moe::kFrontEndSpinLimit;
+  char* end = nullptr;
+  const long n = std::strtol(v, &end, 10);
+  if (*end != '\0' || n < 0 || n > moe::kFrontEndSpinLimit) return moe::kFrontEndSpinLimit;
+  return (int)n;
+}
+
 uint32_t* ws_count_hdr(void* ws) {
   return reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + 2 * kCountRowsBytes);
 }
@@ -470,6 +484,8 @@ moe_status route_permute_impl(const moe_route_args* args, int32_t tile, int32_t 
   q.group_blocks = cp.group_blocks;
   q.num_super = cp.num_super;
   q.counts = expert_counts;
+  q.max_count = T * a.top_k;
+  q.max_padded = (int)moe_max_padded_tokens(T, a.top_k, loc_n, tile);
   q.e2p = e2p;
   q.p2t = p2t;
   q.padded_offsets = padded_offsets;
@@ -604,7 +620,7 @@ moe_status moe_route(const moe_route_args* args, const void* logits, const void*
   if (st != MOE_OK) return st;
   if (rows != nullptr) {
     hipError_t e = launch_with_profile(MOE_KERNEL_COUNTS, stream, [&] {
-      return moe::launch_counts(rows, hdr, cp.num_super, E, expert_counts, stream);
+      return moe::launch_counts(rows, hdr, cp.num_super, E, T * a.top_k, expert_counts, stream);
     });
     if (e != hipSuccess) return hip_fail(e, "counts_kernel launch");
   }
@@ -862,6 +878,7 @@ moe_status rmsnorm_gate_route(const void* hidden, const void* gamma, const void*
   q.ids = topk_ids;
   q.aff = affinities;
   q.workspace = workspace;
+  q.spin_limit = front_end_spin_limit();
   hipError_t e = launch_with_profile(
       MOE_KERNEL_FRONT_END, stream, [&] { return moe::launch_front_end(q, stream); },
       /*single_kernel=*/false);

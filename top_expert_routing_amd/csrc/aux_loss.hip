@@ -158,9 +158,12 @@ __global__ void __launch_bounds__(kAuxBlock)
     if (threadIdx.x == 0) *loss = __uint_as_float(kAuxTimeoutNaN);
     return;
   }
-  // every slot read: return them to zero for the next call
+  // every slot read: return them to zero for the next call (the summing
+  // block's own slot too, which it never wrote: that repairs a dirty one)
   for (int u = 0; u < n_mine; ++u)
     __hip_atomic_store(slots + lo + u, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0)
+    __hip_atomic_store(slots + nb - 1, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (threadIdx.x == 0) *loss = (float)((((red4[0] + red4[1]) + red4[2]) + red4[3]) * scale);
 }
 

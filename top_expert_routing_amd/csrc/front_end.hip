@@ -19,8 +19,9 @@
 // r_t is its own ready flag: the workspace slot is zero between calls and
 // r_t > 0, so a gemm lane polls its token's slot (a device-scope load, coherent
 // across the XCDs' L2 caches) until it is non-zero.  The poll is bounded by a
-// spin limit: one that runs out sets the failure word, and the call then
-// writes -1 into topk_ids instead of hanging.
+// spin limit: one that runs out sets the failure word (and counts the call),
+// and the call then writes -1 into topk_ids instead of hanging; the last
+// select block to have read the word clears it again.
 //
 // select_kernel: one wavefront per token, after the projection: z = sum of
 // the partials in chunk order (+ router bias) -- deterministic; top-k on the
@@ -77,7 +78,6 @@ __device__ __forceinline__ uint32_t round_pair(f32x2v xg, float r) {
 constexpr int kThreads = 256;       // every role: 4 wavefronts
 constexpr int kNormVecs = 8;        // H <= 16384: 16384 / 8 / 256 vectors per thread
 constexpr int kXcds = 8;            // accelerator complex dies of the MI355X
-constexpr int kSpinLimit = 1 << 22; // polls before a wait gives up (far beyond any real wait)
 
 }  // namespace
 
@@ -94,9 +94,12 @@ constexpr int kNS = MOE_FE_GEMM_NS, kS = MOE_FE_GEMM_S;
 static_assert((kNS == 1 || kNS == 2 || kNS == 4) && (kS == 1 || kS == 2), "gemm tile shape");
 constexpr int kTileRows = 64 * kS;  // tokens per gemm block (one completion counter each)
 
-// Workspace: the synchronisation region -- a failure word (its own 256-byte
-// line) and the r_t slots [128], zero between calls -- then the float32
-// partials [H / kc, T, E].
+// Workspace: the synchronisation region -- a failure line of 256 bytes and
+// the r_t slots [128] -- then the float32 partials [H / kc, T, E].  The
+// failure line holds three words: [0] set when a wait gave up, [1] the number
+// of calls whose wait gave up (never cleared here: the caller's to read), [2]
+// the select blocks that have read [0] in such a call.  Only [1] may be
+// non-zero between calls.
 constexpr int kFailBytes = 256;
 static_assert(kFailBytes + 128 * 4 <= kFrontEndSyncBytes, "sync region");
 
@@ -116,6 +119,7 @@ struct FeArgs {
   uint32_t* rstd;     // [T] float32 bits, 0 = not yet written
   float* partial;     // [H / kc, T, E]
   int gemm_begin, gemm_blocks;
+  int spin_limit;     // polls before a wait gives up
 };
 
 // r_t crosses blocks inside one launch: it is stored and loaded with
@@ -129,8 +133,8 @@ __device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
 }
 
 // Poll one word until it is non-zero; 0 when the spin limit ran out.
-__device__ __forceinline__ uint32_t poll_nonzero(const uint32_t* p) {
-  for (int i = 0; i < kSpinLimit; ++i) {
+__device__ __forceinline__ uint32_t poll_nonzero(const uint32_t* p, int spin_limit) {
+  for (int i = 0; i < spin_limit; ++i) {
     const uint32_t v = ld_dev(p);
     if (v != 0u) return v;
     __builtin_amdgcn_s_sleep(2);
@@ -138,9 +142,11 @@ __device__ __forceinline__ uint32_t poll_nonzero(const uint32_t* p) {
   return 0u;
 }
 
-// A wait ran out: record it (the select kernel reads the word).
+// A wait ran out: record it (the select kernel reads the word); the first
+// wait of the call to give up also counts the call.
 __device__ __forceinline__ void mark_failed(const FeArgs& a) {
-  st_dev(a.fail, 1u);
+  if (__hip_atomic_exchange(a.fail, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u)
+    __hip_atomic_fetch_add(a.fail + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
@@ -293,7 +299,7 @@ __device__ void gemm_role(const FeArgs& a, int b, uint16_t* wt, uint16_t* gl) {
     const int row = row0 + 16 * s + col;
     uint32_t bits = 0u;
     if (row < T) {
-      bits = poll_nonzero(a.rstd + row);
+      bits = poll_nonzero(a.rstd + row, a.spin_limit);
       if (bits == 0u) mark_failed(a);
     }
     rr[s] = __uint_as_float(bits);
@@ -428,6 +434,13 @@ __global__ void __launch_bounds__(kThreads) norm_gemm_kernel(FeArgs a) {
   extern __shared__ __align__(16) uint16_t lds[];
   __shared__ float red[kThreads / 64];
   const int b = blockIdx.x;
+  // The failure word and the select blocks' counter start every call at zero,
+  // whatever a region that was not clean held: block 0 runs first, seconds
+  // before any wait could give up.
+  if (b == 0 && threadIdx.x == 0) {
+    st_dev(a.fail, 0u);
+    st_dev(a.fail + 2, 0u);
+  }
   if (b < a.T) rms_role<F16>(a, b, red);
   else if (b >= a.gemm_begin) gemm_role<F16, STEPS>(a, b - a.gemm_begin, lds + 8 + 32 * STEPS, lds);
 }
@@ -478,7 +491,7 @@ template <bool F16, int J>
 __global__ void __launch_bounds__(64)
     select_kernel(const float* __restrict__ partial, int nchunks, const uint16_t* __restrict__ rbias,
                   int T, int E, int k, int act_sigmoid, uint32_t* __restrict__ rstd,
-                  const uint32_t* __restrict__ fail, int32_t* __restrict__ ids,
+                  uint32_t* __restrict__ fail, int32_t* __restrict__ ids,
                   uint16_t* __restrict__ aff) {
   __shared__ uint64_t cand_lds[64];
   const int lane = threadIdx.x;
@@ -582,6 +595,16 @@ __global__ void __launch_bounds__(64)
     for (int j = 0; j < J; ++j) v[j] = ((taken >> j) & 1u) ? num[j] * inv : 0.0f;
     store_bf16<J>(aff + (size_t)t * E + e0, v);
   }
+  // a call whose wait gave up: the last select block to have read the failure
+  // word clears it (nothing of this runs otherwise)
+  if (failed && lane == 0) {
+    const uint32_t seen =
+        __hip_atomic_fetch_add(fail + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (seen == (uint32_t)T - 1u) {
+      st_dev(fail + 2, 0u);
+      st_dev(fail, 0u);
+    }
+  }
 }
 
 int front_end_kchunk(int H) {
@@ -617,6 +640,7 @@ hipError_t launch_front_end(const FrontEndParams& q, hipStream_t s) {
   a.fail = reinterpret_cast<uint32_t*>(ws);
   a.rstd = reinterpret_cast<uint32_t*>(ws + kFailBytes);
   a.partial = reinterpret_cast<float*>(ws + kFrontEndSyncBytes);
+  a.spin_limit = q.spin_limit;
   const int nchunks = q.H / a.kc;
   a.gemm_begin = (q.T + kXcds - 1) / kXcds * kXcds;   // keeps b % 8 for the XCD mapping
   a.gemm_blocks = ((q.E + 16 * kNS - 1) / (16 * kNS)) * ((q.T + kTileRows - 1) / kTileRows) * nchunks;

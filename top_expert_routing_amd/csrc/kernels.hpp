@@ -37,9 +37,15 @@ constexpr int kTokensPerBlock = 64;   // tokens per route/scatter block (one u64
 // scatter blocks of one call clear the set the previous call used.  A header
 // of four words follows the sets:
 //   hdr[0]  the set the next route kernel adds into,
-//   hdr[1]  the set the current call's readers read (written by route block 0),
+//   hdr[1]  the set the current call's readers read, plus 2 when hdr[0] held
+//           neither 0 nor 1 (written by route block 0),
 //   hdr[2 + s]  how many ints of set s the call that last used it touched.
 // A set is entirely zero whenever a route kernel starts adding into it.
+// Every index taken from the region is masked or clamped into it, so a
+// region that is not clean (never zeroed, or left by a launch that failed
+// mid-call) cannot move an access out of bounds.  The readers treat a header
+// out of range, a count outside [0, T k] or padded offsets that overflow as a
+// dirty region: they report it (-1 totals or counts) and clear both sets.
 constexpr int kMaxSuperRows = 64;
 constexpr int kMaxCountExperts = 2048;
 constexpr int kCountSetInts = kMaxSuperRows * kMaxCountExperts;
@@ -108,6 +114,8 @@ struct ScatterParams {
   const int32_t* hist;    // [nb, El] per-block counts
   int group_blocks, num_super;
   int32_t* counts;        // out [El]
+  int max_count;          // T k: no expert count exceeds it
+  int max_padded;         // entries of p2t (moe_max_padded_tokens)
   int32_t* e2p;
   int32_t* p2t;
   int32_t* padded_offsets;
@@ -150,8 +158,8 @@ __host__ __device__ inline RouteLds route_lds_layout(int lpt, int rwpl, int epl,
 size_t route_lds_bytes(int lpt, int rwpl, int epl, int hmask_len, int cap, int k, int n_group);
 size_t scatter_lds_bytes(int El);
 hipError_t launch_route(const RouteParams& p, int lpt, int epl, bool bf16, int nb, hipStream_t s);
-hipError_t launch_counts(int32_t* super_rows, const uint32_t* count_hdr, int num_super, int El,
-                         int32_t* counts, hipStream_t s);
+hipError_t launch_counts(int32_t* super_rows, uint32_t* count_hdr, int num_super, int El,
+                         int max_count, int32_t* counts, hipStream_t s);
 hipError_t launch_scatter(const ScatterParams& p, int nb, hipStream_t s);
 hipError_t launch_empty_outputs(int32_t* counts, int El, int32_t* padded_offsets, int32_t* total,
                                 int32_t* nctas, hipStream_t s);
@@ -195,8 +203,11 @@ struct FrontEndParams {
   void* normed;
   int32_t* ids;
   void* aff;
-  void* workspace;        // sync region (failure word, r_t slots), partials [H / kchunk, T, E]
+  void* workspace;        // sync region (failure line, r_t slots), partials [H / kchunk, T, E]
+  int spin_limit;         // polls before a wait for r_t gives up
 };
+// Polls before a front-end wait gives up: far beyond any real wait (seconds).
+constexpr int kFrontEndSpinLimit = 1 << 22;
 // The front-end workspace starts with a synchronisation region of this many
 // bytes: zero before the first call, zero again after every call.
 constexpr int kFrontEndSyncBytes = 1024;

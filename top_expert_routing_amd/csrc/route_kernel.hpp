@@ -445,7 +445,8 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>)
   }
   const bool counting = p.super_rows != nullptr || p.fused;
   // the set of counting rows this call adds into (requested early, used last)
-  const uint32_t cset = p.super_rows != nullptr ? p.count_hdr[0] : 0u;
+  const uint32_t hdr0 = p.super_rows != nullptr ? p.count_hdr[0] : 0u;
+  const uint32_t cset = hdr0 & 1u;
   if (counting)
     for (int e = tid; e < p.loc_n; e += BLOCK) hmask[e] = 0;
   __syncthreads();
@@ -789,7 +790,7 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>)
     int32_t* srow = p.super_rows + (size_t)cset * kCountSetInts +
                     (size_t)(blk / p.group_blocks) * p.loc_n;
     if (blk == 0 && tid == 0) {          // for this call's readers
-      p.count_hdr[1] = cset;
+      p.count_hdr[1] = cset | (hdr0 > 1u ? 2u : 0u);
       p.count_hdr[2 + cset] = (uint32_t)(p.num_super * p.loc_n);
     }
     for (int e = tid; e < p.loc_n; e += BLOCK) {

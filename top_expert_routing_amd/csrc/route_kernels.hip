@@ -39,19 +39,33 @@
 namespace moe {
 
 // Per-expert totals of moe_route: sums the call's set of counting rows and
-// clears it (each expert's rows are read by one thread only).
-__global__ void counts_kernel(int32_t* __restrict__ super_rows, const uint32_t* count_hdr,
-                              int num_super, int El, int32_t* __restrict__ counts) {
+// clears it (each expert's rows are read by one thread only).  A count outside
+// [0, T k] is reported as -1; a header that shows a dirty region makes every
+// count -1 and clears both sets.
+__global__ void counts_kernel(int32_t* __restrict__ super_rows, uint32_t* count_hdr,
+                              int num_super, int El, int max_count, int32_t* __restrict__ counts) {
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= El) return;
-  super_rows += (size_t)count_hdr[1] * kCountSetInts;
-  int tot = 0;
-  for (int r = 0; r < num_super; ++r) {
-    int32_t* a = super_rows + (size_t)r * El + e;
-    tot += *a;
-    *a = 0;
+  const uint32_t h1 = count_hdr[1];
+  const bool dirty = (h1 >> 1) != 0u;
+  if (e < El) {
+    int32_t* rows = super_rows + (size_t)(h1 & 1u) * kCountSetInts;
+    int tot = 0;
+    for (int r = 0; r < num_super; ++r) {
+      int32_t* a = rows + (size_t)r * El + e;
+      tot += *a;
+      *a = 0;
+    }
+    counts[e] = dirty || tot < 0 || tot > max_count ? -1 : tot;
   }
-  counts[e] = tot;
+  if (dirty) {
+    const int nt = gridDim.x * blockDim.x;
+    for (int i = e; i < 2 * kCountSetInts; i += nt) super_rows[i] = 0;
+    if (e == 0) {
+      count_hdr[0] = 0u;
+      count_hdr[2] = 0u;
+      count_hdr[3] = 0u;
+    }
+  }
 }
 
 // Scatter: one block per 64-token block of the route kernel.
@@ -100,9 +114,12 @@ __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams 
     idv[i] = tid + i * kScatterThreads < valid_pairs ? idv[i] - p.off : -1;
   const int grp = blk / p.group_blocks;
   const int g0 = grp * p.group_blocks;
-  const uint32_t cset = p.count_hdr[1];                  // the set this call's route kernel used
+  const uint32_t h1 = p.count_hdr[1];
+  const uint32_t cset = h1 & 1u;                         // the set this call's route kernel used
   const int32_t* srows = p.super_rows + (size_t)cset * kCountSetInts;
-  const int prev_ext = (int)p.count_hdr[2 + (1u - cset)];   // ints the previous user of the other touched
+  const uint32_t ext_other = p.count_hdr[2 + (1u - cset)];  // ints the previous user of the other touched
+  const uint32_t ext_own = p.count_hdr[2 + cset];           // ints this call's route kernel touched
+  int bad = 0;                                           // a count outside [0, T k]
   if constexpr (S == 1) {
     for (int e = tid; e < El; e += kScatterThreads) {
       int tot = 0, pre = 0;
@@ -124,6 +141,7 @@ __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams 
       base[e] = pre;
       po[e] = (tot + tile - 1) & ~(tile - 1);
       msk[e] = 0;
+      bad |= (tot < 0) | (tot > p.max_count);
     }
   } else {
     // thread h * El + e sums rows h, h + 2, ... of expert e; the second half's
@@ -161,18 +179,11 @@ __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams 
       base[e] = pre;
       po[e] = (tot + tile - 1) & ~(tile - 1);
       msk[e] = 0;
+      bad |= (tot < 0) | (tot > p.max_count);
     }
   }
   if (tid == 0) po[El] = 0;
-  __syncthreads();
-  // The other set was used by the previous call and fully read by its
-  // scatter: clear it (strided over the blocks) for the next call, which adds
-  // into it.
-  {
-    int32_t* other = p.super_rows + (size_t)(1u - cset) * kCountSetInts;
-    for (int i = blk * kScatterThreads + tid; i < prev_ext; i += nb * kScatterThreads) other[i] = 0;
-    if (blk == 0 && tid == 0) p.count_hdr[0] = 1u - cset;
-  }
+  const int bad_count = __syncthreads_or(bad);
 
   // token bitmasks (LDS atomics), then the exclusive scan of the padded sizes
   // over the block, 256 experts per round (wavefront scans in DPP moves)
@@ -183,18 +194,46 @@ __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams 
     if (el >= 0 && el < El) atomicOr(&msk[el], 1ull << ((q * p.k_magic) >> 20));
   }
   int* scan_tmp = cnt + El;                              // kScatterThreads / 64 ints
-  int carry = 0;
+  int carry = 0, neg = 0;
   for (int e0 = 0; e0 < El; e0 += kScatterThreads) {   // uniform trip count
     const int e = e0 + tid;
     const int v = e < El ? po[e] : 0;
     int round_total;
     const int ex = block_excl_scan<kScatterThreads>(v, scan_tmp, round_total);
-    if (e < El) po[e] = carry + ex;
+    if (e < El) {
+      po[e] = carry + ex;
+      neg |= carry + ex < 0;                             // the running sum wrapped
+    }
     carry += round_total;
   }
   if (tid == 0) po[El] = carry;
-  __syncthreads();
+  const int wrapped = __syncthreads_or(neg);
   const int total = po[El];
+  // A dirty counting region (see kCountSetInts): the permutation is not
+  // written past the caller's arrays, the totals report -1 and both sets are
+  // cleared.  Every term is uniform over the grid.
+  const bool dirty = (h1 >> 1) != 0u || ext_other > (uint32_t)kCountSetInts ||
+                     ext_own > (uint32_t)kCountSetInts || bad_count || wrapped || total < 0 ||
+                     total > p.max_padded;
+  // The other set was used by the previous call and fully read by its
+  // scatter: clear it (strided over the blocks) for the next call, which adds
+  // into it; after a dirty region also the part of this call's set that its
+  // route kernel did not touch (the touched part is cleared by the next call).
+  {
+    int32_t* other = p.super_rows + (size_t)(1u - cset) * kCountSetInts;
+    const int n_other = dirty ? kCountSetInts : (int)ext_other;
+    for (int i = blk * kScatterThreads + tid; i < n_other; i += nb * kScatterThreads) other[i] = 0;
+    if (dirty) {
+      int32_t* own = p.super_rows + (size_t)cset * kCountSetInts;
+      const int from = ext_own > (uint32_t)kCountSetInts ? kCountSetInts : (int)ext_own;
+      for (int i = from + blk * kScatterThreads + tid; i < kCountSetInts; i += nb * kScatterThreads)
+        own[i] = 0;
+    }
+    if (blk == 0 && tid == 0) {
+      p.count_hdr[0] = 1u - cset;
+      if (dirty) p.count_hdr[2 + (1u - cset)] = 0u;   // that set is all zero now
+    }
+  }
 
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
@@ -206,13 +245,16 @@ __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams 
     if (el >= 0 && el < El) {
       const uint64_t below = tl == 0 ? 0ull : (msk[el] & ((1ull << tl) - 1ull));
       slot = po[el] + base[el] + __popcll(below);
-      p.p2t[slot] = t0 + tl;
+      if ((unsigned)slot < (unsigned)p.max_padded) p.p2t[slot] = t0 + tl;
+      else slot = -1;                                    // only with a dirty region
     }
     p.e2p[(size_t)t0 * k + q] = slot;
   }
 
-  // tiles of this block's experts: b, b + nb, b + 2 nb, ... (no division)
-  for (int e = blk; e < El; e += nb) {
+  // tiles of this block's experts: b, b + nb, b + 2 nb, ... (no division);
+  // with a clean region the offsets are non-decreasing and end at
+  // total <= max_padded, so every tile and padding slot is in bounds
+  for (int e = dirty ? El : blk; e < El; e += nb) {
     const int seg = po[e];
     const int seg_end = seg + cnt[e];
     const int ntile = (po[e + 1] - seg) >> p.tile_shift;
@@ -226,11 +268,11 @@ __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams 
   if (blk == 0) {
     for (int e = tid; e <= El; e += kScatterThreads) {
       p.padded_offsets[e] = po[e];
-      if (e < El) p.counts[e] = cnt[e];
+      if (e < El) p.counts[e] = dirty ? -1 : cnt[e];
     }
     if (tid == 0) {
-      *p.total_out = total;
-      *p.nctas_out = total >> p.tile_shift;
+      *p.total_out = dirty ? -1 : total;
+      *p.nctas_out = dirty ? -1 : total >> p.tile_shift;
     }
   }
 }
@@ -292,10 +334,10 @@ hipError_t launch_route(const RouteParams& p, int lpt, int epl, bool bf16, int n
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_counts(int32_t* super_rows, const uint32_t* count_hdr, int num_super, int El,
-                         int32_t* counts, hipStream_t s) {
+hipError_t launch_counts(int32_t* super_rows, uint32_t* count_hdr, int num_super, int El,
+                         int max_count, int32_t* counts, hipStream_t s) {
   MOE_LAUNCH(counts_kernel, dim3((El + 255) / 256), dim3(256), 0, s, super_rows, count_hdr,
-             num_super, El, counts);
+             num_super, El, max_count, counts);
   return hipGetLastError();
 }
 
