@@ -92,10 +92,25 @@ def test_workload_full_size(name):
 
 def test_deepseek_like_large_T():
     # the headline method at T = 262144 (4096 route blocks, 64 counting rows of
-    # 64 blocks each), the size the benchmark also times
+    # 64 blocks each, four route blocks per scatter block), the size the
+    # benchmark also times
     w = with_overrides(WORKLOADS["deepseek_v3_like"], T=262144)
     logits, bias = route_inputs(w)
     run_and_check(w, logits, bias, "deepseek_v3_like T=262144")
+
+
+@pytest.mark.parametrize("name,T", [
+    ("qwen_moe_like", 65536 + 5),            # 1025 route blocks, two per scatter block
+    ("deepseek_v3_like", 131072 + 128 + 3),  # 2051 route blocks, four per scatter block
+    ("mixtral_like", 2048 * 64 + 64 * 2 + 7),
+    ("deepseek_v3_like", 1024 * 64 - 1),     # 1024 blocks, the last one ragged
+])
+def test_scatter_blocks_sharing_route_blocks(name, T):
+    # large T: one scatter block serves two or four route blocks; the last
+    # scatter block holds fewer of them, and the last route block fewer tokens
+    w = WORKLOADS[name]
+    logits, bias = route_inputs(w, T=T, seed=T % 1000)
+    run_and_check(w, logits, bias, f"{name} T={T}")
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))

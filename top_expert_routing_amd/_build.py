@@ -39,10 +39,10 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found; the HIP library cannot be built")
 
 
-# Per-source flags.  route_kernels.hip: the scatter kernel's block counter is a
-# single-lane returning atomic whose result is needed only at the kernel's end;
-# the atomic optimizer would turn it into a wave-wide atomic plus readfirstlane
-# at the branch join, which waits for the return at once.
+# Per-source flags.  route_kernels.hip: built without LLVM's AMDGPU atomic
+# optimizer, which turned a single-lane returning atomic (a block counter the
+# scatter kernel once had) into a wave-wide atomic awaited at once; the flag
+# stays with the file's kernels as they were measured.
 SOURCE_FLAGS = {
     "route_kernels.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
 }

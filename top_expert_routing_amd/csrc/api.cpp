@@ -210,15 +210,30 @@ static_assert(kCountRegionBytes % 256 == 0, "the per-block counts follow 256-byt
 
 struct CountPlan {
   int nb = 0, group_blocks = 1, num_super = 1;
+  int sub_blocks = 1;   // route blocks per scatter block
 };
-CountPlan count_plan(int T) {
+// Route blocks per scatter block: every scatter block reads the counting rows
+// (about 2 sqrt(nb) rows of E_loc counts) for its totals, so at large nb
+// those reads dominate and one scatter block serves several route blocks.
+// Limits: a scatter block's pairs fit the k_magic division (R k <= 64) and
+// its LDS (two R E_loc arrays) stays within 64 KiB.
+int scatter_sub_blocks(int nb, int k, int loc_n) {
+  int r = nb >= 2048 ? 4 : (nb >= 1024 ? 2 : 1);
+  while (r > 1 && ((int64_t)r * k > 64 || moe::scatter_lds_bytes(loc_n, r) > 64 * 1024)) r >>= 1;
+  return r;
+}
+// sub_blocks > 1: the group size is a multiple of it, so that the route blocks
+// of one scatter block share a counting group.
+CountPlan count_plan(int T, int sub_blocks = 1) {
   CountPlan c;
   c.nb = num_blocks(T);
+  c.sub_blocks = sub_blocks;
   int g = 1;
   while ((int64_t)g * g < c.nb) ++g;                 // ~sqrt(nb) blocks per row
   const int gmin = (c.nb + moe::kMaxSuperRows - 1) / moe::kMaxSuperRows;
   c.group_blocks = g > gmin ? g : gmin;
   if (c.group_blocks < 1) c.group_blocks = 1;
+  c.group_blocks = (c.group_blocks + sub_blocks - 1) / sub_blocks * sub_blocks;
   c.num_super = (c.nb + c.group_blocks - 1) / c.group_blocks;
   return c;
 }
@@ -439,7 +454,7 @@ moe_status route_permute_impl(const moe_route_args* args, int32_t tile, int32_t 
   void* workspace = nullptr;
   st = wsp.get(need, &workspace, stream);
   if (st != MOE_OK) return st;
-  const CountPlan cp = count_plan(T);
+  const CountPlan cp = count_plan(T, scatter_sub_blocks(num_blocks(T), a.top_k, loc_n));
   int32_t* rows = ws_count_rows(workspace);
   int32_t* hist = ws_hist(workspace);
 
@@ -483,6 +498,8 @@ moe_status route_permute_impl(const moe_route_args* args, int32_t tile, int32_t 
   q.count_hdr = ws_count_hdr(workspace);
   q.group_blocks = cp.group_blocks;
   q.num_super = cp.num_super;
+  q.sub_blocks = cp.sub_blocks;
+  q.route_blocks = cp.nb;
   q.counts = expert_counts;
   q.max_count = T * a.top_k;
   q.max_padded = (int)moe_max_padded_tokens(T, a.top_k, loc_n, tile);
@@ -494,7 +511,10 @@ moe_status route_permute_impl(const moe_route_args* args, int32_t tile, int32_t 
   q.batch_idx = batch_idx;
   q.mn_limit = mn_limit;
   hipError_t e = launch_with_profile(MOE_KERNEL_SCATTER, stream,
-                                     [&] { return moe::launch_scatter(q, cp.nb, stream); });
+                                     [&] {
+                                       return moe::launch_scatter(
+                                           q, (cp.nb + cp.sub_blocks - 1) / cp.sub_blocks, stream);
+                                     });
   if (e != hipSuccess) return hip_fail(e, "scatter_kernel launch");
   return MOE_OK;
 }

@@ -113,6 +113,8 @@ struct ScatterParams {
   uint32_t* count_hdr;    // their header (see kCountSetInts)
   const int32_t* hist;    // [nb, El] per-block counts
   int group_blocks, num_super;
+  int sub_blocks;         // route blocks per scatter block (divides group_blocks)
+  int route_blocks;       // route blocks of the call
   int32_t* counts;        // out [El]
   int max_count;          // T k: no expert count exceeds it
   int max_padded;         // entries of p2t (moe_max_padded_tokens)
@@ -156,7 +158,7 @@ __host__ __device__ inline RouteLds route_lds_layout(int lpt, int rwpl, int epl,
 }
 
 size_t route_lds_bytes(int lpt, int rwpl, int epl, int hmask_len, int cap, int k, int n_group);
-size_t scatter_lds_bytes(int El);
+size_t scatter_lds_bytes(int El, int sub_blocks);
 hipError_t launch_route(const RouteParams& p, int lpt, int epl, bool bf16, int nb, hipStream_t s);
 hipError_t launch_counts(int32_t* super_rows, uint32_t* count_hdr, int num_super, int El,
                          int max_count, int32_t* counts, hipStream_t s);

@@ -68,38 +68,45 @@ __global__ void counts_kernel(int32_t* __restrict__ super_rows, uint32_t* count_
   }
 }
 
-// Scatter: one block per 64-token block of the route kernel.
-//   1. expert totals and this block's base ranks from the call's set of
-//      counting rows (rows of earlier groups) and the per-block counts of
-//      earlier blocks of its own group; the blocks clear the other set, which
-//      the previous call used, for the next call;
-//   2. padded offsets (a scan over the experts), the block's token bitmask per
-//      expert, slot = offset + base + popcount of the lower token bits;
+// Scatter: one block per R consecutive 64-token blocks of the route kernel
+// (its sub-blocks; R divides the counting group size, so they share a group).
+//   1. expert totals and the base rank of each sub-block from the call's set
+//      of counting rows (rows of earlier groups), the per-block counts of
+//      earlier blocks of the group and of the earlier sub-blocks; the blocks
+//      clear the other set, which the previous call used, for the next call;
+//   2. padded offsets (a scan over the experts), each sub-block's token
+//      bitmask per expert, slot = offset + base + popcount of the lower token
+//      bits;
 //   3. the tiles of the experts b, b + nb, b + 2 nb, ...: expert, row limit
 //      and the -1 padding of each segment's last tile.
+// Every block reads the counting rows for the totals; R > 1 shares that read
+// among R route blocks (large T, where those reads dominate).
 constexpr int kScatterThreads = 256;
 
-// NP = (token, choice) pairs per thread: 64 k / kScatterThreads rounded up to
-// a power of two (k <= 4, 8, 16, 32, 64).  The ids are loaded unconditionally
-// (clamped index) so that all NP loads are in flight together.
+// NP = (token, choice) pairs per thread: 64 R k / kScatterThreads rounded up
+// to a power of two.  The ids are loaded unconditionally (clamped index) so
+// that all NP loads are in flight together.
 // S = 2: the counting rows and per-block rows of an expert are split between
 // two threads (every other row; El <= kScatterThreads / 2), so that up to 32
 // counting rows and 32 per-block rows need one round of loads, not two.
-template <int NP, int S>
+template <int NP, int S, bool MULTI>
 __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int El = p.El;
-  uint64_t* msk = reinterpret_cast<uint64_t*>(smem);
-  int* po = reinterpret_cast<int*>(msk + El);           // El + 1
-  int* base = po + El + 1;                               // El
-  int* cnt = base + El;                                  // El
+  const int R = MULTI ? p.sub_blocks : 1;
+  uint64_t* msk = reinterpret_cast<uint64_t*>(smem);    // R El: sub-block r at r El
+  int* po = reinterpret_cast<int*>(msk + R * El);       // El + 1
+  int* base = po + El + 1;                               // R El
+  int* cnt = base + R * El;                              // El
   const int tid = threadIdx.x;
   const int blk = blockIdx.x;
   const int nb = gridDim.x;
   const int tile = p.tile;
   const int k = p.k;
-  const int npairs = kTokensPerBlock * k;
-  const int t0 = blk * kTokensPerBlock;
+  const int b0 = blk * R;                                // first route block
+  const int nsub = min(R, p.route_blocks - b0);
+  const int npairs = kTokensPerBlock * R * k;
+  const int t0 = b0 * kTokensPerBlock;
   const int valid_pairs = min(npairs, (p.T - t0) * k);
 
   // all global reads first (a block always holds a token: index 0 is in bounds)
@@ -112,7 +119,7 @@ __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams 
 #pragma unroll
   for (int i = 0; i < NP; ++i)
     idv[i] = tid + i * kScatterThreads < valid_pairs ? idv[i] - p.off : -1;
-  const int grp = blk / p.group_blocks;
+  const int grp = b0 / p.group_blocks;
   const int g0 = grp * p.group_blocks;
   const uint32_t h1 = p.count_hdr[1];
   const uint32_t cset = h1 & 1u;                         // the set this call's route kernel used
@@ -120,16 +127,24 @@ __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams 
   const uint32_t ext_other = p.count_hdr[2 + (1u - cset)];  // ints the previous user of the other touched
   const uint32_t ext_own = p.count_hdr[2 + cset];           // ints this call's route kernel touched
   int bad = 0;                                           // a count outside [0, T k]
+  // per-sub-block counts of the block's own route blocks (the first needs none)
+  auto own_rows = [&](int e, int pre) {
+    base[e] = pre;
+    for (int r = 1; r < R; ++r) {
+      pre += r < nsub ? p.hist[(size_t)(b0 + r - 1) * El + e] : 0;
+      base[r * El + e] = pre;
+    }
+  };
   if constexpr (S == 1) {
     for (int e = tid; e < El; e += kScatterThreads) {
       int tot = 0, pre = 0;
       // 16 counting rows and 16 per-block rows in flight at a time
-      for (int r0 = 0; r0 < p.num_super || g0 + r0 < blk; r0 += 16) {
+      for (int r0 = 0; r0 < p.num_super || g0 + r0 < b0; r0 += 16) {
         int sv[16], hv[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           sv[i] = r0 + i < p.num_super ? srows[(size_t)(r0 + i) * El + e] : 0;
-          hv[i] = g0 + r0 + i < blk ? p.hist[(size_t)(g0 + r0 + i) * El + e] : 0;
+          hv[i] = g0 + r0 + i < b0 ? p.hist[(size_t)(g0 + r0 + i) * El + e] : 0;
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -138,9 +153,9 @@ __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams 
         }
       }
       cnt[e] = tot;
-      base[e] = pre;
+      own_rows(e, pre);
       po[e] = (tot + tile - 1) & ~(tile - 1);
-      msk[e] = 0;
+      for (int r = 0; r < R; ++r) msk[r * El + e] = 0;
       bad |= (tot < 0) | (tot > p.max_count);
     }
   } else {
@@ -151,13 +166,13 @@ __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams 
     const int e = tid - h * El;
     int tot = 0, pre = 0;
     if (e < El) {
-      for (int r0 = h; r0 < p.num_super || g0 + r0 < blk; r0 += 32) {
+      for (int r0 = h; r0 < p.num_super || g0 + r0 < b0; r0 += 32) {
         int sv[16], hv[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int r = r0 + 2 * i;
           sv[i] = r < p.num_super ? srows[(size_t)r * El + e] : 0;
-          hv[i] = g0 + r < blk ? p.hist[(size_t)(g0 + r) * El + e] : 0;
+          hv[i] = g0 + r < b0 ? p.hist[(size_t)(g0 + r) * El + e] : 0;
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -176,9 +191,9 @@ __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams 
       tot += part[e];
       pre += part[El + e];
       cnt[e] = tot;
-      base[e] = pre;
+      own_rows(e, pre);
       po[e] = (tot + tile - 1) & ~(tile - 1);
-      msk[e] = 0;
+      for (int r = 0; r < R; ++r) msk[r * El + e] = 0;
       bad |= (tot < 0) | (tot > p.max_count);
     }
   }
@@ -186,12 +201,15 @@ __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams 
   const int bad_count = __syncthreads_or(bad);
 
   // token bitmasks (LDS atomics), then the exclusive scan of the padded sizes
-  // over the block, 256 experts per round (wavefront scans in DPP moves)
+  // over the block, 256 experts per round (wavefront scans in DPP moves).
+  // Pair q is token q / k of the block: sub-block (q / k) / 64, bit (q / k) % 64.
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     const int q = tid + i * kScatterThreads;
     const int el = idv[i];
-    if (el >= 0 && el < El) atomicOr(&msk[el], 1ull << ((q * p.k_magic) >> 20));
+    const int tg = (int)((q * p.k_magic) >> 20);
+    const int r = MULTI ? tg >> 6 : 0;                   // single: tg < 64
+    if (el >= 0 && el < El) atomicOr(&msk[r * El + el], 1ull << (MULTI ? tg & 63 : tg));
   }
   int* scan_tmp = cnt + El;                              // kScatterThreads / 64 ints
   int carry = 0, neg = 0;
@@ -239,13 +257,15 @@ __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams 
   for (int i = 0; i < NP; ++i) {
     const int q = tid + i * kScatterThreads;
     if (q >= valid_pairs) continue;
-    const int tl = (int)((q * p.k_magic) >> 20);
+    const int tg = (int)((q * p.k_magic) >> 20);
+    const int tl = MULTI ? tg & 63 : tg;
     const int el = idv[i];
     int slot = -1;
     if (el >= 0 && el < El) {
-      const uint64_t below = tl == 0 ? 0ull : (msk[el] & ((1ull << tl) - 1ull));
-      slot = po[el] + base[el] + __popcll(below);
-      if ((unsigned)slot < (unsigned)p.max_padded) p.p2t[slot] = t0 + tl;
+      const int r = MULTI ? tg >> 6 : 0;
+      const uint64_t below = tl == 0 ? 0ull : (msk[r * El + el] & ((1ull << tl) - 1ull));
+      slot = po[el] + base[r * El + el] + __popcll(below);
+      if ((unsigned)slot < (unsigned)p.max_padded) p.p2t[slot] = t0 + tg;
       else slot = -1;                                    // only with a dirty region
     }
     p.e2p[(size_t)t0 * k + q] = slot;
@@ -341,28 +361,36 @@ hipError_t launch_counts(int32_t* super_rows, uint32_t* count_hdr, int num_super
   return hipGetLastError();
 }
 
-// msk (El u64), po (El + 1), base, cnt (El each), and the split partials (2 El)
-size_t scatter_lds_bytes(int El) {
-  return (size_t)El * 8 + (size_t)(El + 1) * 4 + (size_t)El * 16 + 16;   // + the scan's wave sums
+// msk (R El u64), po (El + 1), base (R El), cnt (El), and the split
+// partials (2 El), or the scan's wave sums
+size_t scatter_lds_bytes(int El, int R) {
+  return (size_t)R * El * 8 + (size_t)(El + 1) * 4 + (size_t)R * El * 4 + (size_t)El * 12 + 16;
 }
 
-template <int S>
+template <int S, bool MULTI>
 static void launch_scatter_s(const ScatterParams& p, int nb, hipStream_t s) {
-  const size_t lds = scatter_lds_bytes(p.El);
-  const int np = (kTokensPerBlock * p.k + kScatterThreads - 1) / kScatterThreads;
-  if (np <= 1) MOE_LAUNCH((scatter_kernel<1, S>), dim3(nb), dim3(kScatterThreads), lds, s, p);
-  else if (np <= 2) MOE_LAUNCH((scatter_kernel<2, S>), dim3(nb), dim3(kScatterThreads), lds, s, p);
-  else if (np <= 4) MOE_LAUNCH((scatter_kernel<4, S>), dim3(nb), dim3(kScatterThreads), lds, s, p);
-  else if (np <= 8) MOE_LAUNCH((scatter_kernel<8, S>), dim3(nb), dim3(kScatterThreads), lds, s, p);
-  else MOE_LAUNCH((scatter_kernel<16, S>), dim3(nb), dim3(kScatterThreads), lds, s, p);
+  const size_t lds = scatter_lds_bytes(p.El, p.sub_blocks);
+  const int np = (kTokensPerBlock * p.sub_blocks * p.k + kScatterThreads - 1) / kScatterThreads;
+  const dim3 g(nb), b(kScatterThreads);
+  if (np <= 1) MOE_LAUNCH((scatter_kernel<1, S, MULTI>), g, b, lds, s, p);
+  else if (np <= 2) MOE_LAUNCH((scatter_kernel<2, S, MULTI>), g, b, lds, s, p);
+  else if (np <= 4) MOE_LAUNCH((scatter_kernel<4, S, MULTI>), g, b, lds, s, p);
+  else if (np <= 8) MOE_LAUNCH((scatter_kernel<8, S, MULTI>), g, b, lds, s, p);
+  else MOE_LAUNCH((scatter_kernel<16, S, MULTI>), g, b, lds, s, p);
 }
 
 hipError_t launch_scatter(const ScatterParams& p, int nb, hipStream_t s) {
   // split the rows when an expert has more than 16 counting or per-block rows
   // to read and two threads per expert fit the block
   const int rows = p.num_super > p.group_blocks - 1 ? p.num_super : p.group_blocks - 1;
-  if (2 * p.El <= kScatterThreads && rows > 16) launch_scatter_s<2>(p, nb, s);
-  else launch_scatter_s<1>(p, nb, s);
+  const bool split = 2 * p.El <= kScatterThreads && rows > 16;
+  if (p.sub_blocks > 1) {
+    if (split) launch_scatter_s<2, true>(p, nb, s);
+    else launch_scatter_s<1, true>(p, nb, s);
+  } else {
+    if (split) launch_scatter_s<2, false>(p, nb, s);
+    else launch_scatter_s<1, false>(p, nb, s);
+  }
   return hipGetLastError();
 }
 
