@@ -55,6 +55,8 @@ def parse():
                     help="seconds of oracle work timed for the headline cpu_baseline")
     ap.add_argument("--cpu-seconds-other", type=float, default=3.0,
                     help="seconds of oracle work timed beside each other workload")
+    ap.add_argument("--only-other", default=None,
+                    help="comma-separated other_configs entries to run (the rest are skipped)")
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="finish with plain device copies of this many MiB (the reference "
@@ -120,12 +122,16 @@ def route_permute_bytes(w, T, total, ntiles):
             2 * ntiles * 4 + w.E * 4 + (w.E + 1) * 4 + 8)
 
 
-def other_configs(mr, torch, np, dev, rotate_mb, K, cpu_seconds=None):
+def other_configs(mr, torch, np, dev, rotate_mb, K, cpu_seconds=None, only=None):
     """The other workloads, each cold (rotating sets past 2x the MALL): ms per
     call and algorithmic GB/s; with cpu_seconds, the oracle timed beside each
-    (cpu_baseline) and the near-tie count of the GPU's output."""
+    (cpu_baseline) and the near-tie count of the GPU's output.  `only`: the names
+    of the entries to run (all when None)."""
     from workloads import WORKLOADS, FRONT_END, front_end_inputs, route_inputs, with_overrides
     res = {}
+
+    def want(name):
+        return only is None or name in only
 
     def dev_logits(w, arr):
         if w.logits_dtype == "bf16":
@@ -133,6 +139,8 @@ def other_configs(mr, torch, np, dev, rotate_mb, K, cpu_seconds=None):
         return torch.from_numpy(arr).to(dev)
 
     for name in ("tiny_softmax_post", "mixtral_like", "qwen_moe_like"):
+        if not want(name):
+            continue
         w = WORKLOADS[name]
         logits, bias = route_inputs(w)
         x0 = dev_logits(w, logits)
@@ -193,6 +201,8 @@ def other_configs(mr, torch, np, dev, rotate_mb, K, cpu_seconds=None):
     # backward of the routing outputs (DeepSeek-V3-like: weights gradient;
     # Qwen-like: weights and full-E scores gradients), cold like the rest
     for name, with_s in (("deepseek_v3_like", False), ("qwen_moe_like", True)):
+        if not want(name + "_backward"):
+            continue
         w = WORKLOADS[name]
         logits, _ = route_inputs(w)
         x0 = dev_logits(w, logits)
@@ -215,135 +225,140 @@ def other_configs(mr, torch, np, dev, rotate_mb, K, cpu_seconds=None):
             "gbs": set_b / (ms * 1e-3) / 1e9, "buffer_sets": R}
         del bsets
 
-    # dense [T, E] probs + routing map from the DeepSeek-V3-like top-k outputs
-    w = WORKLOADS["deepseek_v3_like"]
-    gen = torch.Generator(device="cpu").manual_seed(w.seed + 3)
-    ids0 = torch.argsort(torch.rand((w.T, w.E), generator=gen), dim=1)[:, :w.k].to(torch.int32).to(dev)
-    wts0 = torch.rand((w.T, w.k), generator=gen).to(dev)
-    x_bytes = w.T * w.k * 8 + w.T * w.E * 5
-    R = n_sets(x_bytes, rotate_mb)
-    xsets = [(ids0.clone(), wts0.clone(), torch.empty((w.T, w.E), dtype=torch.float32, device=dev),
-              torch.empty((w.T, w.E), dtype=torch.uint8, device=dev)) for _ in range(R)]
-    ms_x = graph_ms(torch, lambda i: mr.moe_topk_to_dense(w.T, w.E, w.k, xsets[i % R][0], xsets[i % R][1],
-                                                          mr.MOE_F32, xsets[i % R][2], xsets[i % R][3]), K)
-    res["deepseek_v3_like_dense_outputs"] = {
-        "workload": f"{w.description}; top-k ids/weights -> dense probs [T,E] f32 + routing map [T,E] u8",
-        "us_per_call": ms_x * 1e3, "algorithmic_bytes": x_bytes, "gbs": x_bytes / (ms_x * 1e-3) / 1e9,
-        "buffer_sets": R}
-    del xsets
+    if want("deepseek_v3_like_dense_outputs"):
+        # dense [T, E] probs + routing map from the DeepSeek-V3-like top-k outputs
+        w = WORKLOADS["deepseek_v3_like"]
+        gen = torch.Generator(device="cpu").manual_seed(w.seed + 3)
+        ids0 = torch.argsort(torch.rand((w.T, w.E), generator=gen), dim=1)[:, :w.k].to(torch.int32).to(dev)
+        wts0 = torch.rand((w.T, w.k), generator=gen).to(dev)
+        x_bytes = w.T * w.k * 8 + w.T * w.E * 5
+        R = n_sets(x_bytes, rotate_mb)
+        xsets = [(ids0.clone(), wts0.clone(), torch.empty((w.T, w.E), dtype=torch.float32, device=dev),
+                  torch.empty((w.T, w.E), dtype=torch.uint8, device=dev)) for _ in range(R)]
+        ms_x = graph_ms(torch, lambda i: mr.moe_topk_to_dense(w.T, w.E, w.k, xsets[i % R][0], xsets[i % R][1],
+                                                              mr.MOE_F32, xsets[i % R][2], xsets[i % R][3]), K)
+        res["deepseek_v3_like_dense_outputs"] = {
+            "workload": f"{w.description}; top-k ids/weights -> dense probs [T,E] f32 + routing map [T,E] u8",
+            "us_per_call": ms_x * 1e3, "algorithmic_bytes": x_bytes, "gbs": x_bytes / (ms_x * 1e-3) / 1e9,
+            "buffer_sets": R}
+        del xsets
 
-    # the headline method at 16x the tokens (T = 262144, 134 MB of logits): how
-    # close the same kernels come to the HBM roofline once a launch is long
-    # enough to hide its cold reads and its drain
-    w = with_overrides(WORKLOADS["deepseek_v3_like"], T=262144)
-    logits, bias = route_inputs(w)
-    x0 = dev_logits(w, logits)
-    b0 = torch.from_numpy(bias).to(dev)
-    del logits
-    args = mr.make_route_args(w.T, w.E, w.k, score_fn=w.score_fn, n_group=w.n_group,
-                              topk_group=w.topk_group, group_topn=w.group_topn, renorm=w.renorm,
-                              scale=w.scale, logits_dtype=w.logits_dtype, bias_dtype=w.bias_dtype)
-    o0 = mr.alloc_route_outputs(args, dev, permute=True, tile=w.tile)
-    sb = x0.numel() * x0.element_size() + sum(
-        t.numel() * t.element_size() for t in vars(o0).values() if isinstance(t, torch.Tensor))
-    R = n_sets(sb, rotate_mb)
-    lsets = [(x0 if r == 0 else x0.clone(),
-              o0 if r == 0 else mr.alloc_route_outputs(args, dev, permute=True, tile=w.tile))
-             for r in range(R)]
+    if want("deepseek_v3_like_T262144"):
+        # the headline method at 16x the tokens (T = 262144, 134 MB of logits): how
+        # close the same kernels come to the HBM roofline once a launch is long
+        # enough to hide its cold reads and its drain
+        w = with_overrides(WORKLOADS["deepseek_v3_like"], T=262144)
+        logits, bias = route_inputs(w)
+        x0 = dev_logits(w, logits)
+        b0 = torch.from_numpy(bias).to(dev)
+        del logits
+        args = mr.make_route_args(w.T, w.E, w.k, score_fn=w.score_fn, n_group=w.n_group,
+                                  topk_group=w.topk_group, group_topn=w.group_topn, renorm=w.renorm,
+                                  scale=w.scale, logits_dtype=w.logits_dtype, bias_dtype=w.bias_dtype)
+        o0 = mr.alloc_route_outputs(args, dev, permute=True, tile=w.tile)
+        sb = x0.numel() * x0.element_size() + sum(
+            t.numel() * t.element_size() for t in vars(o0).values() if isinstance(t, torch.Tensor))
+        R = n_sets(sb, rotate_mb)
+        lsets = [(x0 if r == 0 else x0.clone(),
+                  o0 if r == 0 else mr.alloc_route_outputs(args, dev, permute=True, tile=w.tile))
+                 for r in range(R)]
 
-    def lstep(i):
-        mr.route_permute(args, lsets[i % R][0], b0, tile=w.tile, out=lsets[i % R][1])
+        def lstep(i):
+            mr.route_permute(args, lsets[i % R][0], b0, tile=w.tile, out=lsets[i % R][1])
 
-    ms = graph_ms(torch, lstep, K)
-    torch.cuda._sleep(int(2.4e9 * 0.05))      # queued work ahead of the stamped launches
-    mr.moe_profile_begin()
-    for i in range(min(K, 50)):
-        lstep(i)
-    mr.moe_profile_end()
-    torch.cuda.synchronize()
-    rms, rn = mr.moe_profile_read(mr.MOE_KERNEL_ROUTE)
-    route_us = rms / rn * 1000.0 if rn else None
-    route_b = w.T * w.E * 2 + w.E * 4 + 2 * w.T * w.k * 4
-    total = int(o0.total_num_padded_tokens.item())
-    ntiles = int(o0.num_non_exiting_ctas.item())
-    nbytes = route_permute_bytes(w, w.T, total, ntiles)
-    res["deepseek_v3_like_T262144"] = {
-        "workload": w.description.replace("T=16384", "T=262144"),
-        "us_per_call": ms * 1e3, "tokens_per_s": w.T / (ms * 1e-3), "algorithmic_bytes": nbytes,
-        "gbs": nbytes / (ms * 1e-3) / 1e9, "buffer_sets": R,
-        "route_kernel_us": route_us, "route_kernel_algorithmic_bytes": route_b,
-        "route_kernel_gbs": route_b / (route_us * 1e-6) / 1e9 if route_us else None,
-        "route_kernel_frac_of_peak": route_b / (route_us * 1e-6) / 1e9 / HBM_PEAK_GBS if route_us else None}
-    del lsets, x0, o0
+        ms = graph_ms(torch, lstep, K)
+        torch.cuda._sleep(int(2.4e9 * 0.05))      # queued work ahead of the stamped launches
+        mr.moe_profile_begin()
+        for i in range(min(K, 50)):
+            lstep(i)
+        mr.moe_profile_end()
+        torch.cuda.synchronize()
+        rms, rn = mr.moe_profile_read(mr.MOE_KERNEL_ROUTE)
+        route_us = rms / rn * 1000.0 if rn else None
+        route_b = w.T * w.E * 2 + w.E * 4 + 2 * w.T * w.k * 4
+        total = int(o0.total_num_padded_tokens.item())
+        ntiles = int(o0.num_non_exiting_ctas.item())
+        nbytes = route_permute_bytes(w, w.T, total, ntiles)
+        res["deepseek_v3_like_T262144"] = {
+            "workload": w.description.replace("T=16384", "T=262144"),
+            "us_per_call": ms * 1e3, "tokens_per_s": w.T / (ms * 1e-3), "algorithmic_bytes": nbytes,
+            "gbs": nbytes / (ms * 1e-3) / 1e9, "buffer_sets": R,
+            "route_kernel_us": route_us, "route_kernel_algorithmic_bytes": route_b,
+            "route_kernel_gbs": route_b / (route_us * 1e-6) / 1e9 if route_us else None,
+            "route_kernel_frac_of_peak": route_b / (route_us * 1e-6) / 1e9 / HBM_PEAK_GBS if route_us else None}
+        del lsets, x0, o0
 
-    # the headline method with bfloat16 routing weights (FlashInfer's
-    # topk_weights dtype): the same step, 2-byte weights
-    w = WORKLOADS["deepseek_v3_like"]
-    logits, bias = route_inputs(w)
-    x0 = dev_logits(w, logits)
-    b0 = torch.from_numpy(bias).to(dev)
-    args = mr.make_route_args(w.T, w.E, w.k, score_fn=w.score_fn, n_group=w.n_group,
-                              topk_group=w.topk_group, group_topn=w.group_topn, renorm=w.renorm,
-                              scale=w.scale, logits_dtype=w.logits_dtype, bias_dtype=w.bias_dtype,
-                              weights_dtype="bf16")
-    o0 = mr.alloc_route_outputs(args, dev, permute=True, tile=w.tile)
-    sb = x0.numel() * x0.element_size() + sum(
-        t.numel() * t.element_size() for t in vars(o0).values() if isinstance(t, torch.Tensor))
-    R = n_sets(sb, rotate_mb)
-    hsets = [(x0 if r == 0 else x0.clone(),
-              o0 if r == 0 else mr.alloc_route_outputs(args, dev, permute=True, tile=w.tile))
-             for r in range(R)]
-    ms = graph_ms(torch, lambda i: mr.route_permute(args, hsets[i % R][0], b0, tile=w.tile,
-                                                    out=hsets[i % R][1]), K)
-    total = int(o0.total_num_padded_tokens.item())
-    ntiles = int(o0.num_non_exiting_ctas.item())
-    nbytes = route_permute_bytes(w, w.T, total, ntiles) - w.T * w.k * 2
-    res["deepseek_v3_like_bf16_weights"] = {
-        "workload": w.description + "; bf16 topk_weights",
-        "us_per_call": ms * 1e3, "tokens_per_s": w.T / (ms * 1e-3), "algorithmic_bytes": nbytes,
-        "gbs": nbytes / (ms * 1e-3) / 1e9, "buffer_sets": R}
-    del hsets, x0, o0
+    if want("deepseek_v3_like_bf16_weights"):
+        # the headline method with bfloat16 routing weights (FlashInfer's
+        # topk_weights dtype): the same step, 2-byte weights
+        w = WORKLOADS["deepseek_v3_like"]
+        logits, bias = route_inputs(w)
+        x0 = dev_logits(w, logits)
+        b0 = torch.from_numpy(bias).to(dev)
+        args = mr.make_route_args(w.T, w.E, w.k, score_fn=w.score_fn, n_group=w.n_group,
+                                  topk_group=w.topk_group, group_topn=w.group_topn, renorm=w.renorm,
+                                  scale=w.scale, logits_dtype=w.logits_dtype, bias_dtype=w.bias_dtype,
+                                  weights_dtype="bf16")
+        o0 = mr.alloc_route_outputs(args, dev, permute=True, tile=w.tile)
+        sb = x0.numel() * x0.element_size() + sum(
+            t.numel() * t.element_size() for t in vars(o0).values() if isinstance(t, torch.Tensor))
+        R = n_sets(sb, rotate_mb)
+        hsets = [(x0 if r == 0 else x0.clone(),
+                  o0 if r == 0 else mr.alloc_route_outputs(args, dev, permute=True, tile=w.tile))
+                 for r in range(R)]
+        ms = graph_ms(torch, lambda i: mr.route_permute(args, hsets[i % R][0], b0, tile=w.tile,
+                                                        out=hsets[i % R][1]), K)
+        total = int(o0.total_num_padded_tokens.item())
+        ntiles = int(o0.num_non_exiting_ctas.item())
+        nbytes = route_permute_bytes(w, w.T, total, ntiles) - w.T * w.k * 2
+        res["deepseek_v3_like_bf16_weights"] = {
+            "workload": w.description + "; bf16 topk_weights",
+            "us_per_call": ms * 1e3, "tokens_per_s": w.T / (ms * 1e-3), "algorithmic_bytes": nbytes,
+            "gbs": nbytes / (ms * 1e-3) / 1e9, "buffer_sets": R}
+        del hsets, x0, o0
 
-    # token dispatch and combine around the expert GEMM, DeepSeek-V3-like route
-    # at the front end's hidden size (7168, bf16), rows of synthetic N(0,1)
-    w = WORKLOADS["deepseek_v3_like"]
-    logits, bias = route_inputs(w)
-    x0 = dev_logits(w, logits)
-    b0 = torch.from_numpy(bias).to(dev)
-    args = mr.make_route_args(w.T, w.E, w.k, score_fn=w.score_fn, n_group=w.n_group,
-                              topk_group=w.topk_group, group_topn=w.group_topn, renorm=w.renorm,
-                              scale=w.scale, logits_dtype=w.logits_dtype, bias_dtype=w.bias_dtype)
-    o = mr.alloc_route_outputs(args, dev, permute=True, tile=w.tile)
-    mr.route_permute(args, x0, b0, tile=w.tile, out=o)
-    torch.cuda.synchronize()
-    H = FRONT_END.H
-    total = int(o.total_num_padded_tokens.item())
-    max_rows = o.permuted_idx_to_token_idx.numel()
-    gen = torch.Generator(device="cpu").manual_seed(w.seed + 2)
-    hid0 = torch.randn((w.T, H), generator=gen).to(torch.bfloat16).to(dev)
-    d_bytes = total * H * 2 + w.T * w.k * H * 2 + total * 4          # rows written + read, p2t
-    c_bytes = w.T * w.k * H * 2 + w.T * H * 2 + w.T * w.k * 8        # rows read + written, maps
-    R = n_sets(max_rows * H * 2 + w.T * H * 2, rotate_mb)
-    dsets = [(hid0 if r == 0 else hid0.clone(),
-              torch.empty((max_rows, H), dtype=torch.bfloat16, device=dev)) for r in range(R)]
-    ms_d = graph_ms(torch, lambda i: mr.moe_dispatch(
-        dsets[i % R][0], mr.MOE_BF16, w.T, H, o.permuted_idx_to_token_idx,
-        o.total_num_padded_tokens, max_rows, dsets[i % R][1]), K)
-    csets = [(ds[1], torch.empty((w.T, H), dtype=torch.bfloat16, device=dev)) for ds in dsets]
-    ms_c = graph_ms(torch, lambda i: mr.moe_combine(
-        csets[i % R][0], mr.MOE_BF16, w.T, H, w.k, o.expanded_idx_to_permuted_idx, o.topk_weights,
-        mr.MOE_F32, csets[i % R][1]), K)
-    res["deepseek_v3_like_dispatch"] = {
-        "workload": f"{w.description}; hidden [{w.T},{H}] bf16 rows into {total} permuted rows",
-        "us_per_call": ms_d * 1e3, "algorithmic_bytes": d_bytes, "gbs": d_bytes / (ms_d * 1e-3) / 1e9,
-        "buffer_sets": R}
-    res["deepseek_v3_like_combine"] = {
-        "workload": f"{w.description}; {w.k} weighted expert rows per token back to [{w.T},{H}] bf16",
-        "us_per_call": ms_c * 1e3, "algorithmic_bytes": c_bytes, "gbs": c_bytes / (ms_c * 1e-3) / 1e9,
-        "buffer_sets": R}
-    del dsets, csets, o
+    if want("deepseek_v3_like_dispatch") or want("deepseek_v3_like_combine"):
+        # token dispatch and combine around the expert GEMM, DeepSeek-V3-like route
+        # at the front end's hidden size (7168, bf16), rows of synthetic N(0,1)
+        w = WORKLOADS["deepseek_v3_like"]
+        logits, bias = route_inputs(w)
+        x0 = dev_logits(w, logits)
+        b0 = torch.from_numpy(bias).to(dev)
+        args = mr.make_route_args(w.T, w.E, w.k, score_fn=w.score_fn, n_group=w.n_group,
+                                  topk_group=w.topk_group, group_topn=w.group_topn, renorm=w.renorm,
+                                  scale=w.scale, logits_dtype=w.logits_dtype, bias_dtype=w.bias_dtype)
+        o = mr.alloc_route_outputs(args, dev, permute=True, tile=w.tile)
+        mr.route_permute(args, x0, b0, tile=w.tile, out=o)
+        torch.cuda.synchronize()
+        H = FRONT_END.H
+        total = int(o.total_num_padded_tokens.item())
+        max_rows = o.permuted_idx_to_token_idx.numel()
+        gen = torch.Generator(device="cpu").manual_seed(w.seed + 2)
+        hid0 = torch.randn((w.T, H), generator=gen).to(torch.bfloat16).to(dev)
+        d_bytes = total * H * 2 + w.T * w.k * H * 2 + total * 4          # rows written + read, p2t
+        c_bytes = w.T * w.k * H * 2 + w.T * H * 2 + w.T * w.k * 8        # rows read + written, maps
+        R = n_sets(max_rows * H * 2 + w.T * H * 2, rotate_mb)
+        dsets = [(hid0 if r == 0 else hid0.clone(),
+                  torch.empty((max_rows, H), dtype=torch.bfloat16, device=dev)) for r in range(R)]
+        ms_d = graph_ms(torch, lambda i: mr.moe_dispatch(
+            dsets[i % R][0], mr.MOE_BF16, w.T, H, o.permuted_idx_to_token_idx,
+            o.total_num_padded_tokens, max_rows, dsets[i % R][1]), K)
+        csets = [(ds[1], torch.empty((w.T, H), dtype=torch.bfloat16, device=dev)) for ds in dsets]
+        ms_c = graph_ms(torch, lambda i: mr.moe_combine(
+            csets[i % R][0], mr.MOE_BF16, w.T, H, w.k, o.expanded_idx_to_permuted_idx, o.topk_weights,
+            mr.MOE_F32, csets[i % R][1]), K)
+        res["deepseek_v3_like_dispatch"] = {
+            "workload": f"{w.description}; hidden [{w.T},{H}] bf16 rows into {total} permuted rows",
+            "us_per_call": ms_d * 1e3, "algorithmic_bytes": d_bytes, "gbs": d_bytes / (ms_d * 1e-3) / 1e9,
+            "buffer_sets": R}
+        res["deepseek_v3_like_combine"] = {
+            "workload": f"{w.description}; {w.k} weighted expert rows per token back to [{w.T},{H}] bf16",
+            "us_per_call": ms_c * 1e3, "algorithmic_bytes": c_bytes, "gbs": c_bytes / (ms_c * 1e-3) / 1e9,
+            "buffer_sets": R}
+        del dsets, csets, o
 
-    res["decode_front_end"] = front_end_bench(mr, torch, np, dev, rotate_mb, K, cpu_seconds)
+    if want("decode_front_end"):
+        res["decode_front_end"] = front_end_bench(mr, torch, np, dev, rotate_mb, K, cpu_seconds)
     return res
 
 
@@ -627,7 +642,8 @@ def main():
     others = None
     if not a.no_other_configs and a.workload == "deepseek_v3_like":
         others = other_configs(mr, torch, np, dev, a.rotate_mb, min(K, 50),
-                               cpu_seconds=None if a.no_cpu_baseline else a.cpu_seconds_other)
+                               cpu_seconds=None if a.no_cpu_baseline else a.cpu_seconds_other,
+                               only=None if a.only_other is None else set(a.only_other.split(",")))
 
     cpu = None
     near = None
