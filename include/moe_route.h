@@ -278,7 +278,9 @@ size_t moe_route_permute_noalloc_max_scratch_bytes(void);
  * through the workspace; that block's wait is bounded, and one that runs out
  * (no block that was dispatched before it finished within seconds: not seen
  * in practice) writes *loss as the float32 NaN with bits 0x7FC0A0A0 and leaves
- * the workspace dirty: zero it again before the next forward.  A dirty slot
+ * the workspace dirty: zero it again before the next forward.  (The
+ * environment variable MOE_ROUTE_AUX_SPIN_LIMIT, an integer no larger than the
+ * default, lowers the limit on each call; 0 forces the give-up, for tests.)  A dirty slot
  * (non-zero on entry) is taken for a published partial: the forward that
  * reads it gives a wrong loss and returns it to zero. */
 moe_status moe_aux_loss(const float* probs, const int32_t* tokens_per_expert, int64_t rows,
@@ -393,7 +395,9 @@ moe_status moe_combine(const void* expert_out, int32_t dtype, int32_t T, int32_t
  * call.  A region that was not zero on entry: a dirty failure word is
  * ignored (each call clears it first); a dirty normalisation-scale slot of a
  * token t < T gives that call wrong ids and affinities, and the call returns
- * the slot to zero. */
+ * the slot to zero.  (The environment variable MOE_ROUTE_FRONT_END_SPIN_LIMIT,
+ * an integer no larger than the default, lowers the limit on each call; 0
+ * forces the give-up, for tests.) */
 moe_status rmsnorm_gate_route(const void* hidden, const void* gamma, const void* router_weights,
                               const void* router_bias, int32_t dtype, int32_t T, int32_t H,
                               int32_t E, float eps, int32_t top_k, int32_t act_fn, void* normed,

@@ -240,3 +240,30 @@ def test_aux_dirty_slots_are_repaired():
         torch.cuda.synchronize()
         assert abs(loss.item() - ref) <= 1e-5 * abs(ref), i
         assert int(torch.count_nonzero(ws[:nb * 8])) == 0
+
+
+def test_aux_forced_give_up(monkeypatch):
+    # the summing block's wait forced to give up at once: the loss is the
+    # documented timeout NaN, the workspace is left dirty, and after zeroing it
+    # the next forward is exact
+    rows, E, k = 30000, 128, 8
+    rng = np.random.default_rng(505)
+    probs = rng.random((rows, E), dtype=np.float32)
+    counts = rng.integers(0, 3000, E).astype(np.int32)
+    p = torch.from_numpy(probs).to(DEV)
+    c = torch.from_numpy(counts).to(DEV)
+    ws = torch.zeros(mr.moe_aux_loss_workspace_size(rows, E), dtype=torch.uint8, device=DEV)
+    loss = torch.empty(1, dtype=torch.float32, device=DEV)
+    monkeypatch.setenv("MOE_ROUTE_AUX_SPIN_LIMIT", "0")
+    log("[gpu] aux forward, forced give-up")
+    mr.moe_aux_loss(p, c, rows, rows, E, k, 1e-2, loss=loss, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(loss.view(torch.int32).item()) & 0xFFFFFFFF == 0x7FC0A0A0
+    assert int(torch.count_nonzero(ws)) > 0                   # the partials stay behind
+    monkeypatch.delenv("MOE_ROUTE_AUX_SPIN_LIMIT")
+    ws.zero_()
+    mr.moe_aux_loss(p, c, rows, rows, E, k, 1e-2, loss=loss, workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle.aux_loss_fwd(probs, counts, rows, E, k, 1e-2)
+    assert abs(loss.item() - ref) <= 1e-5 * abs(ref)
+    assert int(torch.count_nonzero(ws)) == 0

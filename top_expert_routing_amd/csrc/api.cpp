@@ -246,15 +246,23 @@ int32_t* ws_count_rows(void* ws) { return static_cast<int32_t*>(ws); }
 // Polls before a front-end wait gives up.  MOE_ROUTE_FRONT_END_SPIN_LIMIT (an
 // integer in [0, the default]) lowers it, read on every call: a limit of 0
 // makes every wait give up at once, which exercises the give-up path (-1 ids,
-// the failure count) with every kernel still ending normally.
-int front_end_spin_limit() {
-  const char* v = std::getenv("MOE_ROUTE_FRONT_END_SPIN_LIMIT");
-  if (v == nullptr || *v == '\0') return moe::kFrontEndSpinLimit;
+// the failure count) with every kernel still ending normally.  Values outside
+// [0, the default] leave the default.
+int spin_limit_from_env(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  if (v == nullptr || *v == '\0') return dflt;
   char* end = nullptr;
   const long n = std::strtol(v, &end, 10);
-  if (*end != '\0' || n < 0 || n > moe::kFrontEndSpinLimit) return moe::kFrontEndSpinLimit;
+  if (*end != '\0' || n < 0 || n > dflt) return dflt;
   return (int)n;
 }
+int front_end_spin_limit() {
+  return spin_limit_from_env("MOE_ROUTE_FRONT_END_SPIN_LIMIT", moe::kFrontEndSpinLimit);
+}
+// The same for the aux-loss forward's final wait (MOE_ROUTE_AUX_SPIN_LIMIT):
+// a limit of 0 makes the summing block give up at once (the loss is the
+// timeout NaN; the workspace is left dirty).
+int aux_spin_limit() { return spin_limit_from_env("MOE_ROUTE_AUX_SPIN_LIMIT", moe::kAuxSpinLimit); }
 
 uint32_t* ws_count_hdr(void* ws) {
   return reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + 2 * kCountRowsBytes);
@@ -714,7 +722,7 @@ moe_status moe_aux_loss(const float* probs, const int32_t* tokens_per_expert, in
     const int nb = moe::aux_fwd_blocks(rows, E);
     hipError_t e = launch_with_profile(MOE_KERNEL_AUX_FWD, stream, [&] {
       return moe::launch_aux_fwd(probs, tokens_per_expert, rows, E, scale, workspace, nb, loss,
-                                 stream);
+                                 aux_spin_limit(), stream);
     });
     if (e != hipSuccess) return hip_fail(e, "aux forward launch");
   }

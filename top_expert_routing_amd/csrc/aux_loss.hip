@@ -23,8 +23,8 @@
 // device-scope loads (coherent across the XCDs' L2 caches) until none is
 // zero, then returns them to zero.  Only the summing block waits, and every
 // block it waits for was dispatched before it and never waits, so every wait
-// ends; the poll is still bounded, and one that runs out writes the loss as
-// kAuxTimeoutNaN and leaves the slots as they are.
+// ends; the poll is still bounded (kAuxSpinLimit polls), and one that runs out
+// writes the loss as kAuxTimeoutNaN and leaves the slots as they are.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -43,7 +43,6 @@ constexpr int kAuxMaxE = 2048;
 // and two rounds.
 constexpr int kAuxUnroll = 4;
 constexpr int kAuxMaxRun = kAuxMaxBlocks / kAuxBlock;   // slots per summing thread
-constexpr int kAuxSpinLimit = 1 << 22;   // polls before the summing block gives up
 static_assert(kAuxMaxBlocks * 8 <= kAuxSyncBytes, "partial slots exceed the sync region");
 }
 
@@ -56,7 +55,7 @@ __device__ __forceinline__ unsigned long long encode_partial(double s) {
 __global__ void __launch_bounds__(kAuxBlock)
     aux_fwd_kernel(const float* __restrict__ probs, const int32_t* __restrict__ counts,
                    int64_t rows, int E, int64_t rows_per_block, int vec, double scale,
-                   unsigned long long* __restrict__ slots, float* __restrict__ loss) {
+                   unsigned long long* __restrict__ slots, float* __restrict__ loss, int spin_limit) {
   static_assert(kAuxBlock == 256, "the final sum assumes four wavefronts");
   __shared__ __align__(16) float cs[kAuxMaxE];
   __shared__ float red[kAuxBlock / 64];
@@ -129,7 +128,7 @@ __global__ void __launch_bounds__(kAuxBlock)
   const int n_mine = max(0, min(per, nb - 1 - lo));   // slot nb - 1 is `own`
   unsigned long long v[kAuxMaxRun] = {};
   bool ready = n_mine == 0;
-  for (int spin = 0; !ready && spin < kAuxSpinLimit; ++spin) {
+  for (int spin = 0; !ready && spin < spin_limit; ++spin) {
 #pragma unroll
     for (int u = 0; u < kAuxMaxRun; ++u)
       v[u] = __hip_atomic_load(slots + min(lo + u, nb - 1), __ATOMIC_RELAXED,
@@ -204,12 +203,13 @@ int aux_fwd_blocks(int64_t rows, int E) {
 }
 
 hipError_t launch_aux_fwd(const float* probs, const int32_t* counts, int64_t rows, int E,
-                          double scale, void* sync, int nb, float* loss, hipStream_t s) {
+                          double scale, void* sync, int nb, float* loss, int spin_limit,
+                          hipStream_t s) {
   const int64_t rpb = (rows + nb - 1) / nb;
   const int vec = (E % 4 == 0) && ((uintptr_t)probs % 16 == 0);
   MOE_LAUNCH(aux_fwd_kernel, dim3(nb), dim3(kAuxBlock), 0, s, probs, counts, rows, E,
              rpb < 1 ? (int64_t)1 : rpb, vec, scale, static_cast<unsigned long long*>(sync),
-             loss);
+             loss, spin_limit);
   return hipGetLastError();
 }
 

@@ -224,9 +224,11 @@ hipError_t launch_front_end(const FrontEndParams& q, hipStream_t s);
 constexpr int kAuxMaxBlocks = 2048;
 constexpr int kAuxSyncBytes = kAuxMaxBlocks * 8;
 constexpr uint32_t kAuxTimeoutNaN = 0x7fc0a0a0u;
+constexpr int kAuxSpinLimit = 1 << 22;   // polls before the summing block gives up
 int aux_fwd_blocks(int64_t rows, int E);
 hipError_t launch_aux_fwd(const float* probs, const int32_t* counts, int64_t rows, int E,
-                          double scale, void* sync, int nb, float* loss, hipStream_t s);
+                          double scale, void* sync, int nb, float* loss, int spin_limit,
+                          hipStream_t s);
 hipError_t launch_aux_bwd(const int32_t* counts, int64_t rows, int E, double scale,
                           const float* grad_loss, float* grad, hipStream_t s);
 
