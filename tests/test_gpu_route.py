@@ -99,18 +99,21 @@ def test_deepseek_like_large_T():
     run_and_check(w, logits, bias, "deepseek_v3_like T=262144")
 
 
-@pytest.mark.parametrize("name,T", [
-    ("qwen_moe_like", 65536 + 5),            # 1025 route blocks, two per scatter block
-    ("deepseek_v3_like", 131072 + 128 + 3),  # 2051 route blocks, four per scatter block
-    ("mixtral_like", 2048 * 64 + 64 * 2 + 7),
-    ("deepseek_v3_like", 1024 * 64 - 1),     # 1024 blocks, the last one ragged
+@pytest.mark.parametrize("name,T,off,n_loc,tile", [
+    ("qwen_moe_like", 65536 + 5, 0, None, None),            # 1025 route blocks, two per scatter block
+    ("deepseek_v3_like", 131072 + 128 + 3, 0, None, None),  # 2051 route blocks, four per scatter block
+    ("mixtral_like", 2048 * 64 + 64 * 2 + 7, 0, None, None),
+    ("deepseek_v3_like", 1024 * 64 - 1, 0, None, None),     # 1024 blocks, the last one ragged
+    ("qwen_moe_like", 65536 + 5, 32, 64, 1),                # a local-expert shard, tile 1
+    ("deepseek_v3_like", 131072 + 128 + 3, 64, 128, 256),   # a shard, large tiles
 ])
-def test_scatter_blocks_sharing_route_blocks(name, T):
+def test_scatter_blocks_sharing_route_blocks(name, T, off, n_loc, tile):
     # large T: one scatter block serves two or four route blocks; the last
     # scatter block holds fewer of them, and the last route block fewer tokens
     w = WORKLOADS[name]
     logits, bias = route_inputs(w, T=T, seed=T % 1000)
-    run_and_check(w, logits, bias, f"{name} T={T}")
+    run_and_check(w, logits, bias, f"{name} T={T} local {off}+{n_loc} tile {tile}", tile=tile,
+                  off=off, n_loc=n_loc)
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
