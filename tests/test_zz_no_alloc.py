@@ -51,7 +51,8 @@ def test_noalloc_oversize_refused_on_host():
 def test_noalloc_matches_workspace_entry_point():
     calls = [(WORKLOADS["deepseek_v3_like"], 16384),
              (WORKLOADS["deepseek_v3_like"], 4097),
-             (WORKLOADS["qwen_moe_like"], 1000)]
+             (WORKLOADS["qwen_moe_like"], 1000),
+             (WORKLOADS["qwen_moe_like"], 65536 + 5)]   # scatter blocks of two route blocks
     for i, (w, T) in enumerate(calls):
         label = f"noalloc call {i}: {w.name} T={T}"
         log(f"[gpu] {label}")
