@@ -116,6 +116,18 @@ def n_sets(set_bytes, rotate_mb):
     return max(2, min(256, math.ceil(max(rotate_mb * 2 ** 20, 2 * MALL_BYTES + 1) / set_bytes)))
 
 
+def plain_op_entry(torch, rotate_mb, K, desc, nbytes, make, op):
+    """A plain PyTorch kernel that moves about the same HBM bytes as a streaming
+    row, timed in the same harness (cold rotating sets, one HIP graph): what a
+    generic device kernel reaches at this size, beside the row's own kernel."""
+    R = n_sets(nbytes, rotate_mb)
+    sets = [make() for _ in range(R)]
+    ms = graph_ms(torch, lambda i: op(*sets[i % R]), K)
+    del sets
+    return {"op": desc, "us_per_call": ms * 1e3, "bytes": nbytes, "gbs": nbytes / (ms * 1e-3) / 1e9,
+            "buffer_sets": R}
+
+
 def route_permute_bytes(w, T, total, ntiles):
     lsz = 2 if w.logits_dtype == "bf16" else 4
     return (T * w.E * lsz + (w.E * 4 if w.has_bias else 0) + 3 * T * w.k * 4 + total * 4 +
@@ -189,9 +201,20 @@ def other_configs(mr, torch, np, dev, rotate_mb, K, cpu_seconds=None, only=None)
             bwd = graph_ms(torch, lambda i: mr.moe_aux_loss(None, counts, w.T, w.T, w.E, w.k,
                                                             w.aux_coeff, grad_probs=grads[i % R]), K)
             ab = w.T * w.E * 4 + w.E * 4
-            entry["aux_forward"] = {"us_per_call": fwd * 1e3, "gbs": ab / (fwd * 1e-3) / 1e9}
-            entry["aux_backward"] = {"us_per_call": bwd * 1e3, "gbs": ab / (bwd * 1e-3) / 1e9}
             del grads, probs
+            shape = (w.T, w.E)
+            entry["aux_forward"] = {
+                "us_per_call": fwd * 1e3, "gbs": ab / (fwd * 1e-3) / 1e9,
+                "plain_torch_op": plain_op_entry(
+                    torch, rotate_mb, K, "row maximum of a [T,E] f32 tensor (amax over E)",
+                    w.T * w.E * 4 + w.T * 4,
+                    lambda: (torch.randn(shape, device=dev), torch.empty(w.T, device=dev)),
+                    lambda p, m: torch.amax(p, dim=1, out=m))}
+            entry["aux_backward"] = {
+                "us_per_call": bwd * 1e3, "gbs": ab / (bwd * 1e-3) / 1e9,
+                "plain_torch_op": plain_op_entry(
+                    torch, rotate_mb, K, "fill of a [T,E] f32 tensor", w.T * w.E * 4,
+                    lambda: (torch.empty(shape, device=dev),), lambda g: g.fill_(0.5))}
         if cpu_seconds:
             entry["near_ties"] = near_tie_entry(w, logits, bias, o0.topk_ids.cpu().numpy())
             entry["cpu_baseline"] = cpu_baseline_entry(w, cpu_seconds, max_T=8192)
@@ -218,12 +241,23 @@ def other_configs(mr, torch, np, dev, rotate_mb, K, cpu_seconds=None, only=None)
         bsets = [(x0.clone(), ids0.clone(), gw0.clone(), None if gs0 is None else gs0.clone(),
                   torch.empty((w.T, w.E), dtype=torch.float32, device=dev)) for _ in range(R)]
         ms = graph_ms(torch, lambda i: mr.moe_route_backward(args, *bsets[i % R]), K)
+        del bsets
+        shape = (w.T, w.E)
+        if with_s:
+            plain = plain_op_entry(
+                torch, rotate_mb, K, "f32 [T,E] + bf16 [T,E] -> f32 [T,E] (torch.add)",
+                w.T * w.E * 10,
+                lambda: (torch.randn(shape, device=dev), x0.clone(), torch.empty(shape, device=dev)),
+                lambda a, b, c: torch.add(a, b, out=c))
+        else:
+            plain = plain_op_entry(
+                torch, rotate_mb, K, "bf16 [T,E] -> f32 [T,E] (copy_)", w.T * w.E * 6,
+                lambda: (x0.clone(), torch.empty(shape, device=dev)), lambda a, b: b.copy_(a))
         res[name + "_backward"] = {
             "workload": w.description + ("; grad of weights and scores" if with_s else
                                          "; grad of weights") + " -> grad of logits",
             "us_per_call": ms * 1e3, "algorithmic_bytes": set_b,
-            "gbs": set_b / (ms * 1e-3) / 1e9, "buffer_sets": R}
-        del bsets
+            "gbs": set_b / (ms * 1e-3) / 1e9, "buffer_sets": R, "plain_torch_op": plain}
 
     if want("deepseek_v3_like_dense_outputs"):
         # dense [T, E] probs + routing map from the DeepSeek-V3-like top-k outputs
@@ -237,11 +271,15 @@ def other_configs(mr, torch, np, dev, rotate_mb, K, cpu_seconds=None, only=None)
                   torch.empty((w.T, w.E), dtype=torch.uint8, device=dev)) for _ in range(R)]
         ms_x = graph_ms(torch, lambda i: mr.moe_topk_to_dense(w.T, w.E, w.k, xsets[i % R][0], xsets[i % R][1],
                                                               mr.MOE_F32, xsets[i % R][2], xsets[i % R][3]), K)
+        del xsets
         res["deepseek_v3_like_dense_outputs"] = {
             "workload": f"{w.description}; top-k ids/weights -> dense probs [T,E] f32 + routing map [T,E] u8",
             "us_per_call": ms_x * 1e3, "algorithmic_bytes": x_bytes, "gbs": x_bytes / (ms_x * 1e-3) / 1e9,
-            "buffer_sets": R}
-        del xsets
+            "buffer_sets": R,
+            "plain_torch_op": plain_op_entry(
+                torch, rotate_mb, K, "fill of a u8 tensor of T*E*5 bytes", w.T * w.E * 5,
+                lambda: (torch.empty(w.T * w.E * 5, dtype=torch.uint8, device=dev),),
+                lambda b: b.fill_(1))}
 
     if want("deepseek_v3_like_T262144"):
         # the headline method at 16x the tokens (T = 262144, 134 MB of logits): how
@@ -347,15 +385,26 @@ def other_configs(mr, torch, np, dev, rotate_mb, K, cpu_seconds=None, only=None)
         ms_c = graph_ms(torch, lambda i: mr.moe_combine(
             csets[i % R][0], mr.MOE_BF16, w.T, H, w.k, o.expanded_idx_to_permuted_idx, o.topk_weights,
             mr.MOE_F32, csets[i % R][1]), K)
+        del dsets, csets, o
         res["deepseek_v3_like_dispatch"] = {
             "workload": f"{w.description}; hidden [{w.T},{H}] bf16 rows into {total} permuted rows",
             "us_per_call": ms_d * 1e3, "algorithmic_bytes": d_bytes, "gbs": d_bytes / (ms_d * 1e-3) / 1e9,
-            "buffer_sets": R}
+            "buffer_sets": R,
+            "plain_torch_op": plain_op_entry(
+                torch, rotate_mb, K, f"copy of a [{total},{H}] bf16 tensor (copy_)", total * H * 4,
+                lambda: (torch.empty((total, H), dtype=torch.bfloat16, device=dev),
+                         torch.empty((total, H), dtype=torch.bfloat16, device=dev)),
+                lambda a, b: b.copy_(a))}
         res["deepseek_v3_like_combine"] = {
             "workload": f"{w.description}; {w.k} weighted expert rows per token back to [{w.T},{H}] bf16",
             "us_per_call": ms_c * 1e3, "algorithmic_bytes": c_bytes, "gbs": c_bytes / (ms_c * 1e-3) / 1e9,
-            "buffer_sets": R}
-        del dsets, csets, o
+            "buffer_sets": R,
+            "plain_torch_op": plain_op_entry(
+                torch, rotate_mb, K, f"sum over k of a [{w.T},{w.k},{H}] bf16 tensor (torch.sum)",
+                w.T * w.k * H * 2 + w.T * H * 2,
+                lambda: (torch.empty((w.T, w.k, H), dtype=torch.bfloat16, device=dev),
+                         torch.empty((w.T, H), dtype=torch.bfloat16, device=dev)),
+                lambda a, b: torch.sum(a, dim=1, out=b))}
 
     if want("decode_front_end"):
         res["decode_front_end"] = front_end_bench(mr, torch, np, dev, rotate_mb, K, cpu_seconds)
