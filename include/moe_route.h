@@ -109,6 +109,10 @@ typedef enum moe_score_fn { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score_fn;
  * group_score_topn  a group's score is the sum of its group_score_topn largest
  *                   selection keys (2 for DeepSeek-V3-style routing);
  *                   1 <= group_score_topn <= E / n_group when grouping is on.
+ *                   Implemented (else MOE_EUNSUPPORTED): group_score_topn
+ *                   <= 2, and a group size E / n_group equal to w times a
+ *                   power of two for some w in {4, 8, 16, 32} with
+ *                   E <= 64 w (a group spans whole kernel lanes of w experts).
  * renormalize       1 = divide the chosen weights by their sum
  *                   ([FI] norm_topk_prob; [MAX] norm_topk_prob; [LMD]
  *                   norm_topk).  No effect for post-softmax, whose weights
