@@ -68,6 +68,8 @@ BAD_ROUTE = [
     (dict(T=4, E=8, k=2, n_group=2, topk_group=1, group_topn=5), mr.MOE_EINVAL),
     (dict(T=4, E=16, k=2, n_group=2, topk_group=1, group_topn=3), mr.MOE_EUNSUPPORTED),
     (dict(T=4, E=60, k=4, n_group=4, topk_group=2), mr.MOE_EUNSUPPORTED),  # group of 15
+    (dict(T=4, E=96, k=4, n_group=4, topk_group=2), mr.MOE_EUNSUPPORTED),  # group of 24 = 8 x 3
+    (dict(T=4, E=260, k=4, n_group=65, topk_group=8), mr.MOE_EUNSUPPORTED),  # 65 lanes of 4
     (dict(T=4, E=8, k=2, n_group=-1), mr.MOE_EINVAL),
     (dict(T=4, E=8, k=2, scale=float("inf")), mr.MOE_EINVAL),
     (dict(T=4, E=8, k=2, logits_dtype="f16"), mr.MOE_EINVAL),
