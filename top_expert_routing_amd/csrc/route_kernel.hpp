@@ -776,7 +776,11 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>)
           for (int q = lw; q < nval * (E / 4); q += 64) __builtin_nontemporal_store(src[q], out + q);
         }
       } else if (tv) {
-        float* srow = p.scores + (size_t)t * E;
+        // the row offset is formed here again (through an opaque copy of t)
+        // rather than kept from the logit load across the whole token
+        int to = t;
+        asm volatile("" : "+v"(to));
+        float* srow = p.scores + (size_t)to * E;
 #pragma unroll
         for (int i = 0; i < EPL; ++i)
           if (e0 + i < E) srow[e0 + i] = v[i];
