@@ -42,6 +42,19 @@ __device__ __forceinline__ uint64_t pack_key(float key, int idx) {
 }
 __device__ __forceinline__ int unpack_idx(uint64_t p) { return (int)(~(uint32_t)p); }
 
+// The MI355X dispatches the blocks of a 1-D grid to its 8 XCDs round-robin
+// (block b on XCD b % 8), and each XCD has its own L2.  This maps the launch
+// index to a logical block so that every XCD takes one contiguous range of
+// logical blocks (a bijection on [0, nb)): neighbouring logical blocks then
+// share an L2, so lines that consecutive blocks both write (a p2t segment
+// filled in token order) are written back from one XCD, and rows that a range
+// of blocks reads (a counting group) are fetched into one L2.
+__device__ __forceinline__ int xcd_block(int b, int nb) {
+  const int x = b & 7, i = b >> 3;
+  const int per = nb >> 3, extra = nb & 7;
+  return x * per + (x < extra ? x : extra) + i;
+}
+
 // Logistic sigmoid in float32: 1 / (1 + 2^(-x log2 e)) with the hardware
 // exp2 and reciprocal (each about 1 ulp).
 __device__ __forceinline__ float sigmoid_f32(float x) {

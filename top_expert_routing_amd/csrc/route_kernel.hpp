@@ -403,7 +403,7 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>)
   const int cl = tid / LPT;
   const int e0 = lane_c * EPL;
   const int E = p.E, k = p.k;
-  const int blk = blockIdx.x;
+  const int blk = xcd_block((int)blockIdx.x, (int)gridDim.x);   // XCD-contiguous order
   const bool pre = p.pre != 0;
 
   const RouteLds L = route_lds_layout(LPT, RWPL, EPL, p.hmask_len, p.cap, k,

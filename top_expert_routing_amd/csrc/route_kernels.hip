@@ -99,8 +99,8 @@ __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams 
   int* base = po + El + 1;                               // R El
   int* cnt = base + R * El;                              // El
   const int tid = threadIdx.x;
-  const int blk = blockIdx.x;
   const int nb = gridDim.x;
+  const int blk = xcd_block((int)blockIdx.x, nb);     // XCD-contiguous order
   const int tile = p.tile;
   const int k = p.k;
   const int b0 = blk * R;                                // first route block
