@@ -188,6 +188,27 @@ def test_tie_heavy_bf16():
     run_and_check(w2, logits2, np.zeros(w2.E, np.float32), "tie heavy grouped")
 
 
+# Ungrouped calls with 65..128 experts run four lanes of 32 experts per token;
+# their lower bound on the k-th key (3 <= k <= 16) is the k-th largest of the
+# lanes' sixteen top-four keys, found by merging sorted lists across the lanes:
+# k <= 8 keeps the larger eight of the sixteen, k > 8 the smaller eight.  Both
+# halves, padded lanes (E = 100) and ties.
+@pytest.mark.parametrize("k", [3, 7, 8, 9, 13, 16])
+@pytest.mark.parametrize("method", ["softmax_pre", "softmax_post", "sigmoid_bias"])
+@pytest.mark.parametrize("E,dtype", [(128, "bf16"), (100, "f32")])
+def test_four_lane_kth_key_bound(k, method, E, dtype):
+    score_fn = "sigmoid" if method == "sigmoid_bias" else "softmax"
+    w = RouteWorkload(name="four_lane", seed=7300 + 31 * k + E, T=777, E=E, k=k,
+                      score_fn=score_fn, pre_softmax=method == "softmax_pre",
+                      logits_dtype=dtype, logits_std=1.5,
+                      bias_std=0.01 if method == "sigmoid_bias" else None, tile=8)
+    logits, bias = route_inputs(w)
+    run_and_check(w, logits, bias, f"four lanes k={k} {method} E={E}")
+    ties = tie_heavy_logits(777, E, seed=k + E, levels=(-1.0, 0.0, 0.5, 1.0), dtype=dtype)
+    zb = None if bias is None else np.zeros(E, np.float32)
+    run_and_check(w, ties, zb, f"four lanes ties k={k} {method} E={E}")
+
+
 @pytest.mark.parametrize("pre", [False, True])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("E,k", [(8, 2), (32, 1), (64, 4), (128, 8), (256, 8)])

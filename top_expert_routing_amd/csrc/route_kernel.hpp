@@ -591,7 +591,57 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>)
 
     // ---- tau: a lower bound on the k-th eligible key ---------------------------
     float tau;
-    if (kRefineTau && refine) {
+    if (kRefineTau && refine && LPT == 4) {
+      // the k-th largest of the cluster's sixteen top-four keys (a subset of
+      // the keys, so at most the k-th largest key) by two bitonic merges over
+      // quad DPP moves: lanes l and l ^ 1 merge their sorted fours into one
+      // sorted eight, lanes l and l ^ 2 then keep the larger (k <= 8) or the
+      // smaller (k > 8) eight of the sixteen, sorted; every lane of the
+      // cluster ends with the same value
+      auto ce = [](float& hi, float& lo) {
+        const float h = fmaxf(hi, lo), l = fminf(hi, lo);
+        hi = h;
+        lo = l;
+      };
+      const float a4[4] = {m1, m2, m3, m4};
+      float pb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pb[i] = dpp_f<kDppXor1>(a4[i]);
+      float s8[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s8[i] = fmaxf(a4[i], pb[3 - i]);
+        s8[i + 4] = fminf(a4[i], pb[3 - i]);
+      }
+#pragma unroll
+      for (int h = 0; h < 8; h += 4) {
+        ce(s8[h], s8[h + 2]);
+        ce(s8[h + 1], s8[h + 3]);
+        ce(s8[h], s8[h + 1]);
+        ce(s8[h + 2], s8[h + 3]);
+      }
+      float q8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q8[i] = dpp_f<kDppXor2>(s8[i]);
+      float t8[8];
+      const bool upper = k <= 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t8[i] = upper ? fmaxf(s8[i], q8[7 - i]) : fminf(s8[i], q8[7 - i]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ce(t8[i], t8[i + 4]);
+#pragma unroll
+      for (int h = 0; h < 8; h += 4) {
+        ce(t8[h], t8[h + 2]);
+        ce(t8[h + 1], t8[h + 3]);
+        ce(t8[h], t8[h + 1]);
+        ce(t8[h + 2], t8[h + 3]);
+      }
+      const int pos = (upper ? k : k - 8) - 1;
+      tau = t8[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) tau = pos == i ? t8[i] : tau;
+      if (!(tau > -kInf)) tau = kLowest;                  // fewer than k finite keys
+    } else if (kRefineTau && refine) {
       // the k-th largest of the cluster's per-lane top four (a subset of the
       // keys, so at most the k-th largest key): each lane counts the values
       // >= each of its own; the largest own value with count >= k is a bound
