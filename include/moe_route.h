@@ -396,10 +396,12 @@ moe_status moe_combine(const void* expert_out, int32_t dtype, int32_t T, int32_t
  * uint32 failure count at byte offset 4 of the workspace, which the library
  * never clears (read it with a device-to-host copy when -1 ids need an
  * explanation; a caller may reset it); the region is clean again for the next
- * call.  A region that was not zero on entry: a dirty failure word is
- * ignored (each call clears it first); a dirty normalisation-scale slot of a
- * token t < T gives that call wrong ids and affinities, and the call returns
- * the slot to zero.  (The environment variable MOE_ROUTE_FRONT_END_SPIN_LIMIT,
+ * call.  A region that was not zero on entry: a dirty failure word (byte
+ * offset 0) makes that call report a give-up (-1 ids, counted) and is cleared;
+ * the word is never cleared before the projection has run, so that a real
+ * give-up cannot be lost.  A dirty normalisation-scale slot of a token t < T
+ * gives that call wrong ids and affinities, and the call returns the slot to
+ * zero.  (The environment variable MOE_ROUTE_FRONT_END_SPIN_LIMIT,
  * an integer no larger than the default, lowers the limit on each call; 0
  * forces the give-up, for tests.) */
 moe_status rmsnorm_gate_route(const void* hidden, const void* gamma, const void* router_weights,

@@ -206,13 +206,18 @@ def test_front_end_give_up_and_dirty_failure_word(monkeypatch):
     ids, aff = _front_end(ws)
     assert np.array_equal(ids, ids_ref) and np.array_equal(aff, aff_ref)
     assert _fail_line(ws) == [0, 1, 0, 0]
-    # a failure word and counter that are not clean on entry are ignored
+    # a failure word that is not clean on entry is reported as a give-up of
+    # that call (counted once, whatever the readers' counter held) and cleared
     ws[:4].view(torch.int32).fill_(1)
     ws[8:12].view(torch.int32).fill_(12345)
     log("[gpu] front end: dirty failure word")
+    ids, _ = _front_end(ws)
+    assert np.all(ids == -1)
+    assert _fail_line(ws) == [0, 2, 0, 0]
+    log("[gpu] front end: after the dirty failure word")
     ids, aff = _front_end(ws)
     assert np.array_equal(ids, ids_ref) and np.array_equal(aff, aff_ref)
-    assert _fail_line(ws) == [0, 1, 0, 0]
+    assert _fail_line(ws) == [0, 2, 0, 0]
 
 
 def test_aux_dirty_slots_are_repaired():

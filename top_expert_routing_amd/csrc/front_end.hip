@@ -19,9 +19,9 @@
 // r_t is its own ready flag: the workspace slot is zero between calls and
 // r_t > 0, so a gemm lane polls its token's slot (a device-scope load, coherent
 // across the XCDs' L2 caches) until it is non-zero.  The poll is bounded by a
-// spin limit: one that runs out sets the failure word (and counts the call),
-// and the call then writes -1 into topk_ids instead of hanging; the last
-// select block to have read the word clears it again.
+// spin limit: one that runs out sets the failure word, and the call then
+// writes -1 into topk_ids instead of hanging; the last select block to have
+// read the word counts the call and clears the word again.
 //
 // select_kernel: one wavefront per token, after the projection: z = sum of
 // the partials in chunk order (+ router bias) -- deterministic; top-k on the
@@ -99,7 +99,10 @@ constexpr int kTileRows = 64 * kS;  // tokens per gemm block (one completion cou
 // failure line holds three words: [0] set when a wait gave up, [1] the number
 // of calls whose wait gave up (never cleared here: the caller's to read), [2]
 // the select blocks that have read [0] in such a call.  Only [1] may be
-// non-zero between calls.
+// non-zero between calls.  Nothing clears [0] while the projection runs (a
+// clear there could race with a give-up and lose it): it is set by the
+// projection and read, counted and cleared by the selection, which runs after
+// it in stream order.
 constexpr int kFailBytes = 256;
 static_assert(kFailBytes + 128 * 4 <= kFrontEndSyncBytes, "sync region");
 
@@ -142,11 +145,9 @@ __device__ __forceinline__ uint32_t poll_nonzero(const uint32_t* p, int spin_lim
   return 0u;
 }
 
-// A wait ran out: record it (the select kernel reads the word); the first
-// wait of the call to give up also counts the call.
+// A wait ran out: record it (the select kernel reads, counts and clears it).
 __device__ __forceinline__ void mark_failed(const FeArgs& a) {
-  if (__hip_atomic_exchange(a.fail, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u)
-    __hip_atomic_fetch_add(a.fail + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  st_dev(a.fail, 1u);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
@@ -434,13 +435,10 @@ __global__ void __launch_bounds__(kThreads) norm_gemm_kernel(FeArgs a) {
   extern __shared__ __align__(16) uint16_t lds[];
   __shared__ float red[kThreads / 64];
   const int b = blockIdx.x;
-  // The failure word and the select blocks' counter start every call at zero,
-  // whatever a region that was not clean held: block 0 runs first, seconds
-  // before any wait could give up.
-  if (b == 0 && threadIdx.x == 0) {
-    st_dev(a.fail, 0u);
-    st_dev(a.fail + 2, 0u);
-  }
+  // The select blocks' reader count starts every call at zero, whatever a
+  // region that was not clean held (only select blocks touch it, and they run
+  // after this launch).
+  if (b == 0 && threadIdx.x == 0) st_dev(a.fail + 2, 0u);
   if (b < a.T) rms_role<F16>(a, b, red);
   else if (b >= a.gemm_begin) gemm_role<F16, STEPS>(a, b - a.gemm_begin, lds + 8 + 32 * STEPS, lds);
 }
@@ -596,11 +594,13 @@ __global__ void __launch_bounds__(64)
     store_bf16<J>(aff + (size_t)t * E + e0, v);
   }
   // a call whose wait gave up: the last select block to have read the failure
-  // word clears it (nothing of this runs otherwise)
+  // word counts the call, once, and clears the word (nothing of this runs
+  // otherwise)
   if (failed && lane == 0) {
     const uint32_t seen =
         __hip_atomic_fetch_add(fail + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (seen == (uint32_t)T - 1u) {
+      __hip_atomic_fetch_add(fail + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       st_dev(fail + 2, 0u);
       st_dev(fail, 0u);
     }
