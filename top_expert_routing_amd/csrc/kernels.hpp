@@ -136,18 +136,30 @@ struct RouteLds {
   int bias, hmask, row, cand, sel_idx, gscore, total;
   int row_stride, cand_stride, sel_stride, gs_stride;   // in elements
 };
+// Padding words after each lane's slice of a cluster's LDS row (slices of
+// `words` 32-bit words, lpt lanes).  When a cluster's row spans more than the
+// 64 banks, lanes whose slices start a multiple of 64 words apart would hit
+// the same banks with their 16-byte accesses; 4 words per lane spread them
+// (and the rows of consecutive clusters follow directly).  Smaller rows keep
+// the unpadded layout, whose clusters are offset by 4 words instead.
+__host__ __device__ constexpr int route_lane_pad(int lpt, int words) {
+  return lpt * words > 64 ? 4 : 0;
+}
+
 __host__ __device__ inline RouteLds route_lds_layout(int lpt, int rwpl, int epl, int hmask_len,
                                                     int cap, int k, int n_group) {
   RouteLds L{};
   const int block = lpt * 64 < 512 ? lpt * 64 : 512;
   const int ncl = block / lpt;
-  L.row_stride = ((lpt * rwpl + 3) & ~3) + 4;  // words, a multiple of 4
+  const int lp = route_lane_pad(lpt, rwpl);
+  L.row_stride = lp ? (lpt * (rwpl + lp) + 3) & ~3      // words, a multiple of 4
+                    : ((lpt * rwpl + 3) & ~3) + 4;
   L.cand_stride = cap + 2;                     // even: 16-byte aligned rows
   L.sel_stride = k + 1;
   L.gs_stride = n_group > 0 ? ((lpt + 1) & ~1) : 0;   // u64 group keys, read two at a time
   int off = 0;
   auto take = [&](int bytes) { const int o = off; off += (bytes + 15) & ~15; return o; };
-  L.bias = take(lpt * epl * 4);
+  L.bias = take(lpt * (epl + route_lane_pad(lpt, epl)) * 4);
   L.hmask = take(hmask_len * 8);
   L.row = take(ncl * L.row_stride * 4);
   L.cand = take(ncl * L.cand_stride * 8);

@@ -97,8 +97,11 @@ constexpr bool kRawRow = VAR == kVarSoftmax;
 template <int VAR, bool BF16>
 constexpr bool kSigRawOk = VAR == kVarSigmoid && BF16;
 
-template <int VAR, bool BF16>
-__device__ __forceinline__ float row_basis(const uint32_t* rowc, int e, bool sig_raw) {
+// Expert e of the cluster lies in lane e / EPL, whose slice starts lpad
+// padding words per earlier lane further on (see route_lane_pad).
+template <int VAR, bool BF16, int EPL>
+__device__ __forceinline__ float row_basis(const uint32_t* rowc, int e, bool sig_raw, int lpad) {
+  rowc += lpad * (e / EPL);
   if constexpr (kRawRow<VAR, BF16> && BF16) {
     const uint32_t w = rowc[e >> 1];
     return (e & 1) ? bf16_hi(w) : bf16_lo(w);
@@ -183,6 +186,7 @@ struct EmitCtx {
   void* weights;
   bool weights_bf16, renorm, counting, pre;
   bool sig_raw;           // the row holds raw bfloat16 logits of the sigmoid variant
+  int lpad;               // padding words per lane slice of the row
   int mode, k, loc_off, loc_n;
   float scale;
   uint64_t* hmask;
@@ -194,14 +198,14 @@ struct EmitCtx {
 // Weights, ids and the block bitmask for the k selected, by rank: lane c
 // handles ranks c, c + LPT, ... (contiguous stores across the cluster).  The
 // score basis of each selected expert is recomputed from its raw logit.
-template <int LPT, bool BF16, int VAR>
+template <int LPT, int EPL, bool BF16, int VAR>
 __device__ __forceinline__ void emit_selected(const EmitCtx& c, const int* myselidx,
                                               const uint32_t* rowc) {
   const int k = c.k;
   if (k <= LPT) {                             // one rank per lane
     const bool v = c.lane_c < k;
     const int e = v ? myselidx[c.lane_c] : 0;
-    const float r = row_basis<VAR, BF16>(rowc, e, c.sig_raw);
+    const float r = row_basis<VAR, BF16, EPL>(rowc, e, c.sig_raw, c.lpad);
     float ref = 0.0f;
     if (c.mode == kEmitSoftSel) ref = cl_max<LPT>(v ? r : -kInf);
     float inv_den = c.inv_s;
@@ -237,7 +241,7 @@ __device__ __forceinline__ void emit_selected(const EmitCtx& c, const int* mysel
     }
 #pragma unroll
     for (int q = 0; q < KQ; ++q)
-      r[q] = row_basis<VAR, BF16>(rowc, e[q], c.sig_raw);
+      r[q] = row_basis<VAR, BF16, EPL>(rowc, e[q], c.sig_raw, c.lpad);
     float ref = 0.0f;
     if (c.mode == kEmitSoftSel) {
       float mx = -kInf;
@@ -283,14 +287,14 @@ __device__ __forceinline__ void emit_selected(const EmitCtx& c, const int* mysel
   if (c.mode == kEmitSoftSel) {
     float mx = -kInf;
     for (int n = c.lane_c; n < k; n += LPT)
-      mx = fmaxf(mx, row_basis<VAR, BF16>(rowc, myselidx[n], c.sig_raw));
+      mx = fmaxf(mx, row_basis<VAR, BF16, EPL>(rowc, myselidx[n], c.sig_raw, c.lpad));
     ref = cl_max<LPT>(mx);
   }
   float inv_den = c.inv_s;
   if (c.mode != kEmitExactPre) {
     float part = 0.0f;
     for (int n = c.lane_c; n < k; n += LPT) {
-      const float r = row_basis<VAR, BF16>(rowc, myselidx[n], c.sig_raw);
+      const float r = row_basis<VAR, BF16, EPL>(rowc, myselidx[n], c.sig_raw, c.lpad);
       part += c.mode == kEmitPlain ? r : exp_f32(r - ref);
     }
     inv_den = fast_rcp(cl_sum<LPT>(part));
@@ -299,7 +303,7 @@ __device__ __forceinline__ void emit_selected(const EmitCtx& c, const int* mysel
   const float sub = c.mode == kEmitExactPre ? c.m : ref;
   for (int n = c.lane_c; n < k; n += LPT) {
     const int e = myselidx[n];
-    const float r = row_basis<VAR, BF16>(rowc, e, c.sig_raw);
+    const float r = row_basis<VAR, BF16, EPL>(rowc, e, c.sig_raw, c.lpad);
     float w;
     if (c.mode == kEmitPlain)
       w = c.renorm ? r * inv_den : r;
@@ -412,7 +416,9 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>)
   float* bias_s = reinterpret_cast<float*>(smem + L.bias);
   uint64_t* hmask = reinterpret_cast<uint64_t*>(smem + L.hmask);
   uint32_t* rowc = reinterpret_cast<uint32_t*>(smem + L.row) + cl * L.row_stride;
-  uint32_t* myrow = rowc + lane_c * RWPL;
+  const int lpad = route_lane_pad(LPT, RWPL);          // padded lane slices of the row
+  constexpr int BPAD = route_lane_pad(LPT, EPL);       // and of the bias
+  uint32_t* myrow = rowc + lane_c * (RWPL + lpad);
   uint64_t* mycand = reinterpret_cast<uint64_t*>(smem + L.cand) + cl * L.cand_stride;
   int* myselidx = reinterpret_cast<int*>(smem + L.sel_idx) + cl * L.sel_stride;
   uint64_t* mygs = reinterpret_cast<uint64_t*>(smem + L.gscore) + cl * L.gs_stride;
@@ -440,7 +446,7 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>)
       if (e != tid && e < E && p.bias != nullptr)
         b = p.bias_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(p.bias)[e])
                         : static_cast<const float*>(p.bias)[e];
-      bias_s[e] = b;
+      bias_s[e + BPAD * (e / EPL)] = b;
     }
   }
   const bool counting = p.super_rows != nullptr || p.fused;
@@ -454,7 +460,7 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>)
   if constexpr (kBias) {
 #pragma unroll
     for (int i = 0; i < EPL; i += 4) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(bias_s + e0 + i);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(bias_s + e0 + BPAD * lane_c + i);
       breg[i] = v.x; breg[i + 1] = v.y; breg[i + 2] = v.z; breg[i + 3] = v.w;
     }
   }
@@ -710,8 +716,8 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>)
         float kk[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          kk[q] = row_basis<VAR, BF16>(rowc, e0 + ii[q], sig_raw);
-          if constexpr (kBias) kk[q] += bias_s[e0 + ii[q]];
+          kk[q] = row_basis<VAR, BF16, EPL>(rowc, e0 + ii[q], sig_raw, lpad);
+          if constexpr (kBias) kk[q] += bias_s[e0 + BPAD * lane_c + ii[q]];
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) mycand[hv[q] ? pos + q : spare] = pack_key(kk[q], e0 + ii[q]);
@@ -768,6 +774,7 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>)
       ec.weights = p.weights;
       ec.weights_bf16 = p.weights_bf16 != 0;
       ec.sig_raw = sig_raw;
+      ec.lpad = lpad;
       ec.renorm = p.renorm != 0;
       ec.counting = counting;
       ec.pre = pre;
@@ -783,7 +790,7 @@ __global__ void __launch_bounds__(kRouteBlock<LPT>)
       ec.tv = tv;
       ec.m = m;
       ec.inv_s = inv_s;
-      emit_selected<LPT, BF16, VAR>(ec, myselidx, rowc);
+      emit_selected<LPT, EPL, BF16, VAR>(ec, myselidx, rowc);
     }
     // ---- full-E scores for the aux loss --------------------------------------------
     if (p.scores != nullptr) {
