@@ -349,6 +349,19 @@ def test_workspace_reuse_across_sizes():
         count_region_ready(ws, label)
 
 
+# More local experts than threads in a block: the padded offsets take several
+# rounds of the block scan, in the single-block permutation (T <= 64) and in
+# the scatter kernel alike.
+@pytest.mark.parametrize("T", [50, 3000])
+@pytest.mark.parametrize("E,n_group,topk_group", [(1024, 8, 4), (600, 0, 0), (2048, 0, 0)])
+def test_multi_round_offset_scan(T, E, n_group, topk_group):
+    w = RouteWorkload(name="wide", seed=7700 + E + T, T=T, E=E, k=8, score_fn="sigmoid",
+                      pre_softmax=False, n_group=n_group, topk_group=topk_group, group_topn=2,
+                      logits_dtype="bf16", bias_std=0.01, tile=4)
+    logits, bias = route_inputs(w)
+    run_and_check(w, logits, bias, f"multi-round scan E={E} T={T}")
+
+
 @pytest.mark.parametrize("name,T,tile,off,n_loc", [
     ("tiny_softmax_post", 1, 1, 0, None), ("tiny_softmax_post", 64, 16, 0, None),
     ("tiny_softmax_post", 40, 4, 2, 4), ("deepseek_v3_like", 64, 8, 64, 64),

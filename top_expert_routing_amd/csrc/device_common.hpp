@@ -252,7 +252,8 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 
 // Exclusive prefix sum of one value per thread over a block of THREADS
 // threads (a multiple of 64), in thread order; `total` gets the block's sum.
-// tmp: LDS for THREADS / 64 ints.  Contains two block barriers.
+// tmp: LDS for THREADS / 64 ints.  Contains one block barrier; the caller
+// places another before tmp is written again (a further round).
 template <int THREADS>
 __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int& total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -266,7 +267,6 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int& total) {
     before += i < w ? s : 0;
     tot += s;
   }
-  __syncthreads();
   total = tot;
   return before + incl - v;
 }

@@ -347,6 +347,7 @@ __device__ void permute_in_block(const RouteParams& p, const uint64_t* hmask, in
     const int ex = block_excl_scan<BLOCK>(v, scan_tmp, round_total);
     if (e < El) po[e] = carry + ex;
     carry += round_total;
+    if (e0 + BLOCK < El) __syncthreads();               // scan_tmp is written again
   }
   if (tid == 0) po[El] = carry;
   __syncthreads();

@@ -198,7 +198,7 @@ __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams 
     }
   }
   if (tid == 0) po[El] = 0;
-  const int bad_count = __syncthreads_or(bad);
+  __syncthreads();
 
   // token bitmasks (LDS atomics), then the exclusive scan of the padded sizes
   // over the block, 256 experts per round (wavefront scans in DPP moves).
@@ -223,15 +223,16 @@ __global__ void __launch_bounds__(kScatterThreads) scatter_kernel(ScatterParams 
       neg |= carry + ex < 0;                             // the running sum wrapped
     }
     carry += round_total;
+    if (e0 + kScatterThreads < El) __syncthreads();     // scan_tmp is written again
   }
   if (tid == 0) po[El] = carry;
-  const int wrapped = __syncthreads_or(neg);
+  const int wrapped = __syncthreads_or(neg | bad);          // or a count outside [0, T k]
   const int total = po[El];
   // A dirty counting region (see kCountSetInts): the permutation is not
   // written past the caller's arrays, the totals report -1 and both sets are
   // cleared.  Every term is uniform over the grid.
   const bool dirty = (h1 >> 1) != 0u || ext_other > (uint32_t)kCountSetInts ||
-                     ext_own > (uint32_t)kCountSetInts || bad_count || wrapped || total < 0 ||
+                     ext_own > (uint32_t)kCountSetInts || wrapped || total < 0 ||
                      total > p.max_padded;
   // The other set was used by the previous call and fully read by its
   // scatter: clear it (strided over the blocks) for the next call, which adds
