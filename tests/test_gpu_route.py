@@ -349,6 +349,28 @@ def test_workspace_reuse_across_sizes():
         count_region_ready(ws, label)
 
 
+# The LDS row and bias of a cluster are padded per lane when they span more
+# than 64 words: shapes on both sides of that line, with and without a bias,
+# both score variants and both logit types (the emission and the compaction
+# read the padded row back by expert index).
+@pytest.mark.parametrize("E,n_group,score_fn,dtype,bias", [
+    (64, 0, "sigmoid", "f32", True),      # 2 lanes x 32: unpadded
+    (128, 0, "sigmoid", "f32", True),     # 4 lanes x 32 fp32 scores: padded row and bias
+    (128, 4, "sigmoid", "bf16", True),    # grouped, 4 lanes
+    (256, 0, "softmax", "f32", True),     # 8 lanes x 32 raw fp32 words, biased softmax
+    (512, 16, "sigmoid", "bf16", True),   # 16 lanes
+    (96, 0, "softmax", "bf16", False),    # padded experts in the last lane
+])
+def test_padded_lane_slices(E, n_group, score_fn, dtype, bias):
+    w = RouteWorkload(name="pad", seed=7900 + E + n_group, T=999, E=E, k=8, score_fn=score_fn,
+                      pre_softmax=score_fn == "softmax", n_group=n_group,
+                      topk_group=n_group // 2 if n_group else 0, group_topn=2,
+                      logits_dtype=dtype, bias_std=0.05 if bias else None, tile=8)
+    logits, b = route_inputs(w)
+    run_and_check(w, logits, b, f"padded slices E={E} {score_fn} {dtype}")
+    run_and_check(w, logits, b, f"padded slices E={E} {score_fn} {dtype} scores", scores=True)
+
+
 # More local experts than threads in a block: the padded offsets take several
 # rounds of the block scan, in the single-block permutation (T <= 64) and in
 # the scatter kernel alike.
