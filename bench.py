@@ -238,6 +238,9 @@ def other_configs(mr, torch, np, dev, rotate_mb, K, cpu_seconds=None, only=None)
         set_b = (x0.numel() * x0.element_size() + ids0.numel() * 4 + gw0.numel() * 4 +
                  (gs0.numel() * 4 if with_s else 0) + w.T * w.E * 4)
         R = n_sets(set_b, rotate_mb)
+        # algorithmic bytes: the sigmoid weights read only the k chosen logits
+        # of a token, the softmax-before-top-k and score gradients the whole row
+        alg_b = set_b if with_s else set_b - x0.numel() * x0.element_size() + ids0.numel() * x0.element_size()
         bsets = [(x0.clone(), ids0.clone(), gw0.clone(), None if gs0 is None else gs0.clone(),
                   torch.empty((w.T, w.E), dtype=torch.float32, device=dev)) for _ in range(R)]
         ms = graph_ms(torch, lambda i: mr.moe_route_backward(args, *bsets[i % R]), K)
@@ -251,13 +254,13 @@ def other_configs(mr, torch, np, dev, rotate_mb, K, cpu_seconds=None, only=None)
                 lambda a, b, c: torch.add(a, b, out=c))
         else:
             plain = plain_op_entry(
-                torch, rotate_mb, K, "bf16 [T,E] -> f32 [T,E] (copy_)", w.T * w.E * 6,
-                lambda: (x0.clone(), torch.empty(shape, device=dev)), lambda a, b: b.copy_(a))
+                torch, rotate_mb, K, "fill of a f32 [T,E] tensor", w.T * w.E * 4,
+                lambda: (torch.empty(shape, device=dev),), lambda b: b.fill_(1.0))
         res[name + "_backward"] = {
             "workload": w.description + ("; grad of weights and scores" if with_s else
                                          "; grad of weights") + " -> grad of logits",
-            "us_per_call": ms * 1e3, "algorithmic_bytes": set_b,
-            "gbs": set_b / (ms * 1e-3) / 1e9, "buffer_sets": R, "plain_torch_op": plain}
+            "us_per_call": ms * 1e3, "algorithmic_bytes": alg_b,
+            "gbs": alg_b / (ms * 1e-3) / 1e9, "buffer_sets": R, "plain_torch_op": plain}
 
     if want("deepseek_v3_like_dense_outputs"):
         # dense [T, E] probs + routing map from the DeepSeek-V3-like top-k outputs

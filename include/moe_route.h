@@ -311,7 +311,8 @@ moe_status moe_aux_loss(const float* probs, const int32_t* tokens_per_expert, in
  *                and bias fields are not (the choice is given by topk_ids).
  * logits         [T, E], logits_dtype (the forward's input).
  * topk_ids       [T, k] int32, the forward's ids (required with grad_weights);
- *                ids outside [0, E) contribute nothing.
+ *                ids outside [0, E) contribute nothing; a token's ids are
+ *                expected to be distinct, as moe_route writes them.
  * grad_weights   nullable [T, k] float32, the gradient of topk_weights.
  * grad_scores    nullable [T, E] float32, the gradient of the full-E scores.
  * grad_logits    out [T, E] float32, every element written.

@@ -72,3 +72,16 @@ def test_dense_one_output_and_foreign_ids():
     ids[::7, 3] = -1                 # ids outside [0, E) are ignored
     ids[::11, 5] = 256
     check_dense(ids, wts, 256, label="foreign ids")
+
+
+def test_dense_repeated_ids():
+    # of choices naming one expert, the last one's weight stays (the oracle's loop order)
+    ids, wts = _route(301, 256, 8, seed=6)
+    ids = ids.copy()
+    ids[::3, 4] = ids[::3, 1]
+    ids[::4, 7] = ids[::4, 0]
+    check_dense(ids, wts, 256, label="repeated ids")
+    ids2, wts2 = _route(150, 128, 8, seed=9)
+    ids2 = ids2.copy()
+    ids2[:, 6] = ids2[:, 6 - 1]
+    check_dense(ids2, wts2, 128, w_dtype="bf16", label="repeated ids E=128")

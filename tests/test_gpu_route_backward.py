@@ -105,3 +105,47 @@ def test_backward_deterministic():
     a = _run_backward(w, logits, r.ids, gw, None)
     b = _run_backward(w, logits, r.ids, gw, None)
     assert np.array_equal(a, b)
+
+
+# Weight gradients alone (no score gradient) for the score functions whose
+# weights read only the chosen logits: every other element must be exactly 0.
+# E a multiple of 64 up to 512, ragged T, both logit types.
+@pytest.mark.parametrize("score_fn,pre,renorm", [("sigmoid", False, True), ("sigmoid", False, False),
+                                                 ("softmax", False, True)])
+@pytest.mark.parametrize("E,k,T,dtype", [(64, 1, 5, "f32"), (64, 16, 301, "bf16"),
+                                         (128, 8, 1000, "bf16"), (256, 8, 4099, "f32"),
+                                         (256, 16, 65, "bf16"), (512, 12, 333, "f32")])
+def test_backward_weights_only(score_fn, pre, renorm, E, k, T, dtype):
+    base = WORKLOADS["mixtral_like"]
+    w = with_overrides(base, E=E, k=k, score_fn=score_fn, pre_softmax=pre, renorm=renorm,
+                       scale=2.5, logits_dtype=dtype, n_group=0, topk_group=0)
+    check_backward(w, T, seed=4000 + E + k + T, with_w=True, with_s=False,
+                   label=f"weights only {score_fn}/{renorm} E={E} k={k}")
+
+
+def _backward_given_ids(w, logits, ids_gpu, gw_gpu, ids_ref, gw_ref, label):
+    got = _run_backward(w, logits, ids_gpu, gw_gpu, None)
+    ref, mag = oracle.route_backward(logits, w.logits_dtype, ids_ref, gw_ref, None,
+                                     score_fn=w.score_fn, pre_softmax=w.pre_softmax,
+                                     renorm=w.renorm, scale=w.scale)
+    assert np.all(np.isfinite(got)), label
+    assert np.all(got[mag == 0] == 0.0), label
+    bad = np.abs(got - ref) > RTOL * mag
+    assert not bad.any(), (label, int(bad.sum()))
+
+
+@pytest.mark.parametrize("score_fn,pre", [("sigmoid", False), ("softmax", False), ("softmax", True)])
+def test_backward_foreign_ids(score_fn, pre):
+    # ids outside [0, E) contribute nothing, as if that choice were absent
+    w = with_overrides(WORKLOADS["deepseek_v3_like"], score_fn=score_fn, pre_softmax=pre,
+                       n_group=0, topk_group=0, bias_std=None)
+    T = 515
+    logits, _ = route_inputs(w, T=T, seed=21)
+    r = oracle.route(logits, w.logits_dtype, w.k, score_fn=w.score_fn, pre_softmax=w.pre_softmax,
+                     renorm=w.renorm, scale=w.scale)
+    gw = np.random.default_rng(22).standard_normal((T, w.k)).astype(np.float32)
+    ids = r.ids.astype(np.int64).copy()
+    ids[:, 2] = -1
+    ids[:, 5] = w.E
+    keep = [j for j in range(w.k) if j not in (2, 5)]
+    _backward_given_ids(w, logits, ids, gw, ids[:, keep], gw[:, keep], f"{score_fn}/{pre} foreign")
