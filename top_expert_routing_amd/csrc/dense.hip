@@ -68,7 +68,7 @@ __global__ void __launch_bounds__(kDenseThreads)
     if (rmap != nullptr) {
       uint32_t b[J / 4];
 #pragma unroll
-      for (int h = 0; h < J / 4; ++h) b[h] = (sel >> (4 * h)) & 1u | ((sel >> (4 * h + 1)) & 1u) << 8 |
+      for (int h = 0; h < J / 4; ++h) b[h] = ((sel >> (4 * h)) & 1u) | ((sel >> (4 * h + 1)) & 1u) << 8 |
                                               ((sel >> (4 * h + 2)) & 1u) << 16 | ((sel >> (4 * h + 3)) & 1u) << 24;
       if constexpr (J == 4) __builtin_nontemporal_store(b[0], reinterpret_cast<uint32_t*>(rmap + base));
       else __builtin_nontemporal_store((uint64_t)b[0] | ((uint64_t)b[1] << 32), reinterpret_cast<uint64_t*>(rmap + base));
