@@ -286,7 +286,10 @@ size_t moe_route_permute_noalloc_max_scratch_bytes(void);
  * environment variable MOE_ROUTE_AUX_SPIN_LIMIT, an integer no larger than the
  * default, lowers the limit on each call; 0 forces the give-up, for tests.)  A dirty slot
  * (non-zero on entry) is taken for a published partial: the forward that
- * reads it gives a wrong loss and returns it to zero. */
+ * reads it gives a wrong loss.  Its summing block then need not wait for the
+ * other blocks, so a block that publishes after that block has cleared the
+ * slots leaves its slot set: zero the region again after a forward that ran
+ * on a dirty region.  No access leaves the region either way. */
 moe_status moe_aux_loss(const float* probs, const int32_t* tokens_per_expert, int64_t rows,
                         int64_t total_num_tokens, int32_t num_experts, int32_t top_k,
                         float coeff, float* loss, const float* grad_loss, float* grad_probs,
