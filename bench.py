@@ -574,7 +574,7 @@ def main():
     a = parse()
     if a.gpus != 1:
         print(f"bench.py: this routing path runs on one GPU; --gpus {a.gpus} is not supported "
-              "(tokens shard independently across GPUs; see the design notes)", file=sys.stderr)
+              "(tokens shard independently: each GPU routes its own rows with replicated router state)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
