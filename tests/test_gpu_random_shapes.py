@@ -7,6 +7,9 @@ an optional bias), shapes (E up to 2048, k up to 64, a ragged T), dtypes
 local-expert shard and the optional full-E scores, and runs moe_route_permute
 against the oracle under the usual parity rules.  Configurations outside the
 kernels' stated limits (MOE_EUNSUPPORTED) are skipped with the limit named.
+A second family draws large T (33 000 to 140 000 tokens: grids of several
+rounds of route blocks, scatter blocks serving several route blocks) with
+E up to 512 and k up to 16 (`MOE_RANDOM_LARGE_CASES`, 3 by default).
 """
 from __future__ import annotations
 
@@ -64,6 +67,57 @@ def test_random_configuration(i):
     logits, bias = route_inputs(w)
     try:
         run_and_check(w, logits, bias, f"random {i}", weights_dtype=wdt, scores=scores,
+                      off=off, n_loc=n_loc)
+    except mr.MoeError as e:
+        if e.status == mr.MOE_EUNSUPPORTED:
+            pytest.skip(f"outside the kernels' limits: {e}")
+        raise
+
+
+LARGE_CASES = int(os.environ.get("MOE_RANDOM_LARGE_CASES", "3"))
+
+
+def _large_config(i: int):
+    # T large enough for grids of several rounds of route blocks and for the
+    # scatter blocks that serve 2 or 4 route blocks (from 1024 / 2048 route
+    # blocks of 64 tokens on); T * E bounded so that the oracle stays fast
+    rng = np.random.default_rng(20000 + i)
+    score_fn = str(rng.choice(["softmax", "sigmoid"]))
+    pre = bool(rng.integers(2)) if score_fn == "softmax" else False
+    E = int(rng.choice([64, 128, 160, 256, 384, 512]))
+    n_group = topk_group = 0
+    topn = 2
+    if rng.random() < 0.4 and E in (64, 128, 256, 512):
+        n_group = int(rng.choice([2, 4, 8]))
+        topk_group = int(rng.integers(1, n_group))
+        topn = int(rng.choice([1, 2]))
+        kmax = min(16, topk_group * (E // n_group))
+    else:
+        kmax = min(16, E)
+    k = int(rng.integers(1, kmax + 1))
+    T = int(rng.integers(33000, min(140000, 40_000_000 // E) + 1))
+    bias_std = float(rng.choice([0.01, 0.1])) if rng.random() < 0.5 else None
+    w = RouteWorkload(name=f"large{i}", seed=20100 + i, T=T, E=E, k=k, score_fn=score_fn,
+                      pre_softmax=pre, n_group=n_group, topk_group=topk_group, group_topn=topn,
+                      renorm=bool(rng.integers(2)), scale=float(rng.choice([1.0, 2.5])),
+                      logits_dtype=str(rng.choice(["f32", "bf16"])),
+                      logits_std=float(rng.choice([0.5, 1.0, 2.0])), bias_std=bias_std,
+                      bias_dtype=str(rng.choice(["f32", "bf16"])),
+                      tile=int(rng.choice([1, 8, 16, 64, 256])))
+    off, n_loc = 0, None
+    if rng.random() < 0.25:
+        off = int(rng.integers(0, E))
+        n_loc = int(rng.integers(1, E - off + 1))
+    scores = bool(rng.random() < 0.2) and T * E <= 20_000_000
+    return (w, str(rng.choice(["f32", "bf16"])), scores, off, n_loc)
+
+
+@pytest.mark.parametrize("i", range(LARGE_CASES))
+def test_random_large_configuration(i):
+    w, wdt, scores, off, n_loc = _large_config(i)
+    logits, bias = route_inputs(w)
+    try:
+        run_and_check(w, logits, bias, f"random large {i}", weights_dtype=wdt, scores=scores,
                       off=off, n_loc=n_loc)
     except mr.MoeError as e:
         if e.status == mr.MOE_EUNSUPPORTED:
