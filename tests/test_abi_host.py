@@ -238,3 +238,23 @@ def test_topk_to_dense_validation():
     assert X(10, 8, 2, FAKE, FAKE, mr.MOE_F16, FAKE, None, None) == mr.MOE_EINVAL
     assert X(10, 8, 2, FAKE, ctypes.c_void_p(0x1002), mr.MOE_F32, FAKE, None, None) == mr.MOE_EINVAL
     assert X(0, 8, 2, None, None, mr.MOE_F32, FAKE, None, None) == mr.MOE_OK         # nothing to do
+
+
+def test_header_is_plain_c(tmp_path):
+    # the boundary is a C ABI: a C11 translation unit that includes the header
+    # and takes the address of every entry point compiles as C
+    import shutil
+    gcc = shutil.which("gcc")
+    rocm_inc = "/opt/rocm/include"
+    if gcc is None or not os.path.isdir(rocm_inc):
+        pytest.skip("gcc or the HIP runtime headers are not available")
+    names = _declared_functions()
+    assert names, "no entry points found in the header"
+    src = tmp_path / "abi.c"
+    src.write_text('#include "moe_route.h"\nint main(void) {\n  const void* fns[] = {' +
+                   ", ".join(f"(const void*){n}" for n in names) +
+                   "};\n  return fns[0] == 0;\n}\n")
+    res = subprocess.run([gcc, "-std=c11", "-Wall", "-Werror", "-fsyntax-only",
+                          "-D__HIP_PLATFORM_AMD__", f"-I{os.path.dirname(HEADER)}",
+                          f"-I{rocm_inc}", str(src)], capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
