@@ -308,7 +308,7 @@ moe_status moe_aux_loss(const float* probs, const int32_t* tokens_per_expert, in
  * through the score function of args (sigmoid; softmax before or after top-k),
  * the renormalisation (args->renormalize) and args->routed_scaling_factor.
  *
- * args           the forward's arguments: num_tokens, num_experts (<= 512),
+ * args           the forward's arguments: num_tokens, num_experts (<= 2048),
  *                top_k, score_fn, use_pre_softmax, renormalize,
  *                routed_scaling_factor, logits_dtype are used; the grouping
  *                and bias fields are not (the choice is given by topk_ids).
@@ -334,7 +334,7 @@ moe_status moe_route_backward(const moe_route_args* args, const void* logits,
  * topk_ids [T, k] int32 (ids outside [0, E) are ignored), topk_weights [T, k]
  * in weights_dtype (MOE_F32 or MOE_BF16); probs: nullable out [T, E] float32;
  * routing_map: nullable out [T, E] uint8 (bool); at least one is given.
- * E <= 512, k in [1, 64].  No workspace. */
+ * E <= 2048, k in [1, 64].  No workspace. */
 moe_status moe_topk_to_dense(int32_t T, int32_t E, int32_t top_k, const int32_t* topk_ids,
                              const void* topk_weights, int32_t weights_dtype, float* probs,
                              uint8_t* routing_map, hipStream_t stream);

@@ -198,7 +198,7 @@ def test_route_backward_validation():
     assert B(ctypes.byref(args), FAKE, None, FAKE, None, FAKE, None) == mr.MOE_EINVAL   # ids needed
     assert B(ctypes.byref(args), FAKE, FAKE, FAKE, None, None, None) == mr.MOE_EINVAL   # no output
     assert B(ctypes.byref(args), FAKE, FAKE, ctypes.c_void_p(0x1002), None, FAKE, None) == mr.MOE_EINVAL
-    big = mr.make_route_args(64, 1024, 8)
+    big = mr.make_route_args(64, 4096, 8)
     assert B(ctypes.byref(big), *ok[1:]) == mr.MOE_EUNSUPPORTED
     bad_k = mr.make_route_args(64, 16, 17)
     assert B(ctypes.byref(bad_k), *ok[1:]) == mr.MOE_EINVAL
@@ -233,7 +233,7 @@ def test_topk_to_dense_validation():
     # every call below fails on the host, before anything is launched
     assert X(10, 8, 2, FAKE, FAKE, mr.MOE_F32, None, None, None) == mr.MOE_EINVAL    # no output
     assert X(10, 8, 9, FAKE, FAKE, mr.MOE_F32, FAKE, None, None) == mr.MOE_EINVAL    # k > E
-    assert X(10, 600, 8, FAKE, FAKE, mr.MOE_F32, FAKE, None, None) == mr.MOE_EUNSUPPORTED
+    assert X(10, 4096, 8, FAKE, FAKE, mr.MOE_F32, FAKE, None, None) == mr.MOE_EUNSUPPORTED
     assert X(10, 8, 2, None, FAKE, mr.MOE_F32, FAKE, None, None) == mr.MOE_EINVAL
     assert X(10, 8, 2, FAKE, FAKE, mr.MOE_F16, FAKE, None, None) == mr.MOE_EINVAL
     assert X(10, 8, 2, FAKE, ctypes.c_void_p(0x1002), mr.MOE_F32, FAKE, None, None) == mr.MOE_EINVAL

@@ -58,7 +58,8 @@ def test_dense_full_size():
 @pytest.mark.parametrize("T,E,k,w_dtype", [(1, 8, 2, "f32"), (33, 8, 8, "bf16"), (300, 64, 6, "f32"),
                                            (257, 100, 5, "f32"), (400, 128, 8, "bf16"),
                                            (999, 256, 8, "f32"), (130, 512, 16, "bf16"),
-                                           (77, 384, 64, "f32")])
+                                           (77, 384, 64, "f32"), (300, 1000, 8, "f32"),
+                                           (257, 1024, 16, "bf16"), (129, 2048, 64, "f32")])
 def test_dense_shapes(T, E, k, w_dtype):
     ids, wts = _route(T, E, k, seed=T + E + k)
     check_dense(ids, wts, E, w_dtype=w_dtype, label=f"{T}x{E}")

@@ -147,11 +147,11 @@ OTHER_CASES = int(os.environ.get("MOE_RANDOM_OTHER_CASES", "16"))
 
 @pytest.mark.parametrize("i", range(OTHER_CASES))
 def test_random_backward(i):
-    # routing backward (E <= 512): weight and/or score gradients, every mode
+    # routing backward (E <= 2048): weight and/or score gradients, every mode
     from test_gpu_route_backward import check_backward
     rng = np.random.default_rng(9700 + i)
     score_fn = str(rng.choice(["softmax", "sigmoid"]))
-    E = int(rng.choice([8, 16, 24, 32, 48, 64, 100, 128, 200, 256, 384, 512]))
+    E = int(rng.choice([8, 16, 24, 32, 48, 64, 100, 128, 200, 256, 384, 512, 1000, 2048]))
     k = int(rng.integers(1, min(E, 64) + 1))
     w = RouteWorkload(name=f"bwd{i}", seed=9800 + i, T=1, E=E, k=k, score_fn=score_fn,
                       pre_softmax=bool(rng.integers(2)) if score_fn == "softmax" else False,
@@ -168,7 +168,7 @@ def test_random_backward(i):
 def test_random_dense(i):
     from test_gpu_dense import _route, check_dense
     rng = np.random.default_rng(10000 + i)
-    E = int(rng.choice([8, 12, 64, 100, 128, 136, 256, 320, 512]))
+    E = int(rng.choice([8, 12, 64, 100, 128, 136, 256, 320, 512, 1000, 2048]))
     k = int(rng.integers(1, min(E, 64) + 1))
     T = int(rng.integers(1, 3000))
     ids, wts = _route(T, E, k, 10100 + i)

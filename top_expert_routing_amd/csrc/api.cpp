@@ -744,7 +744,7 @@ moe_status moe_route_backward(const moe_route_args* args, const void* logits,
   const moe_route_args& a = *args;
   if (a.num_tokens < 0) return fail(MOE_EINVAL, "num_tokens < 0");
   if (a.num_experts < 1) return fail(MOE_EINVAL, "num_experts < 1");
-  if (a.num_experts > 512) return fail(MOE_EUNSUPPORTED, "num_experts > 512");
+  if (a.num_experts > kMaxExperts) return fail(MOE_EUNSUPPORTED, "num_experts > %d", kMaxExperts);
   if (a.top_k < 1 || a.top_k > a.num_experts)
     return fail(MOE_EINVAL, "top_k must be in [1, num_experts]");
   if (a.top_k > kMaxTopK) return fail(MOE_EUNSUPPORTED, "top_k > %d", kMaxTopK);
@@ -789,7 +789,7 @@ moe_status moe_topk_to_dense(int32_t T, int32_t E, int32_t k, const int32_t* ids
                              int32_t weights_dtype, float* probs, uint8_t* rmap, hipStream_t stream) {
   clear_error();
   if (T < 0 || E < 1) return fail(MOE_EINVAL, "T >= 0 and E >= 1");
-  if (E > 512) return fail(MOE_EUNSUPPORTED, "E > 512");
+  if (E > kMaxExperts) return fail(MOE_EUNSUPPORTED, "E > %d", kMaxExperts);
   if (k < 1 || k > E) return fail(MOE_EINVAL, "top_k must be in [1, E]");
   if (k > kMaxTopK) return fail(MOE_EUNSUPPORTED, "top_k > %d", kMaxTopK);
   if (weights_dtype != MOE_F32 && weights_dtype != MOE_BF16)

@@ -5,7 +5,8 @@
 //
 // A token per cluster of L lanes (L = 32 with J = 8 experts per lane for
 // 128 < E <= 256, 32 x 4 for 64 < E <= 128, else the whole wavefront with
-// J = ceil(E / 64)); lane l of a cluster writes experts [J l, J l + J) with
+// J = 1, 2, 4, 8, 16 or 32, the least that holds E, for E <= 2048); lane l
+// of a cluster writes experts [J l, J l + J) with
 // one vector store per output; lanes j < k of a cluster read the token's j-th
 // id and weight, and k readlanes (or cluster shuffles) bring each to the lane
 // owning the expert; streaming stores.  Write-bound: T E (4 + 1) bytes.
@@ -70,8 +71,14 @@ __global__ void __launch_bounds__(kDenseThreads)
 #pragma unroll
       for (int h = 0; h < J / 4; ++h) b[h] = ((sel >> (4 * h)) & 1u) | ((sel >> (4 * h + 1)) & 1u) << 8 |
                                               ((sel >> (4 * h + 2)) & 1u) << 16 | ((sel >> (4 * h + 3)) & 1u) << 24;
-      if constexpr (J == 4) __builtin_nontemporal_store(b[0], reinterpret_cast<uint32_t*>(rmap + base));
-      else __builtin_nontemporal_store((uint64_t)b[0] | ((uint64_t)b[1] << 32), reinterpret_cast<uint64_t*>(rmap + base));
+      if constexpr (J == 4) {
+        __builtin_nontemporal_store(b[0], reinterpret_cast<uint32_t*>(rmap + base));
+      } else {
+#pragma unroll
+        for (int h = 0; h < J / 8; ++h)
+          __builtin_nontemporal_store((uint64_t)b[2 * h] | ((uint64_t)b[2 * h + 1] << 32),
+                                      reinterpret_cast<uint64_t*>(rmap + base) + h);
+      }
     }
   } else {
 #pragma unroll
@@ -86,7 +93,8 @@ __global__ void __launch_bounds__(kDenseThreads)
 hipError_t launch_dense(int T, int E, int k, const int32_t* ids, const void* weights, bool w_bf16,
                         float* probs, uint8_t* rmap, hipStream_t s) {
   const int L = (E > 64 && E <= 256 && k <= 32) ? 32 : 64;
-  const int J = L == 32 ? (E <= 128 ? 4 : 8) : E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : 8;
+  const int J = L == 32 ? (E <= 128 ? 4 : 8)
+              : E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : E <= 512 ? 8 : E <= 1024 ? 16 : 32;
   const bool vec = J >= 4 && E % J == 0 && (uintptr_t)probs % 16 == 0 && (uintptr_t)rmap % 8 == 0;
   const int per_block = kDenseThreads / 64 * (64 / L);
   const dim3 grid((T + per_block - 1) / per_block);
@@ -102,7 +110,9 @@ hipError_t launch_dense(int T, int E, int k, const int32_t* ids, const void* wei
     case 1: MOE_DENSE(1, 64, false); break;
     case 2: MOE_DENSE(2, 64, false); break;
     case 4: if (vec) MOE_DENSE(4, 64, true); else MOE_DENSE(4, 64, false); break;
-    default: if (vec) MOE_DENSE(8, 64, true); else MOE_DENSE(8, 64, false); break;
+    case 8: if (vec) MOE_DENSE(8, 64, true); else MOE_DENSE(8, 64, false); break;
+    case 16: if (vec) MOE_DENSE(16, 64, true); else MOE_DENSE(16, 64, false); break;
+    default: if (vec) MOE_DENSE(32, 64, true); else MOE_DENSE(32, 64, false); break;
   }
 #undef MOE_DENSE
   return hipGetLastError();

@@ -15,7 +15,8 @@
 // A token per cluster of L lanes (L = 8/16 with four experts per lane for
 // E <= 32/64, L = 16 with eight for E <= 128 (E a multiple of 8, k <= 16),
 // L = 32 with eight for E <= 256,
-// else the whole wavefront with J = ceil(E / 64) per lane);
+// else the whole wavefront with J = 1, 2, 4, 8, 16 or 32 per lane, the least
+// that holds E, for E <= 2048);
 // lane l of a cluster holds experts [J l, J l + J): the logits row, the score
 // gradient row and the output row move with one vector access per lane; the
 // chosen experts' weight gradients reach their owner lanes by readlane (or a
@@ -58,11 +59,14 @@ __device__ __forceinline__ void load_f32(const float* p, int n_valid, float (&v)
 
 template <int J, bool VEC>
 __device__ __forceinline__ void load_bf16(const uint16_t* p, int n_valid, float (&v)[J]) {
-  if constexpr (VEC && J == 8) {
-    const u32x4 q = *reinterpret_cast<const u32x4*>(p);
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  if constexpr (VEC && J % 8 == 0) {
 #pragma unroll
-    for (int h = 0; h < 4; ++h) { v[2 * h] = bf16_lo(w[h]); v[2 * h + 1] = bf16_hi(w[h]); }
+    for (int c = 0; c < J / 8; ++c) {
+      const u32x4 q = reinterpret_cast<const u32x4*>(p)[c];
+      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) { v[8 * c + 2 * h] = bf16_lo(w[h]); v[8 * c + 2 * h + 1] = bf16_hi(w[h]); }
+    }
   } else if constexpr (VEC && J == 4) {
     const uint2 q = *reinterpret_cast<const uint2*>(p);
     v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
@@ -328,7 +332,8 @@ hipError_t launch_route_backward(const RouteBwdParams& p, bool bf16, hipStream_t
   const int L = (p.E <= 32 && p.k <= 8) ? 8 : ((p.E <= 64 && p.k <= 16) || wide16) ? 16
               : (p.E <= 256 && p.k <= 32) ? 32 : 64;
   const int J = wide16 ? 8 : L < 32 ? 4 : L == 32 ? (p.E <= 128 ? 4 : 8)
-              : p.E <= 64 ? 1 : p.E <= 128 ? 2 : p.E <= 256 ? 4 : 8;   // E <= 512
+              : p.E <= 64 ? 1 : p.E <= 128 ? 2 : p.E <= 256 ? 4 : p.E <= 512 ? 8
+              : p.E <= 1024 ? 16 : 32;                                  // E <= 2048
   // vector accesses when every lane's J elements are whole and aligned
   const int esz = bf16 ? 2 : 4;
   const bool vec = J > 1 && p.E % J == 0 &&
@@ -344,7 +349,9 @@ hipError_t launch_route_backward(const RouteBwdParams& p, bool bf16, hipStream_t
     case 1: return bf16 ? launch_bwd_j<true, 1, 64>(p, false, s) : launch_bwd_j<false, 1, 64>(p, false, s);
     case 2: return bf16 ? launch_bwd_j<true, 2, 64>(p, vec, s) : launch_bwd_j<false, 2, 64>(p, vec, s);
     case 4: return bf16 ? launch_bwd_j<true, 4, 64>(p, vec, s) : launch_bwd_j<false, 4, 64>(p, vec, s);
-    default: return bf16 ? launch_bwd_j<true, 8, 64>(p, vec, s) : launch_bwd_j<false, 8, 64>(p, vec, s);
+    case 8: return bf16 ? launch_bwd_j<true, 8, 64>(p, vec, s) : launch_bwd_j<false, 8, 64>(p, vec, s);
+    case 16: return bf16 ? launch_bwd_j<true, 16, 64>(p, vec, s) : launch_bwd_j<false, 16, 64>(p, vec, s);
+    default: return bf16 ? launch_bwd_j<true, 32, 64>(p, vec, s) : launch_bwd_j<false, 32, 64>(p, vec, s);
   }
 }
 
