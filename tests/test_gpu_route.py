@@ -395,3 +395,15 @@ def test_single_block_permutation(name, T, tile, off, n_loc):
     w = with_overrides(WORKLOADS[name], T=T)
     logits, bias = route_inputs(w, T=T, seed=2000 + T + tile + off)
     run_and_check(w, logits, bias, f"single block {name} T={T}", tile=tile, off=off, n_loc=n_loc)
+
+
+@pytest.mark.parametrize("E,k", [(1, 1), (2, 1), (2, 2), (3, 3), (5, 4), (7, 2)])
+@pytest.mark.parametrize("score_fn,pre", [("softmax", True), ("softmax", False), ("sigmoid", False)])
+def test_few_experts(E, k, score_fn, pre):
+    # degenerate expert counts below one lane's eight: padded experts never win;
+    # with k = E every expert is chosen, in descending key order
+    w = RouteWorkload(name="few", seed=500 + 10 * E + k, T=131, E=E, k=k, score_fn=score_fn,
+                      pre_softmax=pre, renorm=True, scale=2.5, logits_dtype="f32",
+                      bias_std=0.05 if score_fn == "sigmoid" else None, tile=4)
+    logits, bias = route_inputs(w)
+    run_and_check(w, logits, bias, f"few experts E={E} k={k}", scores=True)
