@@ -258,3 +258,41 @@ def test_header_is_plain_c(tmp_path):
                           "-D__HIP_PLATFORM_AMD__", f"-I{os.path.dirname(HEADER)}",
                           f"-I{rocm_inc}", str(src)], capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-2000:]
+
+
+def test_binding_refuses_short_tensors():
+    # the binding derives each tensor's bytes from the call's own sizes and
+    # refuses a shorter one before anything reaches the library (CPU tensors:
+    # the size check of an argument comes before its device check, and the
+    # arguments are taken in order)
+    torch = pytest.importorskip("torch")
+    args = mr.make_route_args(64, 256, 8, score_fn="sigmoid", logits_dtype="bf16",
+                              weights_dtype="bf16")
+    short = torch.empty(64 * 256 - 1, dtype=torch.bfloat16)
+    full = torch.empty(64 * 256, dtype=torch.bfloat16)
+    ids = torch.empty(64 * 8, dtype=torch.int32)
+    w = torch.empty(64 * 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="logits: 32766 bytes, the call needs 32768"):
+        mr.moe_route(args, short, None, ids, w)
+    with pytest.raises(ValueError, match="device"):      # sizes right: the device check
+        mr.moe_route(args, full, None, ids, w)
+    with pytest.raises(ValueError, match="logits"):
+        mr.moe_route_permute(args, 8, 0, 256, short, None, ids, w, None, None, None, None,
+                             None, None, None, None, None, None)
+    with pytest.raises(ValueError, match="logits"):
+        mr.moe_route_backward(args, short, ids, w, None, None)
+    with pytest.raises(ValueError, match="topk_ids"):
+        mr.moe_topk_to_dense(64, 256, 8, ids[:-1], w, mr.MOE_BF16, None, None)
+    with pytest.raises(ValueError, match="hidden"):
+        mr.moe_dispatch(torch.empty(10, dtype=torch.bfloat16), mr.MOE_BF16, 4, 128, None, None,
+                        16, None)
+    with pytest.raises(ValueError, match="hidden"):
+        mr.rmsnorm_gate_route(torch.empty(10, dtype=torch.bfloat16), None, None, None, mr.MOE_BF16,
+                              4, 128, 16, 1e-6, 2, mr.MOE_SIGMOID, None, None, None)
+    with pytest.raises(ValueError, match="probs"):
+        mr.moe_aux_loss(torch.empty(7), None, 4, 4, 2, 1, 0.1)
+    # the sizes the other arguments are held to, from their definitions
+    n = mr._route_sizes(args)
+    assert n == dict(logits=64 * 256 * 2, bias=256 * 4, ids=64 * 8 * 4, weights=64 * 8 * 2,
+                     scores=64 * 256 * 4, counts=256 * 4)
+    assert mr._route_sizes(mr.make_route_args(0, 256, 8))["logits"] == 0   # T = 0: nothing

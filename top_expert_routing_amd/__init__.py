@@ -43,9 +43,22 @@ _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "f16": MOE_F16}
 _SF = {"softmax": MOE_SOFTMAX, "sigmoid": MOE_SIGMOID}
 
 
-def _ptr(t):
+_ESZ = {MOE_F32: 4, MOE_BF16: 2, MOE_F16: 2}
+
+
+def _esz(dtype: int) -> int:
+    return _ESZ.get(int(dtype), 0)
+
+
+def _ptr(t, need: int = 0, name: str = "tensor"):
+    """Device pointer of a contiguous tensor.  `need`: the bytes the call reads
+    or writes there, from the call's own sizes (0: not checked); a smaller
+    tensor is refused before anything is launched."""
     if t is None:
         return None
+    have = t.numel() * t.element_size()
+    if need > 0 and have < need:
+        raise ValueError(f"{name}: {have} bytes, the call needs {need}")
     if not t.is_cuda:
         raise ValueError("tensors passed to the library must be device tensors")
     if not t.is_contiguous():
@@ -79,12 +92,48 @@ def make_route_args(T: int, E: int, k: int, score_fn: str = "softmax", pre_softm
 
 # ---- the C entry points ---------------------------------------------------------------
 
+def _route_sizes(args: moe_route_args):
+    """Bytes of the [T, E] logits, the [E] bias, the [T, k] ids and weights and
+    the [T, E] scores that a routing call touches (0 where a size is invalid:
+    the library then reports it)."""
+    T, E, k = args.num_tokens, args.num_experts, args.top_k
+    if T <= 0 or E <= 0 or k <= 0:
+        return dict(logits=0, bias=0, ids=0, weights=0, scores=0, counts=0)
+    return dict(logits=T * E * _esz(args.logits_dtype), bias=E * _esz(args.bias_dtype),
+                ids=T * k * 4, weights=T * k * _esz(args.weights_dtype), scores=T * E * 4,
+                counts=E * 4)
+
+
 def moe_route(args: moe_route_args, logits, bias, topk_ids, topk_weights, scores=None,
               expert_counts=None, workspace=None, stream=None) -> None:
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(_lib.lib.moe_route(ctypes.byref(args), _ptr(logits), _ptr(bias), _ptr(topk_ids),
-                              _ptr(topk_weights), _ptr(scores), _ptr(expert_counts),
+    n = _route_sizes(args)
+    _check(_lib.lib.moe_route(ctypes.byref(args), _ptr(logits, n["logits"], "logits"),
+                              _ptr(bias, n["bias"], "bias"), _ptr(topk_ids, n["ids"], "topk_ids"),
+                              _ptr(topk_weights, n["weights"], "topk_weights"),
+                              _ptr(scores, n["scores"], "scores"),
+                              _ptr(expert_counts, n["counts"], "expert_counts"),
                               _ptr(workspace), ctypes.c_size_t(ws_bytes), _stream(stream)))
+
+
+def _permute_ptrs(args, tile, n_loc, logits, bias, topk_ids, topk_weights, scores,
+                  expert_counts, padded_offsets, total, nctas, e2p, p2t, batch_idx, mn_limit):
+    n = _route_sizes(args)
+    T, k = args.num_tokens, args.top_k
+    mp = mt = 0
+    if T > 0 and k > 0 and n_loc > 0 and tile > 0:
+        mp = max(0, int(_lib.lib.moe_max_padded_tokens(T, k, n_loc, tile)))
+        mt = max(0, int(_lib.lib.moe_max_tiles(T, k, n_loc, tile)))
+    loc = max(0, n_loc)
+    return (_ptr(logits, n["logits"], "logits"), _ptr(bias, n["bias"], "bias"),
+            _ptr(topk_ids, n["ids"], "topk_ids"), _ptr(topk_weights, n["weights"], "topk_weights"),
+            _ptr(scores, n["scores"], "scores"), _ptr(expert_counts, loc * 4, "expert_counts"),
+            _ptr(padded_offsets, (loc + 1) * 4 if loc else 0, "padded_offsets"),
+            _ptr(total, 4, "total_num_padded_tokens"), _ptr(nctas, 4, "num_non_exiting_ctas"),
+            _ptr(e2p, n["ids"], "expanded_idx_to_permuted_idx"),
+            _ptr(p2t, mp * 4, "permuted_idx_to_token_idx"),
+            _ptr(batch_idx, mt * 4, "cta_idx_xy_to_batch_idx"),
+            _ptr(mn_limit, mt * 4, "cta_idx_xy_to_mn_limit"))
 
 
 def moe_route_permute(args: moe_route_args, tile_tokens_dim: int, local_expert_offset: int,
@@ -94,14 +143,14 @@ def moe_route_permute(args: moe_route_args, tile_tokens_dim: int, local_expert_o
                       permuted_idx_to_token_idx, cta_idx_xy_to_batch_idx,
                       cta_idx_xy_to_mn_limit, workspace, stream=None) -> None:
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    p = _permute_ptrs(args, tile_tokens_dim, local_num_experts, logits, bias, topk_ids,
+                      topk_weights, scores, expert_counts, padded_offsets,
+                      total_num_padded_tokens, num_non_exiting_ctas,
+                      expanded_idx_to_permuted_idx, permuted_idx_to_token_idx,
+                      cta_idx_xy_to_batch_idx, cta_idx_xy_to_mn_limit)
     _check(_lib.lib.moe_route_permute(
-        ctypes.byref(args), tile_tokens_dim, local_expert_offset, local_num_experts,
-        _ptr(logits), _ptr(bias), _ptr(topk_ids), _ptr(topk_weights), _ptr(scores),
-        _ptr(expert_counts), _ptr(padded_offsets), _ptr(total_num_padded_tokens),
-        _ptr(num_non_exiting_ctas), _ptr(expanded_idx_to_permuted_idx),
-        _ptr(permuted_idx_to_token_idx), _ptr(cta_idx_xy_to_batch_idx),
-        _ptr(cta_idx_xy_to_mn_limit), _ptr(workspace), ctypes.c_size_t(ws_bytes),
-        _stream(stream)))
+        ctypes.byref(args), tile_tokens_dim, local_expert_offset, local_num_experts, *p,
+        _ptr(workspace), ctypes.c_size_t(ws_bytes), _stream(stream)))
 
 
 def moe_route_permute_noalloc(args: moe_route_args, tile_tokens_dim: int,
@@ -111,13 +160,14 @@ def moe_route_permute_noalloc(args: moe_route_args, tile_tokens_dim: int,
                               expanded_idx_to_permuted_idx, permuted_idx_to_token_idx,
                               cta_idx_xy_to_batch_idx, cta_idx_xy_to_mn_limit,
                               stream=None) -> None:
+    p = _permute_ptrs(args, tile_tokens_dim, local_num_experts, logits, bias, topk_ids,
+                      topk_weights, scores, expert_counts, padded_offsets,
+                      total_num_padded_tokens, num_non_exiting_ctas,
+                      expanded_idx_to_permuted_idx, permuted_idx_to_token_idx,
+                      cta_idx_xy_to_batch_idx, cta_idx_xy_to_mn_limit)
     _check(_lib.lib.moe_route_permute_noalloc(
-        ctypes.byref(args), tile_tokens_dim, local_expert_offset, local_num_experts,
-        _ptr(logits), _ptr(bias), _ptr(topk_ids), _ptr(topk_weights), _ptr(scores),
-        _ptr(expert_counts), _ptr(padded_offsets), _ptr(total_num_padded_tokens),
-        _ptr(num_non_exiting_ctas), _ptr(expanded_idx_to_permuted_idx),
-        _ptr(permuted_idx_to_token_idx), _ptr(cta_idx_xy_to_batch_idx),
-        _ptr(cta_idx_xy_to_mn_limit), _stream(stream)))
+        ctypes.byref(args), tile_tokens_dim, local_expert_offset, local_num_experts, *p,
+        _stream(stream)))
 
 
 def moe_route_permute_noalloc_max_scratch_bytes() -> int:
@@ -128,49 +178,72 @@ def moe_aux_loss(probs, tokens_per_expert, rows: int, total_num_tokens: int, num
                  top_k: int, coeff: float, loss=None, grad_loss=None, grad_probs=None,
                  workspace=None, stream=None) -> None:
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    re = rows * num_experts * 4 if rows > 0 and num_experts > 0 else 0
     _check(_lib.lib.moe_aux_loss(
-        _ptr(probs), _ptr(tokens_per_expert), ctypes.c_int64(rows),
-        ctypes.c_int64(total_num_tokens), num_experts, top_k, ctypes.c_float(coeff),
-        _ptr(loss), _ptr(grad_loss), _ptr(grad_probs), _ptr(workspace),
-        ctypes.c_size_t(ws_bytes), _stream(stream)))
+        _ptr(probs, re, "probs"), _ptr(tokens_per_expert, max(0, num_experts) * 4, "tokens_per_expert"),
+        ctypes.c_int64(rows), ctypes.c_int64(total_num_tokens), num_experts, top_k,
+        ctypes.c_float(coeff), _ptr(loss, 4, "loss"), _ptr(grad_loss, 4, "grad_loss"),
+        _ptr(grad_probs, re, "grad_probs"), _ptr(workspace), ctypes.c_size_t(ws_bytes),
+        _stream(stream)))
 
 
 def moe_route_backward(args: moe_route_args, logits, topk_ids, grad_weights, grad_scores,
                        grad_logits, stream=None) -> None:
-    _check(_lib.lib.moe_route_backward(ctypes.byref(args), _ptr(logits), _ptr(topk_ids),
-                                       _ptr(grad_weights), _ptr(grad_scores), _ptr(grad_logits),
+    n = _route_sizes(args)
+    _check(_lib.lib.moe_route_backward(ctypes.byref(args), _ptr(logits, n["logits"], "logits"),
+                                       _ptr(topk_ids, n["ids"], "topk_ids"),
+                                       _ptr(grad_weights, n["ids"], "grad_weights"),
+                                       _ptr(grad_scores, n["scores"], "grad_scores"),
+                                       _ptr(grad_logits, n["scores"], "grad_logits"),
                                        _stream(stream)))
 
 
 def moe_topk_to_dense(T: int, E: int, top_k: int, topk_ids, topk_weights, weights_dtype: int,
                       probs=None, routing_map=None, stream=None) -> None:
-    _check(_lib.lib.moe_topk_to_dense(T, E, top_k, _ptr(topk_ids), _ptr(topk_weights),
-                                      weights_dtype, _ptr(probs), _ptr(routing_map),
-                                      _stream(stream)))
+    tk = T * top_k if T > 0 and top_k > 0 else 0
+    te = T * E if T > 0 and E > 0 else 0
+    _check(_lib.lib.moe_topk_to_dense(T, E, top_k, _ptr(topk_ids, tk * 4, "topk_ids"),
+                                      _ptr(topk_weights, tk * _esz(weights_dtype), "topk_weights"),
+                                      weights_dtype, _ptr(probs, te * 4, "probs"),
+                                      _ptr(routing_map, te, "routing_map"), _stream(stream)))
 
 
 def moe_dispatch(hidden, dtype: int, T: int, H: int, permuted_idx_to_token_idx,
                  total_num_padded_tokens, max_padded_tokens: int, permuted_hidden,
                  stream=None) -> None:
-    _check(_lib.lib.moe_dispatch(_ptr(hidden), dtype, T, H, _ptr(permuted_idx_to_token_idx),
-                                 _ptr(total_num_padded_tokens), ctypes.c_int64(max_padded_tokens),
-                                 _ptr(permuted_hidden), _stream(stream)))
+    th = T * H * _esz(dtype) if T > 0 and H > 0 else 0
+    mp = max(0, max_padded_tokens)
+    _check(_lib.lib.moe_dispatch(_ptr(hidden, th, "hidden"), dtype, T, H,
+                                 _ptr(permuted_idx_to_token_idx, mp * 4, "permuted_idx_to_token_idx"),
+                                 _ptr(total_num_padded_tokens, 4, "total_num_padded_tokens"),
+                                 ctypes.c_int64(max_padded_tokens),
+                                 _ptr(permuted_hidden, mp * max(0, H) * _esz(dtype), "permuted_hidden"),
+                                 _stream(stream)))
 
 
 def moe_combine(expert_out, dtype: int, T: int, H: int, top_k: int, expanded_idx_to_permuted_idx,
                 topk_weights, weights_dtype: int, out, stream=None) -> None:
+    tk = T * top_k if T > 0 and top_k > 0 else 0
+    th = T * H * _esz(dtype) if T > 0 and H > 0 else 0
     _check(_lib.lib.moe_combine(_ptr(expert_out), dtype, T, H, top_k,
-                                _ptr(expanded_idx_to_permuted_idx), _ptr(topk_weights),
-                                weights_dtype, _ptr(out), _stream(stream)))
+                                _ptr(expanded_idx_to_permuted_idx, tk * 4, "expanded_idx_to_permuted_idx"),
+                                _ptr(topk_weights, tk * _esz(weights_dtype), "topk_weights"),
+                                weights_dtype, _ptr(out, th, "out"), _stream(stream)))
 
 
 def rmsnorm_gate_route(hidden, gamma, router_weights, router_bias, dtype: int, T: int, H: int,
                        E: int, eps: float, top_k: int, act_fn: int, normed, topk_ids,
                        affinities, workspace=None, stream=None) -> None:
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    es = 2 if int(dtype) in (MOE_BF16, MOE_F16) else 0   # else the library reports the dtype
+    ok = T > 0 and H > 0 and E > 0 and top_k > 0 and es > 0
     _check(_lib.lib.rmsnorm_gate_route(
-        _ptr(hidden), _ptr(gamma), _ptr(router_weights), _ptr(router_bias), dtype, T, H, E,
-        ctypes.c_float(eps), top_k, act_fn, _ptr(normed), _ptr(topk_ids), _ptr(affinities),
+        _ptr(hidden, T * H * es if ok else 0, "hidden"), _ptr(gamma, H * es if ok else 0, "gamma"),
+        _ptr(router_weights, H * E * es if ok else 0, "router_weights"),
+        _ptr(router_bias, E * es if ok else 0, "router_bias"), dtype, T, H, E,
+        ctypes.c_float(eps), top_k, act_fn, _ptr(normed, T * H * es if ok else 0, "normed"),
+        _ptr(topk_ids, T * top_k * 4 if ok else 0, "topk_ids"),
+        _ptr(affinities, T * E * 2 if ok else 0, "affinities"),
         _ptr(workspace), ctypes.c_size_t(ws_bytes), _stream(stream)))
 
 
