@@ -1,7 +1,8 @@
 """GPU: the entry points captured into a HIP graph and replayed.
 
 The benchmark replays moe_route_permute, moe_aux_loss and rmsnorm_gate_route
-from captured graphs, whose kernels keep the routing counting region and the
+from captured graphs (and one test captures a layer's whole routing data
+path: route and permute, dispatch, combine, dense outputs and backward), whose kernels keep the routing counting region and the
 front-end synchronisation region ready themselves (no memset nodes).  Each
 test captures one call, then replays it several times with the program's own
 eager work and synchronisations between the replays, poisoning the outputs
@@ -192,3 +193,63 @@ def test_concurrent_streams():
             for f in _ROUTE_FIELDS:
                 assert torch.equal(getattr(o, f), getattr(ref, f)), (w.name, rep, f)
             assert torch.equal(o.permuted_idx_to_token_idx[:total], ref.permuted_idx_to_token_idx[:total])
+
+
+def test_layer_data_path_graph_replays():
+    # one captured graph holding a layer's whole routing data path: route and
+    # permute, dispatch of the hidden rows, combine of the dispatched rows, the
+    # dense outputs and the routing backward; every replay equals the eager calls
+    import torch
+    import top_expert_routing_amd as mr
+    w = with_overrides(WORKLOADS["deepseek_v3_like"], T=1000)
+    T, E, k, H = w.T, w.E, w.k, 256
+    logits, bias = route_inputs(w, T=T, seed=7600)
+    args = _args(mr, w, T)
+    x, b = to_dev(logits, w.logits_dtype), to_dev(bias, w.bias_dtype)
+    rng = np.random.default_rng(7601)
+    hidden = torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(DEV).to(torch.bfloat16)
+    gw = torch.from_numpy(rng.standard_normal((T, k)).astype(np.float32)).to(DEV)
+    mp = mr.moe_max_padded_tokens(T, k, E, w.tile)
+
+    def run(o):
+        mr.route_permute(args, x, b, tile=w.tile, out=o["route"])
+        r = o["route"]
+        mr.moe_dispatch(hidden, mr.MOE_BF16, T, H, r.permuted_idx_to_token_idx,
+                        r.total_num_padded_tokens, mp, o["disp"])
+        mr.moe_combine(o["disp"], mr.MOE_BF16, T, H, k, r.expanded_idx_to_permuted_idx,
+                       r.topk_weights, mr.MOE_F32, o["comb"])
+        mr.moe_topk_to_dense(T, E, k, r.topk_ids, r.topk_weights, mr.MOE_F32, o["probs"], o["rmap"])
+        mr.moe_route_backward(args, x, r.topk_ids, gw, None, o["grad"])
+
+    def buffers():
+        return {"route": mr.alloc_route_outputs(args, DEV, permute=True, tile=w.tile),
+                "disp": torch.empty((mp, H), dtype=torch.bfloat16, device=DEV),
+                "comb": torch.empty((T, H), dtype=torch.bfloat16, device=DEV),
+                "probs": torch.empty((T, E), dtype=torch.float32, device=DEV),
+                "rmap": torch.empty((T, E), dtype=torch.uint8, device=DEV),
+                "grad": torch.empty((T, E), dtype=torch.float32, device=DEV)}
+
+    log(f"[gpu] graph replays: layer data path T={T} H={H}")
+    ref = buffers()
+    run(ref)
+    torch.cuda.synchronize()
+    total = int(ref["route"].total_num_padded_tokens.item())
+    out = buffers()
+    run(out)                                               # first call outside the capture
+    torch.cuda.synchronize()
+    g = _capture(lambda: run(out))
+    for rep in range(REPLAYS):
+        for key in ("disp", "comb", "probs", "grad"):
+            out[key].fill_(float("nan"))
+        out["rmap"].fill_(7)
+        out["route"].topk_ids.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out["route"].topk_ids, ref["route"].topk_ids), rep
+        assert torch.equal(out["disp"][:total].view(torch.int16), ref["disp"][:total].view(torch.int16)), rep
+        for key in ("comb", "probs", "rmap", "grad"):
+            assert torch.equal(out[key].view(torch.uint8), ref[key].view(torch.uint8)), (rep, key)
+        count_region_ready(out["route"].workspace, f"layer path replay {rep}")
+        other = mr.route_permute(args, x, b, tile=w.tile)     # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(other.topk_ids, ref["route"].topk_ids)
